@@ -1,0 +1,265 @@
+"""Loader and numpy wrappers for the C oracle ``libkvq_ref.so``.
+
+TEST INFRASTRUCTURE ONLY: imported by ``tests/``, by the smoke check and by
+the CPU-baseline leg of ``bench.py``.  The product package never imports it.
+
+The C source (``kvq_ref.c``) is the oracle; this module only compiles it
+with gcc and marshals numpy arrays into its host-pointer calls.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+SRC = os.path.join(HERE, "kvq_ref.c")
+LIB = os.path.join(HERE, "libkvq_ref.so")
+
+# ISO C99 (so gcc does not contract a*b+c into an FMA), no fast-math,
+# OpenMP for the independent loops.
+CFLAGS = ["-std=c99", "-O2", "-ffp-contract=off", "-fno-fast-math", "-fopenmp",
+          "-fPIC", "-shared", "-Wall", "-Wextra"]
+
+
+def build(force: bool = True) -> str:
+    """Compile the oracle with gcc into ``oracle/libkvq_ref.so``."""
+    if force or not os.path.exists(LIB) or os.path.getmtime(LIB) < os.path.getmtime(SRC):
+        tmp = LIB + ".tmp"
+        subprocess.check_call(["gcc", *CFLAGS, SRC, "-o", tmp, "-lm"])
+        os.replace(tmp, LIB)
+    return LIB
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB) or os.path.getmtime(LIB) < os.path.getmtime(SRC):
+            build(force=True)
+        L = ctypes.CDLL(LIB)
+        P = ctypes.c_void_p
+        i32, f32, u64, i64 = ctypes.c_int, ctypes.c_float, ctypes.c_uint64, ctypes.c_long
+        L.kvq_ref_bf16_to_f32.argtypes = [ctypes.c_uint16]
+        L.kvq_ref_bf16_to_f32.restype = f32
+        L.kvq_ref_f32_to_bf16.argtypes = [f32]
+        L.kvq_ref_f32_to_bf16.restype = ctypes.c_uint16
+        L.kvq_ref_f16_to_f32.argtypes = [ctypes.c_uint16]
+        L.kvq_ref_f16_to_f32.restype = f32
+        L.kvq_ref_f32_to_f16.argtypes = [f32]
+        L.kvq_ref_f32_to_f16.restype = ctypes.c_uint16
+        for n in ("kvq_ref_f32_to_f16_n", "kvq_ref_f32_to_bf16_n", "kvq_ref_f16_to_f32_n"):
+            getattr(L, n).argtypes = [P, P, ctypes.c_size_t]
+            getattr(L, n).restype = None
+        L.kvq_ref_quantize_group.argtypes = [P, i32, P, P, P]
+        L.kvq_ref_quantize_group.restype = i32
+        L.kvq_ref_unpack_group.argtypes = [P, i32, P]
+        L.kvq_ref_unpack_group.restype = i32
+        L.kvq_ref_pack_group.argtypes = [P, i32, P]
+        L.kvq_ref_pack_group.restype = i32
+        L.kvq_ref_dequantize_group.argtypes = [P, i32, ctypes.c_uint16, ctypes.c_uint16, P]
+        L.kvq_ref_dequantize_group.restype = i32
+        L.kvq_ref_block_bytes.argtypes = [i32, i32, i32]
+        L.kvq_ref_block_bytes.restype = u64
+        L.kvq_ref_quantize_seq.argtypes = [P, i32, i32, i32, P, P, P]
+        L.kvq_ref_quantize_seq.restype = i32
+        L.kvq_ref_restore_seq.argtypes = [P, P, P, i32, P, i32, i32, i32, P]
+        L.kvq_ref_restore_seq.restype = i32
+        L.kvq_ref_attention.argtypes = [P, i64, i64, i32, P, i64, i64, i32, i32, i32, P, i32,
+                                        ctypes.c_double, P]
+        L.kvq_ref_attention.restype = None
+        L.kvq_ref_attend_decode_seq.argtypes = [P, P, P, P, i32, P, P, i32, P, i32, i32, i32,
+                                                P, i32, f32, P]
+        L.kvq_ref_attend_decode_seq.restype = i32
+        L.kvq_ref_attend_chunk_seq.argtypes = [P, P, P, P, i32, P, P, i32, i32, i32, P, P, P,
+                                               i32, i32, f32, i32, i32, P]
+        L.kvq_ref_attend_chunk_seq.restype = i32
+        L.kvq_ref_max_threads.argtypes = []
+        L.kvq_ref_max_threads.restype = i32
+        _lib = L
+    return _lib
+
+
+def _p(a):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _c(a, dtype):
+    return None if a is None else np.ascontiguousarray(a, dtype=dtype)
+
+
+# ---- conversions ----------------------------------------------------------
+def f32_to_f16_bits(x) -> np.ndarray:
+    x = _c(np.asarray(x, dtype=np.float32).ravel(), np.float32)
+    y = np.empty(x.size, np.uint16)
+    lib().kvq_ref_f32_to_f16_n(_p(x), _p(y), x.size)
+    return y
+
+
+def f32_to_bf16_bits(x) -> np.ndarray:
+    x = _c(np.asarray(x, dtype=np.float32).ravel(), np.float32)
+    y = np.empty(x.size, np.uint16)
+    lib().kvq_ref_f32_to_bf16_n(_p(x), _p(y), x.size)
+    return y
+
+
+def f16_bits_to_f32(h) -> np.ndarray:
+    h = _c(np.asarray(h, dtype=np.uint16).ravel(), np.uint16)
+    y = np.empty(h.size, np.float32)
+    lib().kvq_ref_f16_to_f32_n(_p(h), _p(y), h.size)
+    return y
+
+
+# ---- groups ---------------------------------------------------------------
+def quantize_group(x_bf16, bits: int):
+    """Returns (words uint32[2*bits], scale fp16 bits, bias fp16 bits)."""
+    x = _c(x_bf16, np.uint16)
+    assert x.size == 64
+    w = np.zeros(16, np.uint32)
+    s = np.zeros(1, np.uint16)
+    b = np.zeros(1, np.uint16)
+    rc = lib().kvq_ref_quantize_group(_p(x), bits, _p(w), _p(s), _p(b))
+    if rc:
+        raise ValueError("unsupported width")
+    return w[: 2 * bits].copy(), int(s[0]), int(b[0])
+
+
+def unpack_group(words, bits: int) -> np.ndarray:
+    w = np.zeros(16, np.uint32)
+    w[: 2 * bits] = np.asarray(words, np.uint32)
+    c = np.zeros(64, np.uint8)
+    if lib().kvq_ref_unpack_group(_p(w), bits, _p(c)):
+        raise ValueError("unsupported width")
+    return c
+
+
+def pack_group(codes, bits: int) -> np.ndarray:
+    c = _c(codes, np.uint8)
+    w = np.zeros(16, np.uint32)
+    if lib().kvq_ref_pack_group(_p(c), bits, _p(w)):
+        raise ValueError("unsupported width")
+    return w[: 2 * bits].copy()
+
+
+def dequantize_group(words, bits: int, scale_h: int, bias_h: int) -> np.ndarray:
+    w = np.zeros(16, np.uint32)
+    w[: 2 * bits] = np.asarray(words, np.uint32)
+    out = np.zeros(64, np.float32)
+    if lib().kvq_ref_dequantize_group(_p(w), bits, scale_h, bias_h, _p(out)):
+        raise ValueError("unsupported width")
+    return out
+
+
+def block_bytes(bits: int, n_heads: int, head_dim: int) -> int:
+    return int(lib().kvq_ref_block_bytes(bits, n_heads, head_dim))
+
+
+def packed_offsets(bits, n_heads: int, head_dim: int, align: int = 256) -> tuple[np.ndarray, int]:
+    """Byte offsets of consecutive blocks packed back to back (each padded to
+    ``align``), and the total size."""
+    bits = np.asarray(bits, np.uint8).ravel()
+    off = np.zeros(bits.size, np.uint64)
+    pos = 0
+    for j, b in enumerate(bits):
+        off[j] = pos
+        nb = block_bytes(int(b), n_heads, head_dim)
+        pos += (nb + align - 1) // align * align
+    return off, pos
+
+
+# ---- sequences ------------------------------------------------------------
+def quantize_seq(x_bf16, n_heads, head_dim, bits, offset, pool):
+    """Quantize x [64*nb][H][D] (uint16 bf16 bits) into ``pool`` (uint8, in place)."""
+    x = _c(x_bf16, np.uint16)
+    bits = _c(bits, np.uint8)
+    offset = _c(offset, np.uint64)
+    assert pool.dtype == np.uint8 and pool.flags.c_contiguous
+    nb = bits.size
+    assert x.size >= nb * 64 * n_heads * head_dim
+    rc = lib().kvq_ref_quantize_seq(_p(x), n_heads, head_dim, nb, _p(bits), _p(offset), _p(pool))
+    if rc:
+        raise ValueError("kvq_ref_quantize_seq failed")
+
+
+def restore_seq(pool, bits, offset, window, n_heads, head_dim) -> np.ndarray:
+    """fp32 rows [64*nb + W][H][D]: dequantized blocks, then the window."""
+    bits = _c(bits, np.uint8)
+    offset = _c(offset, np.uint64)
+    nw = 0 if window is None else window.size // (n_heads * head_dim)
+    win = None if window is None else _c(window, np.uint16)
+    T = bits.size * 64 + nw
+    out = np.zeros((T, n_heads, head_dim), np.float32)
+    rc = lib().kvq_ref_restore_seq(_p(pool), _p(bits), _p(offset), bits.size, _p(win), nw,
+                                   n_heads, head_dim, _p(out))
+    if rc:
+        raise ValueError("kvq_ref_restore_seq failed")
+    return out
+
+
+def attention(K, V, q_bf16, scale: float) -> np.ndarray:
+    """K fp32 [T][Hkv][dk], V fp32 [T][Hkv][dv], q bf16 bits [Hq][dk] -> fp32 [Hq][dv]."""
+    K = _c(K, np.float32)
+    V = _c(V, np.float32)
+    q = _c(q_bf16, np.uint16)
+    T, H, dk = K.shape
+    dv = V.shape[2]
+    Hq = q.shape[0]
+    out = np.zeros((Hq, dv), np.float32)
+    lib().kvq_ref_attention(_p(K), H * dk, dk, dk, _p(V), H * dv, dv, dv, T, H, _p(q), Hq,
+                            float(scale), _p(out))
+    return out
+
+
+def attend_decode_seq(pool, bits, k_offset, v_offset, k_window, v_window, rope, n_kv_heads,
+                      head_dim, q_bf16, scale) -> np.ndarray:
+    bits = _c(bits, np.uint8)
+    k_offset = _c(k_offset, np.uint64)
+    v_offset = _c(v_offset, np.uint64)
+    nw = 0 if k_window is None else k_window.size // (n_kv_heads * head_dim)
+    k_window = _c(k_window, np.uint16)
+    v_window = _c(v_window, np.uint16)
+    rope = _c(rope, np.uint16)
+    T = bits.size * 64 + nw
+    rope_dim = 0 if rope is None else rope.size // max(1, T * n_kv_heads)
+    q = _c(q_bf16, np.uint16)
+    Hq = q.size // (head_dim + rope_dim)
+    out = np.zeros((Hq, head_dim), np.float32)
+    rc = lib().kvq_ref_attend_decode_seq(_p(pool), _p(bits), _p(k_offset), _p(v_offset), bits.size,
+                                         _p(k_window), _p(v_window), nw, _p(rope), rope_dim,
+                                         n_kv_heads, head_dim, _p(q), Hq, float(scale), _p(out))
+    if rc:
+        raise ValueError("kvq_ref_attend_decode_seq failed")
+    return out
+
+
+def attend_chunk_seq(pool, bits, k_offset, v_offset, k_window, v_window, n_kv_heads, head_dim,
+                     q_new, k_new, v_new, scale, row_begin=0, row_end=None) -> np.ndarray:
+    bits = _c(bits, np.uint8)
+    k_offset = _c(k_offset, np.uint64)
+    v_offset = _c(v_offset, np.uint64)
+    nw = 0 if k_window is None else k_window.size // (n_kv_heads * head_dim)
+    k_window = _c(k_window, np.uint16)
+    v_window = _c(v_window, np.uint16)
+    q_new = _c(q_new, np.uint16)
+    k_new = _c(k_new, np.uint16)
+    v_new = _c(v_new, np.uint16)
+    n_new = k_new.size // (n_kv_heads * head_dim)
+    Hq = q_new.size // max(1, n_new * head_dim) if n_new else 0
+    if row_end is None:
+        row_end = n_new
+    out = np.zeros((n_new, Hq, head_dim), np.float32)
+    rc = lib().kvq_ref_attend_chunk_seq(_p(pool), _p(bits), _p(k_offset), _p(v_offset), bits.size,
+                                        _p(k_window), _p(v_window), nw, n_kv_heads, head_dim,
+                                        _p(q_new), _p(k_new), _p(v_new), n_new, Hq, float(scale),
+                                        row_begin, row_end, _p(out))
+    if rc:
+        raise ValueError("kvq_ref_attend_chunk_seq failed")
+    return out
+
+
+def max_threads() -> int:
+    return int(lib().kvq_ref_max_threads())
