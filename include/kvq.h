@@ -1,0 +1,173 @@
+/*
+ * kvq.h — C ABI of the MI355X (gfx950) quantized KV-cache library.
+ *
+ * The library quantizes a bf16 key/value cache into packed low-bit blocks and
+ * runs attention directly over those blocks, dequantizing on the fly.  The
+ * problem statement comes from these pages:
+ *
+ *   [QKVShare] QKVShare: Quantized KV-Cache Handoff for Multi-Agent On-Device
+ *              LLMs, section Metodologia — a CacheCard packs quantized KV
+ *              groups with per-token widths and metadata; the receiver rebuilds
+ *              16-bit past_key_values and a fused quantized attention kernel is
+ *              left as future work.
+ *   [AgentMem] Agent Memory Below the Prompt: Persistent Q4 KV Cache for
+ *              Multi-Agent LLM Inference on Edge Devices (arXiv 2603.04428),
+ *              Abstract — per-agent 4-bit caches in a block pool, restored
+ *              directly into the attention layer, batched inference over several
+ *              agents' quantized caches, and cross-phase context injection.
+ *   [CoMixKV]  Coordinated Mixed-Precision KV Cache Quantization for Efficient
+ *              LLM-based Multi-agent Systems (arXiv 2611.10096), Abstract —
+ *              widths chosen per agent and layer apply only to newly quantized
+ *              blocks; recent states stay in native precision.
+ *
+ * Format (the pages give none; this library's reading):
+ *   group    64 consecutive elements along head_dim of one (token, head)
+ *   codes    q = clamp(rint((x - bias) * (1/scale)), 0, 2^b - 1), scale =
+ *            (max - min)/(2^b - 1) and bias = min rounded to fp16; codes are
+ *            computed against the stored fp16 values; a zero min/max is +0
+ *   packing  little-endian bitstream: code i at bits [b*i, b*i+b) of 2b uint32
+ *            words per group
+ *   block    64 tokens x all KV heads of one sequence, one width b in
+ *            {2,3,4,8}: codes [H][64][D*b/32] uint32, then meta [H][64][D/64]
+ *            of {fp16 scale, fp16 bias}; H*D*(8b+4) bytes, 256-byte aligned
+ *   window   the newest tokens of a sequence, kept as bf16 [W][H][D]
+ *   restore  x_hat = fma(code, scale, bias) in fp32
+ *
+ * Conventions of every entry point:
+ *   - returns KVQ_OK (0) or a negative KVQ_E* code; kvq_strerror names it;
+ *   - every argument check runs on the host before any HIP call, so an error
+ *     return launches nothing and leaves device memory untouched;
+ *   - work is enqueued asynchronously on `stream` (a hipStream_t passed as
+ *     void*; NULL is the null stream); nothing is allocated, no state is kept,
+ *     and calls are thread-safe;
+ *   - all data pointers are device pointers owned by the caller, except the
+ *     descriptor structs themselves, which live in host memory and are read
+ *     only during the call;
+ *   - device tables (lengths, widths, offsets) are trusted: lengths are clamped
+ *     to the declared capacities, but a width outside {2,3,4,8} or an offset
+ *     outside the pool is a precondition violation (the output is then
+ *     unspecified);
+ *   - NaN, Inf or |x| > 65504 in a cache input is a precondition violation.
+ */
+#ifndef KVQ_H
+#define KVQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define KVQ_OK            0
+#define KVQ_EINVAL       (-1)   /* a null pointer, bad size or misalignment */
+#define KVQ_ENOSPC       (-2)   /* workspace smaller than the matching *_workspace size */
+#define KVQ_EUNSUPPORTED (-3)   /* valid request outside what the kernels implement */
+#define KVQ_EHIP         (-4)   /* the HIP runtime reported an error at launch */
+
+#define KVQ_OUT_BF16 0
+#define KVQ_OUT_F32  1
+
+/* Token bookkeeping of one layer for a batch of A sequences (agents).  The K
+ * and V caches of the layer share it: one width per (sequence, block), used
+ * for both, and the same block/window counts. */
+typedef struct kvq_layout {
+    int32_t n_seqs;            /* A >= 1 */
+    int32_t n_heads;           /* KV heads H >= 1 */
+    int32_t head_dim;          /* D: quantized dims per head, multiple of 64, 64..512 */
+    int32_t max_blocks;        /* >= 0: row stride of bits[] and offset[]; n_blocks[a] <= max_blocks */
+    int32_t window_cap;        /* >= 0: row stride (tokens) of the windows; n_window[a] <= window_cap */
+    const int32_t *n_blocks;   /* device int32 [A]: quantized 64-token blocks of each sequence */
+    const int32_t *n_window;   /* device int32 [A]: bf16 window tokens; NULL allowed if window_cap == 0 */
+    const uint8_t *bits;       /* device uint8 [A][max_blocks]: width of each block (2, 3, 4 or 8) */
+} kvq_layout;
+
+/* Storage of one of K or V of a layer. */
+typedef struct kvq_store {
+    const uint64_t *offset;    /* device uint64 [A][max_blocks]: byte offset of each block in pool, multiple of 256 */
+    uint8_t *pool;             /* device byte pool, 256-byte aligned */
+    uint16_t *window;          /* device bf16 [A][window_cap][H][D]; NULL allowed if window_cap == 0 */
+} kvq_store;
+
+/* Bytes of one block payload of `bits` width for n_heads x head_dim, i.e.
+ * n_heads*head_dim*(8*bits+4); 0 if an argument is unsupported.  With a group
+ * of 64 and 32 bits of metadata this is (bits + 0.5)/16 of the bf16 size: 4-bit
+ * gives 28.125 %, the 4.5-bit figure printed as 28.1 % on KVarN su llama.cpp
+ * (section Dettagli Tecnici e Risultati dei Benchmark KLD), and 4x the capacity
+ * of 16-bit before metadata (AgentMem, Abstract). */
+uint64_t kvq_block_bytes(int32_t bits, int32_t n_heads, int32_t head_dim);
+
+/* Quantize (AgentMem: persist each agent's cache in 4-bit form; CoMixKV: one
+ * width per new block).  For every sequence a and block j < n_blocks[a], read
+ * the 64 bf16 tokens src[a][64j .. 64j+63][H][D] (token-major, as a model emits
+ * K or V; sequence a starts at src + a*src_seq_tokens*H*D) and write the block
+ * payload of width bits[a][j] at dst->pool + dst->offset[a][j].  Windows are
+ * not touched.  Codes, scales and biases are bit-exact to the format above.
+ *   src_seq_tokens >= 64*max_blocks; src 16-byte aligned.
+ * Errors: KVQ_EINVAL (null L/dst/src/tables, bad dims, misalignment),
+ *         KVQ_EHIP. */
+int kvq_quantize(const kvq_layout *L, const kvq_store *dst, const uint16_t *src,
+                 int64_t src_seq_tokens, void *stream);
+
+/* Restore (QKVShare injection path: rebuild 16-bit key/value rows).  For
+ * every sequence a write dst[a][t][H][D] for t < 64*n_blocks[a] + n_window[a]:
+ * dequantized blocks first (fma(code, scale, bias) in fp32, then rounded to
+ * bf16 nearest-even when out_dtype is KVQ_OUT_BF16, or stored as fp32 for
+ * KVQ_OUT_F32), then the window tokens copied unchanged (or widened).  Rows
+ * beyond a sequence's length are not written.
+ *   dst_seq_tokens >= 64*max_blocks + window_cap; dst 16-byte aligned.
+ * Errors: KVQ_EINVAL, KVQ_EUNSUPPORTED (out_dtype), KVQ_EHIP. */
+int kvq_dequantize(const kvq_layout *L, const kvq_store *src, int32_t out_dtype, void *dst,
+                   int64_t dst_seq_tokens, void *stream);
+
+/* Workspace bytes kvq_attend_decode needs for this layout and head count
+ * (written to *bytes).  Errors: KVQ_EINVAL, KVQ_EUNSUPPORTED. */
+int kvq_decode_workspace(const kvq_layout *L, int32_t n_q_heads, int32_t rope_dim, size_t *bytes);
+
+/* Batched decode attention over quantized caches (AgentMem: batched
+ * inference over several agents' quantized caches, restored directly into the
+ * attention layer; QKVShare: the fused quantized attention kernel).  One query
+ * token per sequence.  Query head h of sequence a attends, with scores
+ * softmax_scale * <q, k>, to every cached token of KV head h / (n_q_heads/H):
+ * the 64*n_blocks[a] quantized tokens, then the n_window[a] window tokens.
+ * The result equals softmax attention over the restored rows, within fp32
+ * rounding; an empty sequence gives zeros.
+ *   q    bf16 [A][n_q_heads][D + rope_dim]
+ *   out  fp32 [A][n_q_heads][D]
+ *   V    NULL for latent attention: the values are the restored K rows (the
+ *        first D dims of each key), as in a multi-head latent cache.
+ *   rope NULL or bf16 [A][64*max_blocks + window_cap][H][rope_dim]: raw key
+ *        dims appended after the D quantized ones (rope_dim 0 or 64).
+ *   n_q_heads: a multiple of H with n_q_heads/H <= 16.
+ *   workspace: >= kvq_decode_workspace bytes, 256-byte aligned.
+ * Errors: KVQ_EINVAL, KVQ_ENOSPC, KVQ_EUNSUPPORTED, KVQ_EHIP. */
+int kvq_attend_decode(const kvq_layout *L, const kvq_store *K, const kvq_store *V,
+                      const uint16_t *rope, int32_t rope_dim, const uint16_t *q,
+                      int32_t n_q_heads, float softmax_scale, float *out,
+                      void *workspace, size_t workspace_bytes, void *stream);
+
+/* Workspace bytes kvq_attend_chunk needs (written to *bytes). */
+int kvq_chunk_workspace(const kvq_layout *L, int32_t n_q_heads, int32_t n_new, size_t *bytes);
+
+/* Chunk attention for new-phase tokens over a restored cache (AgentMem:
+ * cross-phase context injection that accumulates attention state without
+ * recomputing the earlier phase).  For every sequence a, new token i (0 <= i <
+ * n_new) and query head h, attend to every cached token of KV head
+ * h / (n_q_heads/H) (blocks, then window) and to new tokens 0..i.
+ *   q_new bf16 [A][n_new][n_q_heads][D]
+ *   k_new, v_new bf16 [A][n_new][H][D]   (unquantized)
+ *   out  fp32 [A][n_new][n_q_heads][D]
+ *   n_q_heads: a multiple of H with n_q_heads/H <= 16.
+ * Errors: KVQ_EINVAL, KVQ_ENOSPC, KVQ_EUNSUPPORTED, KVQ_EHIP. */
+int kvq_attend_chunk(const kvq_layout *L, const kvq_store *K, const kvq_store *V,
+                     const uint16_t *q_new, const uint16_t *k_new, const uint16_t *v_new,
+                     int32_t n_new, int32_t n_q_heads, float softmax_scale, float *out,
+                     void *workspace, size_t workspace_bytes, void *stream);
+
+/* Static text for a status code. */
+const char *kvq_strerror(int status);
+
+#ifdef __cplusplus
+}
+#endif
+#endif

@@ -1,0 +1,269 @@
+// Host side of the kvq C ABI: argument validation (always before any HIP
+// call), work planning and kernel dispatch on the caller's stream.
+#include <math.h>
+#include <stdint.h>
+
+#include "kvq_internal.h"
+
+using namespace kvq;
+
+namespace {
+
+constexpr int kMaxGrid = 65535;
+
+bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+int check_layout(const kvq_layout *L)
+{
+    if (!L) return KVQ_EINVAL;
+    if (L->n_seqs < 1 || L->n_heads < 1 || L->max_blocks < 0 || L->window_cap < 0) return KVQ_EINVAL;
+    if (L->head_dim < 64 || L->head_dim % 64) return KVQ_EINVAL;
+    if (L->head_dim > 512) return KVQ_EUNSUPPORTED;
+    if (L->n_seqs > kMaxGrid || L->n_heads > kMaxGrid) return KVQ_EUNSUPPORTED;
+    if (!L->n_blocks || !aligned(L->n_blocks, 4)) return KVQ_EINVAL;
+    if (L->max_blocks > 0 && !L->bits) return KVQ_EINVAL;
+    if (L->window_cap > 0 && (!L->n_window || !aligned(L->n_window, 4))) return KVQ_EINVAL;
+    // Token indices stay within int32 in the kernels.
+    if ((int64_t)L->max_blocks * 64 + L->window_cap > (int64_t)1 << 30) return KVQ_EUNSUPPORTED;
+    return KVQ_OK;
+}
+
+int check_store(const kvq_layout *L, const kvq_store *S)
+{
+    if (!S) return KVQ_EINVAL;
+    if (L->max_blocks > 0) {
+        if (!S->offset || !S->pool || !aligned(S->offset, 8) || !aligned(S->pool, 256)) return KVQ_EINVAL;
+    }
+    if (L->window_cap > 0 && (!S->window || !aligned(S->window, 16))) return KVQ_EINVAL;
+    return KVQ_OK;
+}
+
+Tables tables(const kvq_layout *L)
+{
+    Tables t;
+    t.A = L->n_seqs;
+    t.H = L->n_heads;
+    t.D = L->head_dim;
+    t.max_blocks = L->max_blocks;
+    t.window_cap = L->window_cap;
+    t.n_blocks = L->n_blocks;
+    t.n_window = L->window_cap > 0 ? L->n_window : nullptr;
+    t.bits = L->bits;
+    return t;
+}
+
+Store store(const kvq_store *S)
+{
+    Store s;
+    s.offset = S->offset;
+    s.pool = S->pool;
+    s.window = S->window;
+    return s;
+}
+
+int hip_status(hipError_t e) { return e == hipSuccess ? KVQ_OK : KVQ_EHIP; }
+
+size_t round256(size_t b) { return (b + 255) / 256 * 256; }
+
+// Plan of one attention call.
+struct Plan {
+    int tok_per_tile, split_keys, n_splits, n_row_tiles;
+    size_t ws_bytes;
+};
+
+int plan_attention(const kvq_layout *L, int n_q_heads, int rope_dim, int n_new, Plan *pl)
+{
+    int st = check_layout(L);
+    if (st) return st;
+    if (n_q_heads < 1 || n_q_heads % L->n_heads) return KVQ_EINVAL;
+    if (rope_dim < 0 || n_new < 0) return KVQ_EINVAL;
+    if (rope_dim != 0 && rope_dim != 64) return KVQ_EUNSUPPORTED;
+    const int G = n_q_heads / L->n_heads;
+    if (G > 16) return KVQ_EUNSUPPORTED;
+    const int64_t max_keys = (int64_t)L->max_blocks * 64 + L->window_cap + n_new;
+    if (max_keys > ((int64_t)1 << 30)) return KVQ_EUNSUPPORTED;
+    generic_plan((int)max_keys, n_new, G, &pl->tok_per_tile, &pl->split_keys, &pl->n_splits);
+    const int n_qtok = n_new ? n_new : 1;
+    pl->n_row_tiles = (n_qtok + pl->tok_per_tile - 1) / pl->tok_per_tile;
+    if ((int64_t)pl->n_row_tiles * L->n_heads > kMaxGrid) return KVQ_EUNSUPPORTED;
+    const size_t rows = (size_t)L->n_seqs * n_qtok * n_q_heads;
+    if (rows > 0x7fffffffu) return KVQ_EUNSUPPORTED;
+    pl->ws_bytes = round256(rows * (size_t)pl->n_splits * (size_t)(L->head_dim + 2) * sizeof(float));
+    return KVQ_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+uint64_t kvq_block_bytes(int32_t bits, int32_t n_heads, int32_t head_dim)
+{
+    if (!(bits == 2 || bits == 3 || bits == 4 || bits == 8)) return 0;
+    if (n_heads < 1 || head_dim < 64 || head_dim > 512 || head_dim % 64) return 0;
+    return (uint64_t)n_heads * (uint64_t)head_dim * (uint64_t)(8 * bits + 4);
+}
+
+int kvq_quantize(const kvq_layout *L, const kvq_store *dst, const uint16_t *src,
+                 int64_t src_seq_tokens, void *stream)
+{
+    int st = check_layout(L);
+    if (st) return st;
+    if (!dst || !dst->pool || !dst->offset) {
+        if (L->max_blocks > 0) return KVQ_EINVAL;
+    } else if (!aligned(dst->pool, 256) || !aligned(dst->offset, 8)) {
+        return KVQ_EINVAL;
+    }
+    if (!src || !aligned(src, 16)) return KVQ_EINVAL;
+    if (src_seq_tokens < (int64_t)L->max_blocks * 64 || (L->n_seqs > 1 && src_seq_tokens < 1))
+        return KVQ_EINVAL;
+    if (L->max_blocks == 0) return KVQ_OK;
+    QuantArgs a;
+    a.t = tables(L);
+    a.offset = dst->offset;
+    a.pool = dst->pool;
+    a.src = src;
+    a.src_seq_tokens = src_seq_tokens;
+    return hip_status(launch_quantize(a, static_cast<hipStream_t>(stream)));
+}
+
+int kvq_dequantize(const kvq_layout *L, const kvq_store *src, int32_t out_dtype, void *dst,
+                   int64_t dst_seq_tokens, void *stream)
+{
+    int st = check_layout(L);
+    if (st) return st;
+    if ((st = check_store(L, src))) return st;
+    if (out_dtype != KVQ_OUT_BF16 && out_dtype != KVQ_OUT_F32) return KVQ_EUNSUPPORTED;
+    if (!dst || !aligned(dst, 16)) return KVQ_EINVAL;
+    if (dst_seq_tokens < (int64_t)L->max_blocks * 64 + L->window_cap) return KVQ_EINVAL;
+    DequantArgs a;
+    a.t = tables(L);
+    a.s = store(src);
+    a.dst = dst;
+    a.dst_seq_tokens = dst_seq_tokens;
+    a.out_f32 = out_dtype == KVQ_OUT_F32;
+    return hip_status(launch_dequantize(a, static_cast<hipStream_t>(stream)));
+}
+
+int kvq_decode_workspace(const kvq_layout *L, int32_t n_q_heads, int32_t rope_dim, size_t *bytes)
+{
+    if (!bytes) return KVQ_EINVAL;
+    Plan pl;
+    int st = plan_attention(L, n_q_heads, rope_dim, 0, &pl);
+    if (st) return st;
+    *bytes = pl.ws_bytes;
+    return KVQ_OK;
+}
+
+int kvq_attend_decode(const kvq_layout *L, const kvq_store *K, const kvq_store *V,
+                      const uint16_t *rope, int32_t rope_dim, const uint16_t *q,
+                      int32_t n_q_heads, float softmax_scale, float *out,
+                      void *workspace, size_t workspace_bytes, void *stream)
+{
+    Plan pl;
+    int st = plan_attention(L, n_q_heads, rope_dim, 0, &pl);
+    if (st) return st;
+    if ((st = check_store(L, K))) return st;
+    if (V && (st = check_store(L, V))) return st;
+    if ((rope_dim > 0) != (rope != nullptr)) return KVQ_EINVAL;
+    if (rope && !aligned(rope, 16)) return KVQ_EINVAL;
+    if (!q || !out || !aligned(q, 16) || !aligned(out, 16)) return KVQ_EINVAL;
+    if (!isfinite(softmax_scale)) return KVQ_EINVAL;
+    if (workspace_bytes < pl.ws_bytes) return KVQ_ENOSPC;
+    if (!workspace || !aligned(workspace, 256)) return KVQ_EINVAL;
+
+    AttnArgs a{};
+    a.t = tables(L);
+    a.k = store(K);
+    a.v = V ? store(V) : store(K);
+    a.v_is_k = V == nullptr;
+    a.rope = rope;
+    a.rope_dim = rope_dim;
+    a.rope_tokens = (int64_t)L->max_blocks * 64 + L->window_cap;
+    a.q = q;
+    a.n_new = 0;
+    a.n_qtok = 1;
+    a.Hq = n_q_heads;
+    a.G = n_q_heads / L->n_heads;
+    a.Dk = L->head_dim + rope_dim;
+    a.Dv = L->head_dim;
+    a.scale = softmax_scale;
+    a.tok_per_tile = pl.tok_per_tile;
+    a.n_row_tiles = pl.n_row_tiles;
+    a.split_keys = pl.split_keys;
+    a.n_splits = pl.n_splits;
+    a.part = static_cast<float *>(workspace);
+    a.out = out;
+    return hip_status(launch_attend_generic(a, static_cast<hipStream_t>(stream)));
+}
+
+int kvq_chunk_workspace(const kvq_layout *L, int32_t n_q_heads, int32_t n_new, size_t *bytes)
+{
+    if (!bytes) return KVQ_EINVAL;
+    if (n_new < 0) return KVQ_EINVAL;
+    Plan pl;
+    int st = plan_attention(L, n_q_heads, 0, n_new, &pl);
+    if (st) return st;
+    *bytes = n_new ? pl.ws_bytes : 0;
+    return KVQ_OK;
+}
+
+int kvq_attend_chunk(const kvq_layout *L, const kvq_store *K, const kvq_store *V,
+                     const uint16_t *q_new, const uint16_t *k_new, const uint16_t *v_new,
+                     int32_t n_new, int32_t n_q_heads, float softmax_scale, float *out,
+                     void *workspace, size_t workspace_bytes, void *stream)
+{
+    if (n_new < 0) return KVQ_EINVAL;
+    Plan pl;
+    int st = plan_attention(L, n_q_heads, 0, n_new, &pl);
+    if (st) return st;
+    if ((st = check_store(L, K))) return st;
+    if (!V) return KVQ_EUNSUPPORTED;
+    if ((st = check_store(L, V))) return st;
+    if (!q_new || !k_new || !v_new || !out) return KVQ_EINVAL;
+    if (!aligned(q_new, 16) || !aligned(k_new, 16) || !aligned(v_new, 16) || !aligned(out, 16))
+        return KVQ_EINVAL;
+    if (!isfinite(softmax_scale)) return KVQ_EINVAL;
+    if (n_new == 0) return KVQ_OK;
+    if (workspace_bytes < pl.ws_bytes) return KVQ_ENOSPC;
+    if (!workspace || !aligned(workspace, 256)) return KVQ_EINVAL;
+
+    AttnArgs a{};
+    a.t = tables(L);
+    a.k = store(K);
+    a.v = store(V);
+    a.v_is_k = 0;
+    a.rope = nullptr;
+    a.rope_dim = 0;
+    a.rope_tokens = 0;
+    a.q = q_new;
+    a.k_new = k_new;
+    a.v_new = v_new;
+    a.n_new = n_new;
+    a.n_qtok = n_new;
+    a.Hq = n_q_heads;
+    a.G = n_q_heads / L->n_heads;
+    a.Dk = L->head_dim;
+    a.Dv = L->head_dim;
+    a.scale = softmax_scale;
+    a.tok_per_tile = pl.tok_per_tile;
+    a.n_row_tiles = pl.n_row_tiles;
+    a.split_keys = pl.split_keys;
+    a.n_splits = pl.n_splits;
+    a.part = static_cast<float *>(workspace);
+    a.out = out;
+    return hip_status(launch_attend_generic(a, static_cast<hipStream_t>(stream)));
+}
+
+const char *kvq_strerror(int status)
+{
+    switch (status) {
+    case KVQ_OK: return "ok";
+    case KVQ_EINVAL: return "invalid argument (null pointer, bad size or misalignment)";
+    case KVQ_ENOSPC: return "workspace too small";
+    case KVQ_EUNSUPPORTED: return "unsupported shape or option";
+    case KVQ_EHIP: return "HIP runtime error at launch";
+    default: return "unknown status";
+    }
+}
+
+}  // extern "C"

@@ -1,0 +1,74 @@
+// Internal declarations shared by the host API and the HIP kernels of kvq.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/kvq.h"
+
+namespace kvq {
+
+// Per-layer token bookkeeping, passed by value to kernels.
+struct Tables {
+    int A, H, D, max_blocks, window_cap;
+    const int32_t *n_blocks;
+    const int32_t *n_window;   // may be null (no window)
+    const uint8_t *bits;
+};
+
+// Storage of one of K or V.
+struct Store {
+    const uint64_t *offset;
+    const uint8_t *pool;
+    const uint16_t *window;
+};
+
+struct QuantArgs {
+    Tables t;
+    const uint64_t *offset;
+    uint8_t *pool;
+    const uint16_t *src;
+    int64_t src_seq_tokens;
+};
+
+struct DequantArgs {
+    Tables t;
+    Store s;
+    void *dst;
+    int64_t dst_seq_tokens;
+    int out_f32;
+};
+
+// Attention over quantized + window (+ new) keys.  Decode is the case
+// n_new == 0 with one query token per sequence.
+struct AttnArgs {
+    Tables t;
+    Store k, v;
+    int v_is_k;                 // latent attention: values are the K rows
+    const uint16_t *rope;       // [A][rope_tokens][H][rope_dim] or null
+    int rope_dim;
+    int64_t rope_tokens;
+    const uint16_t *q;          // [A][n_qtok][Hq][Dk]
+    const uint16_t *k_new;      // [A][n_new][H][D] (chunk)
+    const uint16_t *v_new;
+    int n_new;                  // 0 for decode
+    int n_qtok;                 // query tokens per sequence (1 for decode, n_new for chunk)
+    int Hq, G, Dk, Dv;
+    float scale;
+    int tok_per_tile;           // query tokens per row tile
+    int n_row_tiles;            // row tiles per (sequence, KV head)
+    int split_keys;             // keys per split
+    int n_splits;               // splits per row
+    float *part;                // [rows][n_splits][Dv + 2]
+    float *out;                 // [A][n_qtok][Hq][Dv]
+};
+
+// Launchers (return hipError_t of the launch).
+hipError_t launch_quantize(const QuantArgs &a, hipStream_t s);
+hipError_t launch_dequantize(const DequantArgs &a, hipStream_t s);
+hipError_t launch_attend_generic(const AttnArgs &a, hipStream_t s);
+
+// Generic path's split size and workspace.
+void generic_plan(int max_keys, int n_new, int G, int *tok_per_tile, int *split_keys, int *n_splits);
+
+}  // namespace kvq

@@ -1,0 +1,304 @@
+// Quantize and restore kernels (gfx950).
+//
+// Format and arithmetic: affine min/max groups of 64 elements along head_dim,
+// fp16 scale and bias, codes against the stored fp16 values, little-endian
+// bitstream packing (the reading of the "quantized KV groups" of QKVShare,
+// Metodologia, and of the 4-bit format of Agent Memory Below the Prompt,
+// Abstract; one width per block as in CoMixKV, Abstract).
+//
+// This translation unit is compiled with -ffp-contract=off and correctly
+// rounded fp32 division: the codes, scales and biases it writes are
+// bit-for-bit the documented sequence of IEEE binary32 operations.
+//
+// Layout of the work: one workgroup (256 lanes, 4 wave64s) per (block,
+// head, sequence).  A group of 64 bf16 values (128 contiguous bytes) belongs
+// to 8 lanes, 8 values (16 bytes) each, so a wave covers 8 groups per step and
+// its global loads are full 128-byte segments.  min/max use 3 xor-shuffles
+// inside each 8-lane slice.  Every lane loads all of its data before the
+// arithmetic, to keep several 16-byte loads in flight per lane.
+#include "kvq_internal.h"
+
+namespace kvq {
+namespace {
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+__device__ __forceinline__ uint16_t f32_to_f16_bits(float f)
+{
+    _Float16 h = (_Float16)f;                      // v_cvt_f16_f32, round to nearest even
+    return __builtin_bit_cast(uint16_t, h);
+}
+__device__ __forceinline__ float f16_bits_to_f32(uint16_t b)
+{
+    return (float)__builtin_bit_cast(_Float16, b);
+}
+
+// bf16 round to nearest even of a finite fp32 value.
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f)
+{
+    uint32_t u = __float_as_uint(f);
+    return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+}
+
+__device__ __forceinline__ int seq_blocks(const Tables &t, int a)
+{
+    int nb = t.n_blocks[a];
+    return nb < 0 ? 0 : (nb > t.max_blocks ? t.max_blocks : nb);
+}
+__device__ __forceinline__ int seq_window(const Tables &t, int a)
+{
+    if (!t.n_window) return 0;
+    int nw = t.n_window[a];
+    return nw < 0 ? 0 : (nw > t.window_cap ? t.window_cap : nw);
+}
+
+// Quantize the 64 tokens x D dims of (block j, head h) at width B.
+template <int B, int NG>
+__device__ __forceinline__ void quant_block(const uint16_t *__restrict__ src_blk, int H,
+                                            uint8_t *__restrict__ blk, int h)
+{
+    constexpr int D = NG * 64;
+    constexpr int N = (1 << B) - 1;
+    constexpr int ITER = 2 * NG;                    // 64*NG groups / 32 per step
+    constexpr int CODE_ROW = D * B / 8;             // bytes per (head, token)
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int sub = lane & 7;                       // lane within the group
+    const int gl = lane >> 3;                       // group within the wave step
+
+    uint4 raw[ITER];
+#pragma unroll
+    for (int k = 0; k < ITER; k++) {
+        int gi = wave * 8 + gl + 32 * k;            // group index inside the (block, head)
+        int r = gi / NG, g = gi % NG;
+        raw[k] = *reinterpret_cast<const uint4 *>(src_blk + ((size_t)r * H + h) * D + g * 64 + sub * 8);
+    }
+
+    uint8_t *codes = blk + (size_t)h * 64 * CODE_ROW;
+    uint8_t *meta = blk + (size_t)H * 64 * CODE_ROW + (size_t)h * 64 * NG * 4;
+
+#pragma unroll
+    for (int k = 0; k < ITER; k++) {
+        const int gi = wave * 8 + gl + 32 * k;
+        float x[8];
+        x[0] = bf16_lo(raw[k].x); x[1] = bf16_hi(raw[k].x);
+        x[2] = bf16_lo(raw[k].y); x[3] = bf16_hi(raw[k].y);
+        x[4] = bf16_lo(raw[k].z); x[5] = bf16_hi(raw[k].z);
+        x[6] = bf16_lo(raw[k].w); x[7] = bf16_hi(raw[k].w);
+        float mn = x[0], mx = x[0];
+#pragma unroll
+        for (int i = 1; i < 8; i++) { mn = fminf(mn, x[i]); mx = fmaxf(mx, x[i]); }
+#pragma unroll
+        for (int o = 1; o < 8; o <<= 1) {
+            mn = fminf(mn, __shfl_xor(mn, o));
+            mx = fmaxf(mx, __shfl_xor(mx, o));
+        }
+        mn = mn + 0.0f;                             // a zero extreme is +0
+        mx = mx + 0.0f;
+        const float s = (mx - mn) / (float)N;       // correctly rounded divide
+        const uint16_t sh = f32_to_f16_bits(s);
+        const uint16_t bh = f32_to_f16_bits(mn);
+        const float sf = f16_bits_to_f32(sh);
+        const float bf = f16_bits_to_f32(bh);
+        const float inv = (sf == 0.0f) ? 0.0f : 1.0f / sf;
+
+        uint64_t v = 0;                             // this lane's 8 codes, b bits each
+#pragma unroll
+        for (int i = 0; i < 8; i++) {
+            float t = (x[i] - bf) * inv;
+            float r = __builtin_rintf(t);
+            r = (r >= 0.0f) ? r : 0.0f;             // NaN -> 0
+            r = (r > (float)N) ? (float)N : r;
+            v |= (uint64_t)(uint32_t)r << (B * i);
+        }
+
+        uint8_t *gc = codes + (size_t)gi * (8 * B);  // group's code words (2B of them)
+        if constexpr (B == 4) {
+            reinterpret_cast<uint32_t *>(gc)[sub] = (uint32_t)v;
+        } else if constexpr (B == 8) {
+            reinterpret_cast<uint2 *>(gc)[sub] = make_uint2((uint32_t)v, (uint32_t)(v >> 32));
+        } else if constexpr (B == 2) {
+            uint32_t mine = (uint32_t)v;            // 16 bits
+            uint32_t other = __shfl_xor(mine, 1);
+            if ((sub & 1) == 0) reinterpret_cast<uint32_t *>(gc)[sub >> 1] = mine | (other << 16);
+        } else {                                    // B == 3: 24 bits, 4 lanes -> 3 words
+            uint32_t mine = (uint32_t)v;
+            uint32_t next = __shfl(mine, (lane + 1) & 63);
+            int j = sub & 3;
+            if (j < 3) {
+                uint32_t w = (mine >> (8 * j)) | (next << (24 - 8 * j));
+                reinterpret_cast<uint32_t *>(gc)[3 * (sub >> 2) + j] = w;
+            }
+        }
+        if (sub == 0)
+            reinterpret_cast<uint32_t *>(meta)[gi] = (uint32_t)sh | ((uint32_t)bh << 16);
+    }
+}
+
+template <int NG>
+__global__ __launch_bounds__(256) void quantize_kernel(QuantArgs a)
+{
+    const int j = blockIdx.x, h = blockIdx.y, s = blockIdx.z;
+    if (j >= seq_blocks(a.t, s)) return;
+    const int b = a.t.bits[(size_t)s * a.t.max_blocks + j];
+    uint8_t *blk = a.pool + a.offset[(size_t)s * a.t.max_blocks + j];
+    const uint16_t *src_blk = a.src + ((size_t)s * a.src_seq_tokens + (size_t)j * 64) * a.t.H * (NG * 64);
+    switch (b) {
+    case 2: quant_block<2, NG>(src_blk, a.t.H, blk, h); break;
+    case 3: quant_block<3, NG>(src_blk, a.t.H, blk, h); break;
+    case 4: quant_block<4, NG>(src_blk, a.t.H, blk, h); break;
+    case 8: quant_block<8, NG>(src_blk, a.t.H, blk, h); break;
+    default: break;                                 // precondition violation: nothing written
+    }
+}
+
+// ---- restore ---------------------------------------------------------------
+template <int B>
+__device__ __forceinline__ void lane_codes(const uint8_t *gc, int sub, uint32_t c[8])
+{
+    // This lane's 8 codes occupy stream bits [8B*sub, 8B*sub + 8B) of the group.
+    const uint32_t *w = reinterpret_cast<const uint32_t *>(gc);
+    uint64_t bitsv;
+    if constexpr (B == 8) {
+        uint2 p = reinterpret_cast<const uint2 *>(gc)[sub];
+        bitsv = (uint64_t)p.x | ((uint64_t)p.y << 32);
+    } else if constexpr (B == 4) {
+        bitsv = w[sub];
+    } else if constexpr (B == 2) {
+        bitsv = (w[sub >> 1] >> ((sub & 1) * 16)) & 0xffffu;
+    } else {
+        int pos = 24 * sub, wi = pos >> 5, o = pos & 31;
+        uint64_t lo = w[wi];
+        if (o + 24 > 32) lo |= (uint64_t)w[wi + 1] << 32;
+        bitsv = (lo >> o) & 0xffffffu;
+    }
+#pragma unroll
+    for (int i = 0; i < 8; i++) c[i] = (uint32_t)(bitsv >> (B * i)) & ((1u << B) - 1u);
+}
+
+template <int B, int NG>
+__device__ __forceinline__ void restore_block(const uint8_t *__restrict__ blk, int H, int h,
+                                              void *dst_blk, int out_f32)
+{
+    constexpr int D = NG * 64;
+    constexpr int CODE_ROW = D * B / 8;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int sub = lane & 7, gl = lane >> 3;
+    const uint8_t *codes = blk + (size_t)h * 64 * CODE_ROW;
+    const uint32_t *meta = reinterpret_cast<const uint32_t *>(blk + (size_t)H * 64 * CODE_ROW +
+                                                              (size_t)h * 64 * NG * 4);
+#pragma unroll 2
+    for (int k = 0; k < 2 * NG; k++) {
+        const int gi = wave * 8 + gl + 32 * k;
+        const int r = gi / NG, g = gi % NG;
+        uint32_t c[8];
+        lane_codes<B>(codes + (size_t)gi * 8 * B, sub, c);
+        const uint32_t m = meta[gi];
+        const float sf = f16_bits_to_f32((uint16_t)(m & 0xffffu));
+        const float bf = f16_bits_to_f32((uint16_t)(m >> 16));
+        float y[8];
+#pragma unroll
+        for (int i = 0; i < 8; i++) y[i] = __builtin_fmaf((float)c[i], sf, bf);
+        const size_t e = ((size_t)r * H + h) * D + g * 64 + sub * 8;
+        if (out_f32) {
+            float4 *o = reinterpret_cast<float4 *>(static_cast<float *>(dst_blk) + e);
+            o[0] = make_float4(y[0], y[1], y[2], y[3]);
+            o[1] = make_float4(y[4], y[5], y[6], y[7]);
+        } else {
+            uint4 o;
+            o.x = f32_to_bf16_bits(y[0]) | (f32_to_bf16_bits(y[1]) << 16);
+            o.y = f32_to_bf16_bits(y[2]) | (f32_to_bf16_bits(y[3]) << 16);
+            o.z = f32_to_bf16_bits(y[4]) | (f32_to_bf16_bits(y[5]) << 16);
+            o.w = f32_to_bf16_bits(y[6]) | (f32_to_bf16_bits(y[7]) << 16);
+            *reinterpret_cast<uint4 *>(static_cast<uint16_t *>(dst_blk) + e) = o;
+        }
+    }
+}
+
+template <int NG>
+__global__ __launch_bounds__(256) void dequantize_kernel(DequantArgs a)
+{
+    constexpr int D = NG * 64;
+    const int j = blockIdx.x, h = blockIdx.y, s = blockIdx.z;
+    const int nb = seq_blocks(a.t, s);
+    const int H = a.t.H;
+    const size_t esz = a.out_f32 ? 4 : 2;
+    char *dst_seq = static_cast<char *>(a.dst) + (size_t)s * a.dst_seq_tokens * H * D * esz;
+    if (j < nb) {
+        const int b = a.t.bits[(size_t)s * a.t.max_blocks + j];
+        const uint8_t *blk = a.s.pool + a.s.offset[(size_t)s * a.t.max_blocks + j];
+        void *dst_blk = dst_seq + (size_t)j * 64 * H * D * esz;
+        switch (b) {
+        case 2: restore_block<2, NG>(blk, H, h, dst_blk, a.out_f32); break;
+        case 3: restore_block<3, NG>(blk, H, h, dst_blk, a.out_f32); break;
+        case 4: restore_block<4, NG>(blk, H, h, dst_blk, a.out_f32); break;
+        case 8: restore_block<8, NG>(blk, H, h, dst_blk, a.out_f32); break;
+        default: break;
+        }
+        return;
+    }
+    // Window tiles: 64 window tokens per workgroup, copied after the blocks.
+    const int wt = j - a.t.max_blocks;
+    if (wt < 0) return;
+    const int nw = seq_window(a.t, s);
+    const int w0 = wt * 64;
+    if (w0 >= nw) return;
+    const int rows = min(64, nw - w0);
+    const uint16_t *win = a.s.window + ((size_t)s * a.t.window_cap + w0) * H * D;
+    const size_t tok0 = (size_t)nb * 64 + w0;
+    for (int e = threadIdx.x * 8; e < rows * D; e += 256 * 8) {
+        const int r = e / D, d = e % D;
+        const uint4 v = *reinterpret_cast<const uint4 *>(win + ((size_t)r * H + h) * D + d);
+        const size_t o = ((tok0 + r) * H + h) * D + d;
+        if (a.out_f32) {
+            float4 *p = reinterpret_cast<float4 *>(reinterpret_cast<float *>(dst_seq) + o);
+            p[0] = make_float4(bf16_lo(v.x), bf16_hi(v.x), bf16_lo(v.y), bf16_hi(v.y));
+            p[1] = make_float4(bf16_lo(v.z), bf16_hi(v.z), bf16_lo(v.w), bf16_hi(v.w));
+        } else {
+            *reinterpret_cast<uint4 *>(reinterpret_cast<uint16_t *>(dst_seq) + o) = v;
+        }
+    }
+}
+
+}  // namespace
+
+hipError_t launch_quantize(const QuantArgs &a, hipStream_t s)
+{
+    if (a.t.max_blocks == 0) return hipSuccess;
+    dim3 grid(a.t.max_blocks, a.t.H, a.t.A);
+    switch (a.t.D / 64) {
+    case 1: quantize_kernel<1><<<grid, 256, 0, s>>>(a); break;
+    case 2: quantize_kernel<2><<<grid, 256, 0, s>>>(a); break;
+    case 3: quantize_kernel<3><<<grid, 256, 0, s>>>(a); break;
+    case 4: quantize_kernel<4><<<grid, 256, 0, s>>>(a); break;
+    case 5: quantize_kernel<5><<<grid, 256, 0, s>>>(a); break;
+    case 6: quantize_kernel<6><<<grid, 256, 0, s>>>(a); break;
+    case 7: quantize_kernel<7><<<grid, 256, 0, s>>>(a); break;
+    case 8: quantize_kernel<8><<<grid, 256, 0, s>>>(a); break;
+    default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_dequantize(const DequantArgs &a, hipStream_t s)
+{
+    const int wtiles = (a.t.window_cap + 63) / 64;
+    const int gx = a.t.max_blocks + wtiles;
+    if (gx == 0) return hipSuccess;
+    dim3 grid(gx, a.t.H, a.t.A);
+    switch (a.t.D / 64) {
+    case 1: dequantize_kernel<1><<<grid, 256, 0, s>>>(a); break;
+    case 2: dequantize_kernel<2><<<grid, 256, 0, s>>>(a); break;
+    case 3: dequantize_kernel<3><<<grid, 256, 0, s>>>(a); break;
+    case 4: dequantize_kernel<4><<<grid, 256, 0, s>>>(a); break;
+    case 5: dequantize_kernel<5><<<grid, 256, 0, s>>>(a); break;
+    case 6: dequantize_kernel<6><<<grid, 256, 0, s>>>(a); break;
+    case 7: dequantize_kernel<7><<<grid, 256, 0, s>>>(a); break;
+    case 8: dequantize_kernel<8><<<grid, 256, 0, s>>>(a); break;
+    default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+}  // namespace kvq

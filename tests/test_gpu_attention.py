@@ -1,0 +1,181 @@
+"""GPU parity of decode and chunk attention against the oracle: within
+2e-3 max-abs and 1e-3 relative L2 (fp32 outputs against fp64 attention over
+the oracle's own restored rows), through the C ABI."""
+import numpy as np
+import pytest
+import torch
+
+import kvq_synth as syn
+import oracle
+from parity import build, close, gpu_pool_matches, ref_decode, to_dev_bf16
+
+pytestmark = pytest.mark.gpu
+
+
+def _decode(b, q_bits, scale):
+    q = to_dev_bf16(q_bits)
+    out = b.cache.attend_decode(q, scale)
+    torch.cuda.synchronize()
+    return out.cpu().numpy()
+
+
+def test_decode_tiny_workload():
+    w = syn.workload(0)
+    k, v = w.kv(0, 0, syn.TAG_K), w.kv(0, 0, syn.TAG_V)
+    b = build(w.n_kv_heads, w.head_dim, w.lengths, k_src=[k], v_src=[v])
+    q = w.q(0)
+    close(_decode(b, q, w.scale), ref_decode(b, q, w.scale), what="tiny")
+
+
+@pytest.mark.parametrize("G", [1, 2, 4, 8, 16])
+def test_decode_gqa_groups(G):
+    H, D = 2, 128
+    lengths = [64 * 7 + 3, 64 * 2, 1000]
+    b = build(H, D, lengths, keep_recent=40, seed=G)
+    q = syn.random_normal_bf16((3, G * H, D), 11 + G)
+    close(_decode(b, q, D ** -0.5), ref_decode(b, q, D ** -0.5), what=f"G={G}")
+
+
+def test_decode_edge_lengths():
+    """Empty sequence, one window token, exactly one block, block + 1."""
+    H, D = 2, 64
+    lengths = [0, 1, 64, 65, 63, 128]
+    window = [0, 1, 0, 1, 63, 0]
+    b = build(H, D, lengths, window=window, seed=4)
+    q = syn.random_normal_bf16((6, 8, D), 12)
+    got = _decode(b, q, 0.125)
+    want = ref_decode(b, q, 0.125)
+    assert np.all(got[0] == 0.0)
+    close(got, want, what="edges")
+
+
+@pytest.mark.parametrize("D", [64, 256, 512])
+def test_decode_mixed_widths_window(D):
+    rng = np.random.default_rng(D)
+    H, G = 4, 2
+    lengths = [int(v) for v in rng.integers(200, 2000, size=4)]
+    window = [128 + (L % 64) for L in lengths]
+    nb = [(L - w) // 64 for L, w in zip(lengths, window)]
+    bits = [rng.choice(np.array([2, 3, 4, 8], np.uint8), size=n, p=[0.4, 0.4, 0.15, 0.05]) for n in nb]
+    b = build(H, D, lengths, bits=bits, window=window, seed=D)
+    q = syn.random_normal_bf16((4, G * H, D), 13)
+    close(_decode(b, q, D ** -0.5), ref_decode(b, q, D ** -0.5), what=f"mixed D={D}")
+
+
+def test_decode_latent_with_rope():
+    H, D, R, Hq = 1, 512, 64, 16
+    lengths = [64 * 20, 64 * 3 + 9]
+    b = build(H, D, lengths, latent=True, rope_dim=R, keep_recent=0, window=[0, 9], seed=5)
+    q = syn.random_normal_bf16((2, Hq, D + R), 14)
+    s = 576 ** -0.5
+    close(_decode(b, q, s), ref_decode(b, q, s), what="latent+rope")
+
+
+def test_decode_llama_10_agents_full():
+    w = syn.workload(1)
+    k_src = [w.kv(a, 0, syn.TAG_K) for a in range(w.n_agents)]
+    v_src = [w.kv(a, 0, syn.TAG_V) for a in range(w.n_agents)]
+    b = build(w.n_kv_heads, w.head_dim, w.lengths, k_src=k_src, v_src=v_src)
+    q = w.q(0)
+    close(_decode(b, q, w.scale), ref_decode(b, q, w.scale), what="llama-10")
+
+
+def test_decode_gemma_mixed_full_layer():
+    """One sampled layer of the Gemma-3-12B mixed-width workload, all 8 agents."""
+    w = syn.workload(2)
+    layer = w.layers[0]
+    k_src = [w.kv(a, layer, syn.TAG_K) for a in range(w.n_agents)]
+    v_src = [w.kv(a, layer, syn.TAG_V) for a in range(w.n_agents)]
+    bits = [w.bits(a, layer) for a in range(w.n_agents)]
+    b = build(w.n_kv_heads, w.head_dim, w.lengths, bits=bits, window=w.n_window,
+              k_src=k_src, v_src=v_src)
+    gpu_pool_matches(b)
+    q = w.q(layer)
+    close(_decode(b, q, w.scale), ref_decode(b, q, w.scale), what="gemma-mixed")
+
+
+def test_decode_mla_4_agents_full():
+    w = syn.workload(4)
+    k_src = [w.kv(a, 0, syn.TAG_K) for a in range(w.n_agents)]
+    rope = [w.rope(a, 0) for a in range(w.n_agents)]
+    b = build(1, 512, w.lengths, latent=True, rope_dim=64, k_src=k_src, rope=rope)
+    q = w.q(0)
+    close(_decode(b, q, w.scale), ref_decode(b, q, w.scale), what="mla")
+
+
+def test_decode_deterministic():
+    b = build(8, 128, [4096, 3000], keep_recent=128, seed=9)
+    q = syn.random_normal_bf16((2, 32, 128), 15)
+    a1 = _decode(b, q, 0.1)
+    a2 = _decode(b, q, 0.1)
+    assert np.array_equal(a1, a2)
+
+
+# ---- chunk -------------------------------------------------------------------
+def _chunk(b, qn, kn, vn, scale):
+    out = b.cache.attend_chunk(to_dev_bf16(qn), to_dev_bf16(kn), to_dev_bf16(vn), scale)
+    torch.cuda.synchronize()
+    return out.cpu().numpy()
+
+
+def _ref_chunk(b, a, qn, kn, vn, scale, rows=None):
+    s = b.seq(a)
+    c = b.cache
+    r0, r1 = (0, qn.shape[0]) if rows is None else rows
+    return oracle.attend_chunk_seq(b.ref_pool, s["bits"], s["koff"], s["voff"], s["kw"], s["vw"],
+                                   c.H, c.D, qn, kn, vn, scale, r0, r1)
+
+
+@pytest.mark.parametrize("G,n_new", [(4, 37), (1, 5), (2, 64), (16, 3)])
+def test_chunk_small(G, n_new):
+    H, D = 2, 128
+    lengths = [64 * 5 + 20, 64 * 2]
+    b = build(H, D, lengths, window=[20, 0], seed=G)
+    A = 2
+    qn = syn.random_normal_bf16((A, n_new, G * H, D), 21)
+    kn = syn.random_normal_bf16((A, n_new, H, D), 22)
+    vn = syn.random_normal_bf16((A, n_new, H, D), 23)
+    got = _chunk(b, qn, kn, vn, D ** -0.5)
+    for a in range(A):
+        want = _ref_chunk(b, a, qn[a], kn[a], vn[a], D ** -0.5)
+        close(got[a], want, what=f"chunk a={a}")
+
+
+def test_chunk_empty_cache():
+    H, D = 1, 64
+    b = build(H, D, [0], seed=1)
+    qn = syn.random_normal_bf16((1, 9, 4, D), 31)
+    kn = syn.random_normal_bf16((1, 9, H, D), 32)
+    vn = syn.random_normal_bf16((1, 9, H, D), 33)
+    got = _chunk(b, qn, kn, vn, 0.125)
+    close(got[0], _ref_chunk(b, 0, qn[0], kn[0], vn[0], 0.125), what="chunk-empty")
+    # the first new token sees only itself: output equals its value
+    v0 = syn.bf16_to_f32(vn[0, 0, 0])
+    assert np.allclose(got[0, 0], v0[None, :], atol=1e-6)
+
+
+def test_chunk_one_token_equals_decode():
+    H, D = 8, 128
+    b = build(H, D, [64 * 10 + 5], window=[5], seed=2)
+    qn = syn.random_normal_bf16((1, 1, 32, D), 41)
+    kn = syn.random_normal_bf16((1, 1, H, D), 42)
+    vn = syn.random_normal_bf16((1, 1, H, D), 43)
+    got = _chunk(b, qn, kn, vn, D ** -0.5)
+    close(got[0], _ref_chunk(b, 0, qn[0], kn[0], vn[0], D ** -0.5), what="chunk-1")
+
+
+def test_chunk_llama_32k_restore_512_sampled_rows():
+    """Full 32768-token restore + 512-token causal chunk; the oracle checks
+    sampled query rows (first, second, middle, last), the GPU runs the whole
+    launch as the benchmark does."""
+    w = syn.workload(3)
+    k_src = [w.kv(0, 0, syn.TAG_K)]
+    v_src = [w.kv(0, 0, syn.TAG_V)]
+    b = build(w.n_kv_heads, w.head_dim, w.lengths, k_src=k_src, v_src=v_src)
+    gpu_pool_matches(b)
+    qn, kn, vn = w.chunk_new()
+    got = _chunk(b, qn[None], kn[None], vn[None], w.scale)[0]
+    assert np.all(np.isfinite(got))
+    for r0, r1 in [(0, 2), (255, 256), (510, 512)]:
+        want = _ref_chunk(b, 0, qn, kn, vn, w.scale, rows=(r0, r1))
+        close(got[r0:r1], want[r0:r1], what=f"chunk rows {r0}:{r1}")
