@@ -1,0 +1,327 @@
+#!/usr/bin/env python3
+"""Benchmark of the quantized KV-cache hot path on one MI355X.
+
+One step = the whole path over one batch of synthetic input: quantize every
+K and V cache of the workload (kvq_quantize), then attend over the packed
+blocks (kvq_attend_decode, or kvq_attend_chunk for the restore + chunk
+workload).  Inputs are resident in HBM before timing; cache copies rotate
+so that no step reads what the 256 MB Infinity Cache still holds from the
+previous steps.
+
+Prints one JSON line.  `value` is the whole step's algorithmic bytes (bf16
+read + codes/metadata written by quantize; codes, metadata, bf16 window,
+rope, queries and outputs of attention) divided by the step time, in GB/s.
+`roofline` is for the dominant kernel (largest share of the step time), from
+per-launch HIP event timing on the launch stream.  `cpu_baseline` times the
+C oracle on a bounded sample of the same workload on the host cores.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 1]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "quantized-KV decode attn effective HBM GB/s + tokens/s; quantize GB/s"
+HBM_PEAK_GBS = 8000.0
+MFMA_F16_PEAK_TFLOPS = 2500.0
+MALL_BYTES = 256 << 20
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--workload", type=int, default=1, choices=[1, 2, 3, 4])
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    return p.parse_args()
+
+
+# ---------------------------------------------------------------------------
+def gpu_inputs(w, torch, seed: int):
+    """bf16 sources [A][Lmax][H][D] for K and V (and rope) of every layer,
+    N(0,1) with the workload's outlier channels, drawn on the GPU."""
+    import kvq_synth as syn
+    g = torch.Generator(device="cuda")
+    g.manual_seed(seed)
+    A, H, D = w.n_agents, w.n_kv_heads, w.head_dim
+    S = max(64 * b for b in w.n_blocks)
+    chans = syn.outlier_channels(w.wid, H, D, w.outliers) if w.outliers else None
+
+    def draw(shape, outl):
+        x = torch.randn(shape, generator=g, device="cuda", dtype=torch.float32)
+        if outl is not None:
+            for h, c in enumerate(outl):
+                x[..., h, torch.as_tensor(c, device="cuda")] *= w.outlier_gain
+        return x.to(torch.bfloat16).contiguous()
+
+    k = draw((A, S, H, D), chans)
+    v = None if w.rope_dim else draw((A, S, H, D), None)
+    return k, v
+
+
+def algorithmic_bytes(w, cache, n_q_heads):
+    """(quantize bytes for K+V, attention bytes) of one layer."""
+    import quantized_kv_cache_group_amd as kvq
+    H, D = w.n_kv_heads, w.head_dim
+    blocks = 0
+    qelems = 0
+    for a in range(w.n_agents):
+        for j in range(w.n_blocks[a]):
+            blocks += kvq.block_bytes(int(cache.bits_host[a, j]), H, D)
+        qelems += 64 * w.n_blocks[a] * H * D
+    n_t = 1 if w.rope_dim else 2                       # K and V, or the latent only
+    quant = n_t * (qelems * 2 + blocks)
+    attn = n_t * blocks
+    attn += n_t * sum(w.n_window) * H * D * 2           # bf16 window
+    attn += sum(w.lengths) * H * w.rope_dim * 2         # bf16 rope
+    if w.n_new:
+        Hq = n_q_heads
+        attn += w.n_new * (Hq + 2 * H) * D * 2 + w.n_new * Hq * D * 4
+    else:
+        attn += w.n_agents * n_q_heads * (D + w.rope_dim) * 2 + w.n_agents * n_q_heads * D * 4
+    return quant, attn
+
+
+def chunk_flops(w):
+    P = w.lengths[0]
+    visits = sum(P + i + 1 for i in range(w.n_new))
+    return visits * w.n_q_heads * 4 * w.head_dim
+
+
+# ---------------------------------------------------------------------------
+def cpu_baseline(w, layer_ids):
+    """Time the oracle on a bounded sample: quantize + attend for as many
+    agents as fit in about 20 s (for the chunk: the quantize of the cache and
+    a few query rows, the attention time scaled to all rows), as GB/s of the
+    same algorithmic traffic the GPU figure counts."""
+    import kvq_synth as syn
+    import oracle
+    oracle.lib()
+    H, D = w.n_kv_heads, w.head_dim
+    layer = layer_ids[0]
+    t_used, bytes_done, agents_done, note = 0.0, 0.0, 0, ""
+    for a in range(w.n_agents):
+        k = w.kv(a, layer, syn.TAG_K)
+        v = None if w.rope_dim else w.kv(a, layer, syn.TAG_V)
+        nb, nw = w.n_blocks[a], w.n_window[a]
+        bits = w.bits(a, layer)
+        off, tot = oracle.packed_offsets(bits, H, D)
+        pool = np.zeros(2 * tot if v is not None else tot, np.uint8)
+        voff = off + np.uint64(tot) if v is not None else None
+        kw = k[64 * nb:64 * nb + nw] if nw else None
+        vw = v[64 * nb:64 * nb + nw] if (nw and v is not None) else None
+        n_t = 1 if v is None else 2
+        blk = sum(oracle.block_bytes(int(b), H, D) for b in bits)
+        t0 = time.perf_counter()
+        oracle.quantize_seq(k, H, D, bits, off, pool)
+        if v is not None:
+            oracle.quantize_seq(v, H, D, bits, voff, pool)
+        tq = time.perf_counter() - t0
+        b_q = n_t * (64 * nb * H * D * 2 + blk)
+        if w.n_new:
+            qn, kn, vn = w.chunk_new()
+            rows = 4
+            t1 = time.perf_counter()
+            oracle.attend_chunk_seq(pool, bits, off, voff, kw, vw, H, D, qn, kn, vn, w.scale,
+                                    w.n_new - rows, w.n_new)
+            ta = (time.perf_counter() - t1) * (w.n_new / rows)
+            _, b_a = algorithmic_bytes(w, _FakeCache(w, [bits]), w.n_q_heads)
+            t_used += tq + ta
+            bytes_done += b_q + b_a
+            agents_done = 1
+            note = (f"; attention timed on the last {rows} of {w.n_new} query rows "
+                    f"and scaled by {w.n_new // rows}")
+            break
+        q = w.q(layer)[a]
+        rope = w.rope(a, layer) if w.rope_dim else None
+        t1 = time.perf_counter()
+        oracle.attend_decode_seq(pool, bits, off, voff, kw, vw, rope, H, D, q, w.scale)
+        t_used += tq + (time.perf_counter() - t1)
+        b_a = (n_t * blk + n_t * nw * H * D * 2 + w.lengths[a] * H * w.rope_dim * 2 +
+               w.n_q_heads * (D + w.rope_dim) * 2 + w.n_q_heads * D * 4)
+        bytes_done += b_q + b_a
+        agents_done += 1
+        if t_used > 20.0:
+            break
+    return {"value": round(bytes_done / t_used / 1e9, 4), "unit": "GB/s",
+            "cores": oracle.max_threads(), "kind": "oracle",
+            "sample": f"quantize + attend of {agents_done} of {w.n_agents} agents of layer {layer}: "
+                      f"{bytes_done / 1e6:.1f} MB of algorithmic traffic in {t_used:.2f} s{note}"}
+
+
+class _FakeCache:
+    def __init__(self, w, bits_list):
+        mb = max(w.n_blocks)
+        self.bits_host = np.full((w.n_agents, max(mb, 1)), 4, np.uint8)
+        for a, b in enumerate(bits_list):
+            self.bits_host[a, :b.size] = b
+
+
+# ---------------------------------------------------------------------------
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}); "
+              "the library has no multi-GPU path", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import kvq_synth as syn
+    import quantized_kv_cache_group_amd as kvq
+
+    kvq.lib()
+    torch.cuda.set_device(0)
+    w = syn.workload(args.workload)
+    H, D, A, Hq = w.n_kv_heads, w.head_dim, w.n_agents, w.n_q_heads
+    layers = w.layers if args.workload == 2 else [0]
+    latent = w.rope_dim > 0
+
+    # Cache copies per layer, rotated across steps.
+    caches_per_layer = []
+    for li, layer in enumerate(layers):
+        bits = [w.bits(a, layer) for a in range(A)]
+        caches_per_layer.append(bits)
+    q_bytes, a_bytes = 0, 0
+    per_layer_bytes = []
+    for bits in caches_per_layer:
+        fake = _FakeCache(w, bits)
+        qb, ab = algorithmic_bytes(w, fake, Hq)
+        per_layer_bytes.append((qb, ab))
+        q_bytes += qb
+        a_bytes += ab
+    footprint_one = a_bytes + q_bytes                 # bytes touched per step
+    R = max(2, int(np.ceil(2 * MALL_BYTES / max(footprint_one, 1))) + 1)
+    R = min(R, 12)
+    sets = []
+    for r in range(R):
+        cs = [kvq.LayerCache(H, D, w.n_blocks, w.n_window, bits, latent=latent, rope_dim=w.rope_dim)
+              for bits in caches_per_layer]
+        sets.append(cs)
+    n_src = 2 if len(layers) == 1 else 1
+    srcs = [[gpu_inputs(w, torch, 1000 * r + li) for li in range(len(layers))] for r in range(n_src)]
+    gq = torch.Generator(device="cuda")
+    gq.manual_seed(7)
+    if w.n_new:
+        qn = torch.randn((A, w.n_new, Hq, D), generator=gq, device="cuda").to(torch.bfloat16)
+        kn = torch.randn((A, w.n_new, H, D), generator=gq, device="cuda").to(torch.bfloat16)
+        vn = torch.randn((A, w.n_new, H, D), generator=gq, device="cuda").to(torch.bfloat16)
+        out = torch.empty((A, w.n_new, Hq, D), dtype=torch.float32, device="cuda")
+        ws = torch.empty(sets[0][0].chunk_workspace_bytes(Hq, w.n_new), dtype=torch.uint8, device="cuda")
+    else:
+        qs = [torch.randn((A, Hq, D + w.rope_dim), generator=gq, device="cuda").to(torch.bfloat16)
+              for _ in layers]
+        out = torch.empty((A, Hq, D), dtype=torch.float32, device="cuda")
+        ws = torch.empty(max(sets[0][0].decode_workspace_bytes(Hq), 256), dtype=torch.uint8,
+                         device="cuda")
+    # Windows and rope are bf16 storage: filled once per copy with N(0,1).
+    for cs in sets:
+        for c in cs:
+            for t in (c.k_window, c.v_window, c.rope):
+                if t is not None:
+                    t.normal_(generator=gq)
+    torch.cuda.synchronize()
+
+    stream = torch.cuda.current_stream()
+    ev = []
+
+    def step(i, record):
+        cs_w = sets[i % R]
+        cs_r = sets[(i + R // 2) % R]
+        src = srcs[i % n_src]
+        marks = []
+        for li in range(len(layers)):
+            k, v = src[li]
+            e0 = torch.cuda.Event(enable_timing=True) if record else None
+            if record:
+                e0.record(stream)
+            cs_w[li].quantize("k", k)
+            if v is not None:
+                cs_w[li].quantize("v", v)
+            e1 = torch.cuda.Event(enable_timing=True) if record else None
+            if record:
+                e1.record(stream)
+            if w.n_new:
+                cs_r[li].attend_chunk(qn, kn, vn, w.scale, out=out, workspace=ws)
+            else:
+                cs_r[li].attend_decode(qs[li], w.scale, out=out, workspace=ws)
+            e2 = torch.cuda.Event(enable_timing=True) if record else None
+            if record:
+                e2.record(stream)
+                marks.append((e0, e1, e2))
+        return marks
+
+    for i in range(args.warmup):
+        step(i, False)
+    torch.cuda.synchronize()
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    all_marks = []
+    t_start.record(stream)
+    for i in range(args.steps):
+        all_marks.append(step(args.warmup + i, True))
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    total_ms = t_start.elapsed_time(t_end)
+    ms_step = total_ms / args.steps
+    tq = [m[0].elapsed_time(m[1]) for ms in all_marks for m in ms]   # per layer, K (+V)
+    ta = [m[1].elapsed_time(m[2]) for ms in all_marks for m in ms]
+    n_launch_q = 1 if latent else 2
+    quant_launch_ms = float(np.mean(tq)) / n_launch_q
+    attn_ms = float(np.mean(ta))
+    step_bytes = q_bytes + a_bytes
+    value = step_bytes / (ms_step * 1e-3) / 1e9
+    quant_gbs = (q_bytes / len(layers)) / (float(np.mean(tq)) * 1e-3) / 1e9
+    attn_gbs = (a_bytes / len(layers)) / (attn_ms * 1e-3) / 1e9
+    res = {
+        "metric": METRIC, "value": round(value, 2), "unit": "GB/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": w.name, "agents": A, "layers": len(layers), "q_heads": Hq,
+                   "kv_heads": H, "head_dim": D, "cache_tokens": w.lengths if A <= 10 else None,
+                   "bits": "2/3/4/8 mixed, mean 3" if args.workload == 2 else 4, "group": 64,
+                   "rope_dim": w.rope_dim, "new_tokens": w.n_new,
+                   "rotated_copies": R},
+        "quantize_GBps": round(quant_gbs, 2),
+        "quantize_us_per_launch": round(quant_launch_ms * 1e3, 3),
+        "attn_us": round(attn_ms * 1e3, 3),
+        "attn_effective_GBps": round(attn_gbs, 2),
+    }
+    if w.n_new:
+        fl = chunk_flops(w)
+        res["chunk_TFLOPs"] = round(fl / (attn_ms * 1e-3) / 1e12, 2)
+        res["prefill_tokens_per_s"] = round(w.n_new / (attn_ms * 1e-3), 1)
+    else:
+        res["decode_tokens_per_s"] = round(A / (attn_ms * len(layers) * 1e-3), 1)
+    # Roofline of the dominant kernel.
+    if n_launch_q * quant_launch_ms >= attn_ms:
+        per_launch = (q_bytes / len(layers)) / n_launch_q
+        ach = per_launch / (quant_launch_ms * 1e-3) / 1e9
+        res["roofline"] = {"kernel": "kvq quantize", "bound": "hbm", "achieved": round(ach, 2),
+                           "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBS, 4),
+                           "traffic": None}
+    elif w.n_new:
+        fl = chunk_flops(w) / (attn_ms * 1e-3) / 1e12
+        res["roofline"] = {"kernel": "kvq attend_chunk", "bound": "mfma", "achieved": round(fl, 2),
+                           "peak": MFMA_F16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                           "frac": round(fl / MFMA_F16_PEAK_TFLOPS, 4), "traffic": None}
+    else:
+        res["roofline"] = {"kernel": "kvq attend_decode", "bound": "hbm",
+                           "achieved": round(attn_gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                           "frac": round(attn_gbs / HBM_PEAK_GBS, 4), "traffic": None}
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(w, layers)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

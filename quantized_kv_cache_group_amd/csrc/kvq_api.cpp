@@ -65,9 +65,11 @@ int hip_status(hipError_t e) { return e == hipSuccess ? KVQ_OK : KVQ_EHIP; }
 
 size_t round256(size_t b) { return (b + 255) / 256 * 256; }
 
-// Plan of one attention call.
+// Plan of one attention call: the generic kernel's decomposition, and for
+// decode also the tuned kernel's (the workspace covers whichever runs).
 struct Plan {
     int tok_per_tile, split_keys, n_splits, n_row_tiles;
+    int sb, dec_splits;         // tuned decode
     size_t ws_bytes;
 };
 
@@ -89,6 +91,11 @@ int plan_attention(const kvq_layout *L, int n_q_heads, int rope_dim, int n_new, 
     const size_t rows = (size_t)L->n_seqs * n_qtok * n_q_heads;
     if (rows > 0x7fffffffu) return KVQ_EUNSUPPORTED;
     pl->ws_bytes = round256(rows * (size_t)pl->n_splits * (size_t)(L->head_dim + 2) * sizeof(float));
+    if (n_new == 0) {
+        decode_gqa_plan(L->n_seqs, L->n_heads, L->max_blocks, L->window_cap, &pl->sb, &pl->dec_splits);
+        const size_t t = round256(rows * (size_t)pl->dec_splits * (size_t)(L->head_dim + 2) * sizeof(float));
+        if (t > pl->ws_bytes) pl->ws_bytes = t;
+    }
     return KVQ_OK;
 }
 
@@ -170,6 +177,22 @@ int kvq_attend_decode(const kvq_layout *L, const kvq_store *K, const kvq_store *
     if (!isfinite(softmax_scale)) return KVQ_EINVAL;
     if (workspace_bytes < pl.ws_bytes) return KVQ_ENOSPC;
     if (!workspace || !aligned(workspace, 256)) return KVQ_EINVAL;
+
+    if (V && rope_dim == 0 && decode_gqa_supported(L->head_dim)) {
+        DecodeArgs d{};
+        d.t = tables(L);
+        d.k = store(K);
+        d.v = store(V);
+        d.q = q;
+        d.out = out;
+        d.part = static_cast<float *>(workspace);
+        d.Hq = n_q_heads;
+        d.G = n_q_heads / L->n_heads;
+        d.SB = pl.sb;
+        d.n_splits = pl.dec_splits;
+        d.c = softmax_scale * 1.4426950408889634f;
+        return hip_status(launch_decode_gqa(d, static_cast<hipStream_t>(stream)));
+    }
 
     AttnArgs a{};
     a.t = tables(L);

@@ -63,10 +63,26 @@ struct AttnArgs {
     float *out;                 // [A][n_qtok][Hq][Dv]
 };
 
+// Tuned grouped-query decode (matrix cores), head_dim 64/128/256.
+struct DecodeArgs {
+    Tables t;
+    Store k, v;
+    const uint16_t *q;          // [A][Hq][D]
+    float *out;                 // [A][Hq][D]
+    float *part;                // [A*Hq][n_splits][D + 2]
+    int Hq, G;
+    int SB;                     // 64-token blocks per split
+    int n_splits;               // grid.x: block splits + 1 window split
+    float c;                    // softmax_scale * log2(e)
+};
+
 // Launchers (return hipError_t of the launch).
 hipError_t launch_quantize(const QuantArgs &a, hipStream_t s);
 hipError_t launch_dequantize(const DequantArgs &a, hipStream_t s);
 hipError_t launch_attend_generic(const AttnArgs &a, hipStream_t s);
+hipError_t launch_decode_gqa(const DecodeArgs &a, hipStream_t s);
+void decode_gqa_plan(int A, int H, int max_blocks, int window_cap, int *SB, int *n_splits);
+bool decode_gqa_supported(int D);
 
 // Generic path's split size and workspace.
 void generic_plan(int max_keys, int n_new, int G, int *tok_per_tile, int *split_keys, int *n_splits);
