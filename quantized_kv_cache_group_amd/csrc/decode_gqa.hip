@@ -30,139 +30,30 @@
 // tokens 8q..8q+7 of the step, which is exactly the B-operand layout P.V
 // needs; no shuffles move probabilities between lanes.
 #include "kvq_internal.h"
+#include "unpack.h"
 
 namespace kvq {
 namespace {
 
-typedef _Float16 h2 __attribute__((ext_vector_type(2)));
-typedef _Float16 h8 __attribute__((ext_vector_type(8)));
-typedef float f4 __attribute__((ext_vector_type(4)));
-typedef float f2 __attribute__((ext_vector_type(2)));
+using namespace dev;
 
-constexpr uint32_t MAGIC = 0x64006400u;   // fp16 1024.0 in both halves
 constexpr int VT_PAD = 8;                  // LDS row padding (halves)
 constexpr int STEP = 32;                   // tokens per step
-constexpr float LOG2E = 1.4426950408889634f;
-
-__device__ __forceinline__ h2 as_h2(uint32_t u) { return __builtin_bit_cast(h2, u); }
-__device__ __forceinline__ uint32_t u32_of(h2 h) { return __builtin_bit_cast(uint32_t, h); }
-__device__ __forceinline__ uint32_t perm(uint32_t hi, uint32_t lo, uint32_t sel)
-{
-    return __builtin_amdgcn_perm(hi, lo, sel);
-}
-__device__ __forceinline__ int clampi(int v, int lo, int hi) { return v < lo ? lo : (v > hi ? hi : v); }
-
-// Four fp16 pairs (c0,c4) (c1,c5) (c2,c6) (c3,c7) of one chunk of 8 codes,
-// as exact small integers in fp16.  `x` holds 1024 + m*c per half; the
-// constants undo the magic and the per-position multiplier m.
-struct Pairs {
-    h2 p[4];
-};
-
-template <int B>
-struct Unpack;
-
-template <>
-struct Unpack<4> {
-    // chunk: one dword, code i at bits 4i.
-    __device__ static __forceinline__ Pairs run(uint32_t w)
-    {
-        const uint32_t w8 = w >> 8;
-        const h2 x0 = as_h2((w & 0x000F000Fu) | MAGIC);
-        const h2 x1 = as_h2((w & 0x00F000F0u) | MAGIC);
-        const h2 x2 = as_h2((w8 & 0x000F000Fu) | MAGIC);
-        const h2 x3 = as_h2((w8 & 0x00F000F0u) | MAGIC);
-        const h2 one = {(_Float16)1.0f, (_Float16)1.0f}, m1024 = {(_Float16)-1024.0f, (_Float16)-1024.0f};
-        const h2 s16 = {(_Float16)0.0625f, (_Float16)0.0625f}, m64 = {(_Float16)-64.0f, (_Float16)-64.0f};
-        Pairs r;
-        r.p[0] = __builtin_elementwise_fma(x0, one, m1024);
-        r.p[1] = __builtin_elementwise_fma(x1, s16, m64);
-        r.p[2] = __builtin_elementwise_fma(x2, one, m1024);
-        r.p[3] = __builtin_elementwise_fma(x3, s16, m64);
-        return r;
-    }
-};
-
-template <>
-struct Unpack<2> {
-    // chunk: 16 bits (upper half of v zero), code i at bits 2i.
-    __device__ static __forceinline__ Pairs run(uint32_t v)
-    {
-        const uint32_t y = v | (v << 8);          // hi half: codes 4..7 at bits 0..7
-        Pairs r;
-#pragma unroll
-        for (int i = 0; i < 4; i++) {
-            const h2 x = as_h2((y & (0x00030003u << (2 * i))) | MAGIC);
-            const float inv = 1.0f / (float)(1 << (2 * i));
-            const h2 s = {(_Float16)inv, (_Float16)inv};
-            const h2 b = {(_Float16)(-1024.0f * inv), (_Float16)(-1024.0f * inv)};
-            r.p[i] = __builtin_elementwise_fma(x, s, b);
-        }
-        return r;
-    }
-};
-
-template <>
-struct Unpack<8> {
-    // chunk: two dwords, code i at byte i.
-    __device__ static __forceinline__ Pairs run2(uint32_t w0, uint32_t w1)
-    {
-        const h2 one = {(_Float16)1.0f, (_Float16)1.0f}, m1024 = {(_Float16)-1024.0f, (_Float16)-1024.0f};
-        Pairs r;
-#pragma unroll
-        for (int i = 0; i < 4; i++) {
-            const uint32_t sel = 0x0C000C00u | ((uint32_t)(4 + i) << 16) | (uint32_t)i;
-            r.p[i] = __builtin_elementwise_fma(as_h2(perm(w1, w0, sel) | MAGIC), one, m1024);
-        }
-        return r;
-    }
-};
-
-template <>
-struct Unpack<3> {
-    // chunk: 3 bytes starting at byte r of the 8 bytes {lo, hi}; code i at
-    // bits 3i of those 24 bits.
-    __device__ static __forceinline__ Pairs run3(uint32_t lo, uint32_t hi, int r)
-    {
-        const uint32_t z = perm(hi, lo, ((uint32_t)(r + 2) << 24) | ((uint32_t)(r + 1) << 16) |
-                                            ((uint32_t)(r + 1) << 8) | (uint32_t)r);
-        const uint32_t z2 = perm(hi, lo, 0x0C000000u | ((uint32_t)(r + 2) << 16) |
-                                             ((uint32_t)(r + 2) << 8) | (uint32_t)(r + 1));
-        const h2 x0 = as_h2((z & 0x00700007u) | MAGIC);                 // c0 x1,  c4 x16
-        const h2 x1 = as_h2((z & 0x03800038u) | MAGIC);                 // c1 x8,  c5 x128
-        const h2 x2 = as_h2((z & 0x000001C0u) | (z2 & 0x001C0000u) | MAGIC);  // c2 x64, c6 x4
-        const h2 x3 = as_h2((z2 & 0x00E0000Eu) | MAGIC);                // c3 x2,  c7 x32
-        Pairs o;
-        o.p[0] = __builtin_elementwise_fma(x0, h2{(_Float16)1.0f, (_Float16)0.0625f},
-                                           h2{(_Float16)-1024.0f, (_Float16)-64.0f});
-        o.p[1] = __builtin_elementwise_fma(x1, h2{(_Float16)0.125f, (_Float16)0.0078125f},
-                                           h2{(_Float16)-128.0f, (_Float16)-8.0f});
-        o.p[2] = __builtin_elementwise_fma(x2, h2{(_Float16)0.015625f, (_Float16)0.25f},
-                                           h2{(_Float16)-16.0f, (_Float16)-256.0f});
-        o.p[3] = __builtin_elementwise_fma(x3, h2{(_Float16)0.5f, (_Float16)0.03125f},
-                                           h2{(_Float16)-512.0f, (_Float16)-32.0f});
-        return o;
-    }
-};
 
 // A lane's share of one token row: chunks [q*2NG, (q+1)*2NG) of 8 codes
-// (d in [16*NG*q, 16*NG*(q+1))), loaded as dwords.
+// (d in [16*NG*q, 16*NG*(q+1))), held as NDW dwords.
 template <int B, int NG>
-struct RowLoad {
+struct Row {
     static constexpr int BYTES = 2 * NG * B;                 // codes bytes of the lane
     static constexpr bool ODD = (B == 3 && NG == 1);         // 6 bytes at offset 6q
     static constexpr int NDW = ODD ? 2 : BYTES / 4;
-    uint32_t w[NDW];
-    int r0;                                                  // byte offset of chunk 0 in w
 
-    __device__ __forceinline__ void load(const uint8_t *row, int q)
+    __device__ static __forceinline__ void load(uint32_t *w, const uint8_t *row, int q)
     {
         if constexpr (ODD) {
-            const int off = 6 * q;
-            const uint32_t *p = reinterpret_cast<const uint32_t *>(row + (off & ~3));
+            const uint32_t *p = reinterpret_cast<const uint32_t *>(row + ((6 * q) & ~3));
             w[0] = p[0];
             w[1] = p[1];
-            r0 = off & 3;
         } else {
             const uint8_t *base = row + q * BYTES;
             if constexpr (BYTES % 16 == 0) {
@@ -181,12 +72,11 @@ struct RowLoad {
 #pragma unroll
                 for (int i = 0; i < NDW; i++) w[i] = reinterpret_cast<const uint32_t *>(base)[i];
             }
-            r0 = 0;
         }
     }
 
     // Exact codes of chunk c as fp16 pairs.
-    __device__ __forceinline__ Pairs chunk(int c) const
+    __device__ static __forceinline__ Pairs chunk(const uint32_t *w, int q, int c)
     {
         if constexpr (B == 4) {
             return Unpack<4>::run(w[c]);
@@ -195,29 +85,19 @@ struct RowLoad {
             return Unpack<2>::run((c & 1) ? (d >> 16) : (d & 0xffffu));
         } else if constexpr (B == 8) {
             return Unpack<8>::run2(w[2 * c], w[2 * c + 1]);
+        } else if constexpr (ODD) {
+            const int o = ((6 * q) & 3) + 3 * c;               // o <= 5
+            return Unpack<3>::run3(o >= 4 ? w[1] : w[0], w[1], o & 3);
         } else {
-            if constexpr (ODD) {
-                const int o = r0 + 3 * c;          // o <= 5
-                return Unpack<3>::run3(o >= 4 ? w[1] : w[0], w[1], o & 3);
-            } else {
-                const int o = 3 * c;
-                const int i = o >> 2;
-                const uint32_t lo = w[i];
-                const uint32_t hi = (i + 1 < NDW) ? w[i + 1] : w[i];
-                return Unpack<3>::run3(lo, hi, o & 3);
-            }
+            const int o = 3 * c;
+            const int i = o >> 2;
+            const uint32_t lo = w[i];
+            const uint32_t hi = (i + 1 < NDW) ? w[i + 1] : w[i];
+            return Unpack<3>::run3(lo, hi, o & 3);
         }
     }
 };
 
-// Dequantized fp16 values of a chunk: pairs (c0,c4) .. (c3,c7) -> fma(c, s, b).
-__device__ __forceinline__ void dequant(Pairs &pr, uint32_t meta)
-{
-    const h2 sb = as_h2(meta);
-    const h2 s = {sb[0], sb[0]}, b = {sb[1], sb[1]};
-#pragma unroll
-    for (int i = 0; i < 4; i++) pr.p[i] = __builtin_elementwise_fma(pr.p[i], s, b);
-}
 
 __device__ __forceinline__ h8 operand(const Pairs &pr)
 {
@@ -243,35 +123,52 @@ struct DecodeState {
     float m_run, l_run;                      // log2-domain running max, running sum
 };
 
-// One 32-token step of a quantized block (half = which 32 tokens of the 64):
-// S^T tiles into s[0..1], V^T rows into LDS.
-template <int B, int NG>
-__device__ __forceinline__ void step_block(const DecodeState<NG> &st, const uint8_t *kblk,
-                                           const uint8_t *vblk, int H, int g, int half,
-                                           _Float16 *vt, f4 s[2])
+// Registers of one 32-token step of a quantized block, loaded ahead of use.
+// Sized for widths up to 4 bits; 8-bit blocks load at compute time instead.
+template <int NG>
+struct Raw {
+    static constexpr int KW = 2 * NG;        // dwords per (tensor, tile) at 4 bits
+    uint32_t k[2][KW], v[2][KW];
+    uint32_t km[2], vm[2];
+};
+
+__device__ __forceinline__ size_t step_row(int g, int half, int m, int tau)
 {
-    constexpr int D = 64 * NG, KS = 2 * NG;
-    constexpr int CODE_ROW = D * B / 8;
+    return (size_t)g * 64 + 32 * half + tile_token(m, tau);
+}
+
+template <int B, int NG>
+__device__ __forceinline__ void load_step(Raw<NG> &r, const uint8_t *kblk, const uint8_t *vblk,
+                                          int H, int g, int half)
+{
+    constexpr int CODE_ROW = 64 * NG * B / 8;
     const int lane = threadIdx.x, m = lane & 15, q = lane >> 4;
     const size_t meta0 = (size_t)H * 64 * CODE_ROW;
     const int grp = (NG * q) >> 2;           // group of the lane's dims [16*NG*q, 16*NG*(q+1))
-
-    RowLoad<B, NG> kl[2], vl[2];
-    uint32_t km[2], vm[2];
 #pragma unroll
     for (int tau = 0; tau < 2; tau++) {
-        const size_t row = (size_t)g * 64 + 32 * half + tile_token(m, tau);
-        kl[tau].load(kblk + row * CODE_ROW, q);
-        vl[tau].load(vblk + row * CODE_ROW, q);
-        km[tau] = reinterpret_cast<const uint32_t *>(kblk + meta0)[row * NG + grp];
-        vm[tau] = reinterpret_cast<const uint32_t *>(vblk + meta0)[row * NG + grp];
+        const size_t row = step_row(g, half, m, tau);
+        Row<B, NG>::load(r.k[tau], kblk + row * CODE_ROW, q);
+        Row<B, NG>::load(r.v[tau], vblk + row * CODE_ROW, q);
+        r.km[tau] = reinterpret_cast<const uint32_t *>(kblk + meta0)[row * NG + grp];
+        r.vm[tau] = reinterpret_cast<const uint32_t *>(vblk + meta0)[row * NG + grp];
     }
+}
+
+// S^T tiles of the step into s[0..1]; V^T rows of the step into LDS.
+template <int B, int NG, int W>
+__device__ __forceinline__ void compute_rows(const DecodeState<NG> &st, const uint32_t (&kw)[2][W],
+                                             const uint32_t (&vw)[2][W], const uint32_t km[2],
+                                             const uint32_t vm[2], _Float16 *vt, f4 s[2])
+{
+    constexpr int KS = 2 * NG;
+    const int lane = threadIdx.x, m = lane & 15, q = lane >> 4;
 #pragma unroll
     for (int tau = 0; tau < 2; tau++) {
         f4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int k = 0; k < KS; k++) {
-            Pairs pr = kl[tau].chunk(k);
+            Pairs pr = Row<B, NG>::chunk(kw[tau], q, k);
             dequant(pr, km[tau]);
             acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(operand(pr), st.qop[k], acc, 0, 0, 0);
         }
@@ -282,7 +179,7 @@ __device__ __forceinline__ void step_block(const DecodeState<NG> &st, const uint
         const int t = tile_token(m, tau);
 #pragma unroll
         for (int k = 0; k < KS; k++) {
-            Pairs pr = vl[tau].chunk(k);
+            Pairs pr = Row<B, NG>::chunk(vw[tau], q, k);
             dequant(pr, vm[tau]);
             const int d0 = 8 * (q * KS + k);
 #pragma unroll
@@ -294,19 +191,29 @@ __device__ __forceinline__ void step_block(const DecodeState<NG> &st, const uint
     }
 }
 
-__device__ __forceinline__ float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
-__device__ __forceinline__ float bf_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
-
-// Pairs (e0,e4) (e1,e5) (e2,e6) (e3,e7) of 8 bf16 values, as fp16.
-__device__ __forceinline__ Pairs bf16_pairs(uint4 v)
+// 8-bit blocks: load and compute in place (no prefetch registers).
+template <int NG>
+__device__ __forceinline__ void step_block8(const DecodeState<NG> &st, const uint8_t *kblk,
+                                            const uint8_t *vblk, int H, int g, int half,
+                                            _Float16 *vt, f4 s[2])
 {
-    Pairs r;
-    r.p[0] = __builtin_convertvector(f2{bf_lo(v.x), bf_lo(v.z)}, h2);
-    r.p[1] = __builtin_convertvector(f2{bf_hi(v.x), bf_hi(v.z)}, h2);
-    r.p[2] = __builtin_convertvector(f2{bf_lo(v.y), bf_lo(v.w)}, h2);
-    r.p[3] = __builtin_convertvector(f2{bf_hi(v.y), bf_hi(v.w)}, h2);
-    return r;
+    constexpr int W = Row<8, NG>::NDW;
+    constexpr int CODE_ROW = 64 * NG;
+    const int lane = threadIdx.x, m = lane & 15, q = lane >> 4;
+    const size_t meta0 = (size_t)H * 64 * CODE_ROW;
+    const int grp = (NG * q) >> 2;
+    uint32_t kw[2][W], vw[2][W], km[2], vm[2];
+#pragma unroll
+    for (int tau = 0; tau < 2; tau++) {
+        const size_t row = step_row(g, half, m, tau);
+        Row<8, NG>::load(kw[tau], kblk + row * CODE_ROW, q);
+        Row<8, NG>::load(vw[tau], vblk + row * CODE_ROW, q);
+        km[tau] = reinterpret_cast<const uint32_t *>(kblk + meta0)[row * NG + grp];
+        vm[tau] = reinterpret_cast<const uint32_t *>(vblk + meta0)[row * NG + grp];
+    }
+    compute_rows<8, NG, W>(st, kw, vw, km, vm, vt, s);
 }
+
 
 // One 32-token step of the bf16 window, tokens t0 .. t0+31 (rows past nw are
 // read from row nw-1 and masked by the caller).
@@ -398,11 +305,6 @@ __device__ __forceinline__ void softmax_pv(DecodeState<NG> &st, const f4 s[2], i
     __syncthreads();                          // reads done before the next step writes
 }
 
-__device__ __forceinline__ int seq_blocks(const Tables &t, int a) { return clampi(t.n_blocks[a], 0, t.max_blocks); }
-__device__ __forceinline__ int seq_window(const Tables &t, int a)
-{
-    return t.n_window ? clampi(t.n_window[a], 0, t.window_cap) : 0;
-}
 
 template <int NG>
 __global__ __launch_bounds__(64) void decode_gqa_split(DecodeArgs p)
@@ -435,23 +337,43 @@ __global__ __launch_bounds__(64) void decode_gqa_split(DecodeArgs p)
     st.l_run = 0.0f;
 
     if (!win) {
-        const int j1 = min((s + 1) * p.SB, nb);
-        for (int j = s * p.SB; j < j1; j++) {
-            const size_t e = (size_t)a * p.t.max_blocks + j;
+        const int j0 = s * p.SB;
+        const int n_steps = 2 * (min(j0 + p.SB, nb) - j0);
+        const uint8_t *kbase = p.k.pool, *vbase = p.v.pool;
+        const size_t e0 = (size_t)a * p.t.max_blocks + j0;
+        const int H = p.t.H;
+        Raw<NG> ra, rb;
+        auto issue = [&](Raw<NG> &r, int i) {
+            const size_t e = e0 + (i >> 1);
             const int b = p.t.bits[e];
-            const uint8_t *kb = p.k.pool + p.k.offset[e];
-            const uint8_t *vb = p.v.pool + p.v.offset[e];
-#pragma unroll 1
-            for (int half = 0; half < 2; half++) {
-                f4 sc[2];
-                switch (b) {
-                case 2: step_block<2, NG>(st, kb, vb, p.t.H, g, half, vt, sc); break;
-                case 3: step_block<3, NG>(st, kb, vb, p.t.H, g, half, vt, sc); break;
-                case 4: step_block<4, NG>(st, kb, vb, p.t.H, g, half, vt, sc); break;
-                default: step_block<8, NG>(st, kb, vb, p.t.H, g, half, vt, sc); break;
-                }
-                softmax_pv<NG>(st, sc, STEP, vt, p.c);
+            const uint8_t *kb = kbase + p.k.offset[e], *vb = vbase + p.v.offset[e];
+            switch (b) {
+            case 2: load_step<2, NG>(r, kb, vb, H, g, i & 1); break;
+            case 3: load_step<3, NG>(r, kb, vb, H, g, i & 1); break;
+            case 4: load_step<4, NG>(r, kb, vb, H, g, i & 1); break;
+            default: break;                       // 8-bit: loaded at compute time
             }
+        };
+        auto run = [&](const Raw<NG> &r, int i) {
+            const size_t e = e0 + (i >> 1);
+            const int b = p.t.bits[e];
+            f4 sc[2];
+            switch (b) {
+            case 2: compute_rows<2, NG, Raw<NG>::KW>(st, r.k, r.v, r.km, r.vm, vt, sc); break;
+            case 3: compute_rows<3, NG, Raw<NG>::KW>(st, r.k, r.v, r.km, r.vm, vt, sc); break;
+            case 4: compute_rows<4, NG, Raw<NG>::KW>(st, r.k, r.v, r.km, r.vm, vt, sc); break;
+            default:
+                step_block8<NG>(st, kbase + p.k.offset[e], vbase + p.v.offset[e], H, g, i & 1, vt, sc);
+                break;
+            }
+            softmax_pv<NG>(st, sc, STEP, vt, p.c);
+        };
+        if (n_steps > 0) issue(ra, 0);
+        for (int i = 0; i < n_steps; i += 2) {
+            issue(rb, i + 1);                     // every block has two steps
+            run(ra, i);
+            if (i + 2 < n_steps) issue(ra, i + 2);
+            run(rb, i + 1);
         }
     } else {
         const uint16_t *kw = p.k.window + (size_t)a * p.t.window_cap * p.t.H * D;
@@ -477,26 +399,60 @@ __global__ __launch_bounds__(64) void decode_gqa_split(DecodeArgs p)
 }
 
 // Combine the splits of one (sequence, query head): max-rescaled sums in the
-// log2 domain of the split kernel.
-__global__ __launch_bounds__(64) void decode_gqa_merge(DecodeArgs p)
+// log2 domain of the split kernel.  One wave per row: lanes first reduce the
+// split maxima and sums, keep the split weights in LDS, then stream the
+// partial outputs with independent loads.
+constexpr int MERGE_ROWS = 4;
+constexpr int MAX_SPLITS = 512;
+
+__global__ __launch_bounds__(64 * MERGE_ROWS) void decode_gqa_merge(DecodeArgs p)
 {
-    const int row = blockIdx.x;
+    __shared__ float wsh[MERGE_ROWS][MAX_SPLITS];
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int row = blockIdx.x * MERGE_ROWS + wave;
+    if (row >= p.t.A * p.Hq) return;
     const int a = row / p.Hq;
     const int D = p.t.D;
     const int nb = seq_blocks(p.t, a), nw = seq_window(p.t, a);
     const int ns = (nb + p.SB - 1) / p.SB + (nw > 0 ? 1 : 0);
-    const float *pr = p.part + (size_t)row * p.n_splits * (D + 2);
+    const size_t stride = (size_t)(D + 2);
+    const float *pr = p.part + (size_t)row * p.n_splits * stride;
     float M = -INFINITY;
-    for (int s = 0; s < ns; s++) M = fmaxf(M, pr[(size_t)s * (D + 2)]);
+    for (int s = lane; s < ns; s += 64) M = fmaxf(M, pr[s * stride]);
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) M = fmaxf(M, __shfl_xor(M, o));
     float L = 0.0f;
-    for (int s = 0; s < ns; s++) L += __builtin_amdgcn_exp2f(pr[(size_t)s * (D + 2)] - M) * pr[(size_t)s * (D + 2) + 1];
+    for (int s = lane; s < ns; s += 64) {
+        const float w = __builtin_amdgcn_exp2f(pr[s * stride] - M);
+        wsh[wave][s] = w;
+        L += w * pr[s * stride + 1];
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) L += __shfl_xor(L, o);
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     const float inv = L > 0.0f ? 1.0f / L : 0.0f;
     float *o = p.out + (size_t)row * D;
-    for (int d = threadIdx.x; d < D; d += 64) {
-        float acc = 0.0f;
-        for (int s = 0; s < ns; s++)
-            acc += __builtin_amdgcn_exp2f(pr[(size_t)s * (D + 2)] - M) * pr[(size_t)s * (D + 2) + 2 + d];
-        o[d] = acc * inv;
+    for (int d = 2 * lane; d < D; d += 128) {
+        float ax = 0.0f, ay = 0.0f;
+        int s = 0;
+        for (; s + 4 <= ns; s += 4) {
+            float2 v[4];
+#pragma unroll
+            for (int u = 0; u < 4; u++) v[u] = *reinterpret_cast<const float2 *>(pr + (s + u) * stride + 2 + d);
+#pragma unroll
+            for (int u = 0; u < 4; u++) {
+                const float w = wsh[wave][s + u];
+                ax += w * v[u].x;
+                ay += w * v[u].y;
+            }
+        }
+        for (; s < ns; s++) {
+            const float2 v = *reinterpret_cast<const float2 *>(pr + s * stride + 2 + d);
+            ax += wsh[wave][s] * v.x;
+            ay += wsh[wave][s] * v.y;
+        }
+        *reinterpret_cast<float2 *>(o + d) = make_float2(ax * inv, ay * inv);
     }
 }
 
@@ -506,6 +462,10 @@ void decode_gqa_plan(int A, int H, int max_blocks, int window_cap, int *SB, int 
 {
     int sb = 16;
     while (sb > 1 && (long)A * H * ((max_blocks + sb - 1) / sb) < 2048) sb >>= 1;
+#ifdef KVQ_DECODE_SB
+    sb = KVQ_DECODE_SB;                     // build-time tuning override
+#endif
+    while ((max_blocks + sb - 1) / sb + 1 > MAX_SPLITS) sb <<= 1;
     *SB = sb;
     *n_splits = (max_blocks + sb - 1) / sb + (window_cap > 0 ? 1 : 0);
     if (*n_splits < 1) *n_splits = 1;
@@ -524,7 +484,12 @@ hipError_t launch_decode_gqa(const DecodeArgs &p, hipStream_t s)
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    decode_gqa_merge<<<dim3(p.t.A * p.Hq), 64, 0, s>>>(p);
+    return launch_decode_merge(p, s);
+}
+
+hipError_t launch_decode_merge(const DecodeArgs &p, hipStream_t s)
+{
+    decode_gqa_merge<<<dim3((p.t.A * p.Hq + MERGE_ROWS - 1) / MERGE_ROWS), 64 * MERGE_ROWS, 0, s>>>(p);
     return hipGetLastError();
 }
 

@@ -191,7 +191,13 @@ int kvq_attend_decode(const kvq_layout *L, const kvq_store *K, const kvq_store *
         d.SB = pl.sb;
         d.n_splits = pl.dec_splits;
         d.c = softmax_scale * 1.4426950408889634f;
-        return hip_status(launch_decode_gqa(d, static_cast<hipStream_t>(stream)));
+        hipStream_t hs = static_cast<hipStream_t>(stream);
+        if (decode_g4_supported(L->head_dim, d.G)) {
+            hipError_t e = launch_decode_g4(d, hs);
+            if (e != hipSuccess) return KVQ_EHIP;
+            return hip_status(launch_decode_merge(d, hs));
+        }
+        return hip_status(launch_decode_gqa(d, hs));
     }
 
     AttnArgs a{};

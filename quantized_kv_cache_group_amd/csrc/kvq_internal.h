@@ -80,7 +80,10 @@ struct DecodeArgs {
 hipError_t launch_quantize(const QuantArgs &a, hipStream_t s);
 hipError_t launch_dequantize(const DequantArgs &a, hipStream_t s);
 hipError_t launch_attend_generic(const AttnArgs &a, hipStream_t s);
-hipError_t launch_decode_gqa(const DecodeArgs &a, hipStream_t s);
+hipError_t launch_decode_gqa(const DecodeArgs &a, hipStream_t s);     // split + merge
+hipError_t launch_decode_g4(const DecodeArgs &a, hipStream_t s);      // split only (G <= 4)
+hipError_t launch_decode_merge(const DecodeArgs &a, hipStream_t s);
+bool decode_g4_supported(int D, int G);
 void decode_gqa_plan(int A, int H, int max_blocks, int window_cap, int *SB, int *n_splits);
 bool decode_gqa_supported(int D);
 
