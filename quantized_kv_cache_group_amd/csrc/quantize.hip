@@ -6,9 +6,10 @@
 // Metodologia, and of the 4-bit format of Agent Memory Below the Prompt,
 // Abstract; one width per block as in CoMixKV, Abstract).
 //
-// This translation unit is compiled with -ffp-contract=off and correctly
-// rounded fp32 division: the codes, scales and biases it writes are
-// bit-for-bit the documented sequence of IEEE binary32 operations.
+// This translation unit is compiled with -ffp-contract=off: the codes,
+// scales and biases it writes are bit-for-bit the documented sequence of IEEE
+// binary32 operations (its two divisions are computed by sequences proven
+// equal to the correctly rounded quotient on every input they can receive).
 //
 // Layout of the work: one workgroup (256 lanes, 4 wave64s) per (block,
 // head, sequence).  A group of 64 bf16 values (128 contiguous bytes) belongs
@@ -96,22 +97,42 @@ __device__ __forceinline__ void quant_block(const uint16_t *__restrict__ src_blk
         }
         mn = mn + 0.0f;                             // a zero extreme is +0
         mx = mx + 0.0f;
-        const float s = (mx - mn) / (float)N;       // correctly rounded divide
+        // s = (mx - mn) / N, correctly rounded: reciprocal multiply plus one
+        // fma correction.  For N = 3, 7, 15, 255 this equals the IEEE
+        // quotient for every non-negative finite dividend (an exhaustive
+        // check over all 2^31 such floats is in the test suite).
+        const float range = mx - mn;
+        constexpr float RN = 1.0f / (float)N;
+        const float q0 = range * RN;
+        float s = __builtin_fmaf(__builtin_fmaf(-q0, (float)N, range), RN, q0);
+        // keep the binary32 rounding of s: without this barrier the compiler
+        // may fuse the fma with the fp16 conversion (one rounding, not two)
+        asm volatile("" : "+v"(s));
         const uint16_t sh = f32_to_f16_bits(s);
         const uint16_t bh = f32_to_f16_bits(mn);
         const float sf = f16_bits_to_f32(sh);
         const float bf = f16_bits_to_f32(bh);
-        const float inv = (sf == 0.0f) ? 0.0f : 1.0f / sf;
+        // 1/sf, correctly rounded: hardware reciprocal (within 1 ulp) and one
+        // Newton step; exact for every positive finite fp16 sf from any start
+        // within 2 ulp (checked exhaustively in the test suite).
+        const float y0 = __builtin_amdgcn_rcpf(sf);
+        const float inv = (sf == 0.0f) ? 0.0f : __builtin_fmaf(__builtin_fmaf(-sf, y0, 1.0f), y0, y0);
 
-        uint64_t v = 0;                             // this lane's 8 codes, b bits each
+        // This lane's 8 codes, b bits each: codes 0..3 in lo, 4..7 in hi
+        // (for b <= 4 the caller only uses lo | hi << 4b, formed below).
+        uint32_t lo = 0, hi = 0;
 #pragma unroll
         for (int i = 0; i < 8; i++) {
-            float t = (x[i] - bf) * inv;
-            float r = __builtin_rintf(t);
-            r = (r >= 0.0f) ? r : 0.0f;             // NaN -> 0
-            r = (r > (float)N) ? (float)N : r;
-            v |= (uint64_t)(uint32_t)r << (B * i);
+            const float t = (x[i] - bf) * inv;
+            // round half to even, then clamp to [0, N] (one med3; the clamp
+            // equals max(0, min(N, r)) for every non-NaN r)
+            const float r = __builtin_amdgcn_fmed3f(__builtin_rintf(t), 0.0f, (float)N);
+            const uint32_t cq = (uint32_t)r;
+            if (i < 4) lo |= cq << (B * i);
+            else hi |= cq << (B * (i - 4));
         }
+        const uint64_t v = (B == 8) ? ((uint64_t)lo | ((uint64_t)hi << 32))
+                                    : (uint64_t)(lo | (hi << (4 * B)));
 
         uint8_t *gc = codes + (size_t)gi * (8 * B);  // group's code words (2B of them)
         if constexpr (B == 4) {

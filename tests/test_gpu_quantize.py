@@ -118,3 +118,21 @@ def test_quantize_deterministic():
     b.cache.quantize("k", to_dev_bf16(buf))
     torch.cuda.synchronize()
     assert torch.equal(p1, b.cache.k_pool)
+
+
+@pytest.mark.parametrize("bits", [2, 3, 4, 8])
+def test_quantize_scale_sweep(bits):
+    """Groups whose ranges sweep every binade from fp16-subnormal steps to
+    the fp16 limit, with random offsets: scales, biases and codes bit-exact."""
+    r = np.random.default_rng(1000 + bits)
+    n_blocks, H, D = 48, 2, 128
+    L = 64 * n_blocks
+    x = r.standard_normal((L, H, D)).astype(np.float32)
+    e = r.uniform(-30, 15, size=(L, H, D // 64, 1)).astype(np.float32)
+    off = r.uniform(-1, 1, size=(L, H, D // 64, 1)).astype(np.float32)
+    g = x.reshape(L, H, D // 64, 64)
+    g = (g * np.exp2(e) + off * np.exp2(e + r.uniform(0, 4))).astype(np.float32)
+    g = np.clip(g, -60000, 60000)
+    k = syn.bf16_bits(g.reshape(L, H, D))
+    b = build(H, D, [L], bits=[np.full(n_blocks, bits, np.uint8)], k_src=[k], v_src=[k])
+    gpu_pool_matches(b)
