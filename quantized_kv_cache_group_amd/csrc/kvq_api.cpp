@@ -70,6 +70,8 @@ size_t round256(size_t b) { return (b + 255) / 256 * 256; }
 struct Plan {
     int tok_per_tile, split_keys, n_splits, n_row_tiles;
     int sb, dec_splits;         // tuned decode
+    int ch_row_tiles, ch_splits, ch_split_tiles;   // tuned chunk
+    bool ch_ok;
     size_t ws_bytes;
 };
 
@@ -95,6 +97,26 @@ int plan_attention(const kvq_layout *L, int n_q_heads, int rope_dim, int n_new, 
         decode_gqa_plan(L->n_seqs, L->n_heads, L->max_blocks, L->window_cap, &pl->sb, &pl->dec_splits);
         const size_t t = round256(rows * (size_t)pl->dec_splits * (size_t)(L->head_dim + 2) * sizeof(float));
         if (t > pl->ws_bytes) pl->ws_bytes = t;
+    }
+    pl->ch_ok = false;
+    if (n_new > 0 && chunk_supported(L->head_dim)) {
+        const int R = chunk_rows_per_wg(L->head_dim);
+        const int64_t row_tiles = ((int64_t)n_new * G + R - 1) / R;
+        const int64_t tiles = (max_keys + 63) / 64;
+        const int64_t units = row_tiles * L->n_heads * L->n_seqs;
+        if (row_tiles * L->n_heads <= kMaxGrid) {
+            int64_t ns = (512 + units - 1) / units;
+            if (ns > tiles) ns = tiles;
+            if (ns < 1) ns = 1;
+            const int64_t st = (tiles + ns - 1) / ns;
+            ns = (tiles + st - 1) / st;
+            pl->ch_row_tiles = (int)row_tiles;
+            pl->ch_split_tiles = (int)st;
+            pl->ch_splits = (int)ns;
+            pl->ch_ok = true;
+            const size_t t = round256(rows * (size_t)ns * (size_t)(L->head_dim + 2) * sizeof(float));
+            if (t > pl->ws_bytes) pl->ws_bytes = t;
+        }
     }
     return KVQ_OK;
 }
@@ -255,6 +277,26 @@ int kvq_attend_chunk(const kvq_layout *L, const kvq_store *K, const kvq_store *V
     if (n_new == 0) return KVQ_OK;
     if (workspace_bytes < pl.ws_bytes) return KVQ_ENOSPC;
     if (!workspace || !aligned(workspace, 256)) return KVQ_EINVAL;
+
+    if (pl.ch_ok) {
+        ChunkArgs c{};
+        c.t = tables(L);
+        c.k = store(K);
+        c.v = store(V);
+        c.q_new = q_new;
+        c.k_new = k_new;
+        c.v_new = v_new;
+        c.n_new = n_new;
+        c.Hq = n_q_heads;
+        c.G = n_q_heads / L->n_heads;
+        c.c = softmax_scale * 1.4426950408889634f;
+        c.n_row_tiles = pl.ch_row_tiles;
+        c.n_splits = pl.ch_splits;
+        c.split_tiles = pl.ch_split_tiles;
+        c.part = static_cast<float *>(workspace);
+        c.out = out;
+        return hip_status(launch_chunk(c, static_cast<hipStream_t>(stream)));
+    }
 
     AttnArgs a{};
     a.t = tables(L);

@@ -76,6 +76,22 @@ struct DecodeArgs {
     float c;                    // softmax_scale * log2(e)
 };
 
+// Chunk attention (matrix cores), head_dim 64/128/256.
+struct ChunkArgs {
+    Tables t;
+    Store k, v;
+    const uint16_t *q_new;      // [A][n_new][Hq][D]
+    const uint16_t *k_new;      // [A][n_new][H][D]
+    const uint16_t *v_new;
+    int n_new, Hq, G;
+    float c;                    // softmax_scale * log2(e)
+    int n_row_tiles;            // query-row tiles per (sequence, KV head)
+    int n_splits;               // key splits (grid.x)
+    int split_tiles;            // 64-key tiles per split
+    float *part;                // [A*n_new*Hq][n_splits][D + 2]
+    float *out;                 // [A][n_new][Hq][D]
+};
+
 // Launchers (return hipError_t of the launch).
 hipError_t launch_quantize(const QuantArgs &a, hipStream_t s);
 hipError_t launch_dequantize(const DequantArgs &a, hipStream_t s);
@@ -84,6 +100,9 @@ hipError_t launch_decode_gqa(const DecodeArgs &a, hipStream_t s);     // split +
 hipError_t launch_decode_g4(const DecodeArgs &a, hipStream_t s);      // split only (G <= 4)
 hipError_t launch_decode_merge(const DecodeArgs &a, hipStream_t s);
 bool decode_g4_supported(int D, int G);
+hipError_t launch_chunk(const ChunkArgs &a, hipStream_t s);          // split + merge
+bool chunk_supported(int D);
+int chunk_rows_per_wg(int D);
 void decode_gqa_plan(int A, int H, int max_blocks, int window_cap, int *SB, int *n_splits);
 bool decode_gqa_supported(int D);
 
