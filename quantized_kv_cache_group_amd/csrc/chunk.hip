@@ -57,8 +57,9 @@ __device__ __forceinline__ int vpos(int k)
     return h32 + 8 * ((kk & 15) >> 2) + 4 * (kk >> 4) + (kk & 3);
 }
 
-// Raw registers of one dequant lane's share of a tile: key = lane/4, dims
-// [q*D/4, (q+1)*D/4) with q = lane%4.  Sized for bf16 rows (D/2 bytes), which
+// Raw registers of one dequant lane's share of a tile: key = lane (0..63),
+// dims [w*D/4, (w+1)*D/4) for wave w, so one LDS write instruction of a wave
+// covers 64 keys of one V^T row (no bank conflicts).  Sized for bf16 rows (D/2 bytes), which
 // also covers every code width.
 template <int NG>
 struct TileRaw {
@@ -108,7 +109,7 @@ __device__ __forceinline__ void load_raw(TileRaw<NG> &r, const ChunkArgs &p, int
                                          int nb, int nw, int T)
 {
     using C = Cfg<NG>;
-    const int tid = threadIdx.x, key = tid >> 2, qq = tid & 3;
+    const int tid = threadIdx.x, key = tid & 63, qq = tid >> 6;
     const int t = kt * TILE + key;
     if (kt < nb) {
         const size_t e = (size_t)a * p.t.max_blocks + kt;
@@ -190,7 +191,7 @@ template <int NG, int B>
 __device__ __forceinline__ void store_tile_w(const TileRaw<NG> &r, _Float16 *ks, _Float16 *vs)
 {
     using C = Cfg<NG>;
-    const int tid = threadIdx.x, key = tid >> 2, qq = tid & 3;
+    const int tid = threadIdx.x, key = tid & 63, qq = tid >> 6;
     const int vp = vpos(key);
 #pragma unroll
     for (int c = 0; c < C::CPT; c++) {
@@ -222,7 +223,7 @@ __device__ __forceinline__ void store_tile(const TileRaw<NG> &r, _Float16 *ks, _
 }
 
 template <int NG>
-__global__ __launch_bounds__(256) void chunk_split(ChunkArgs p)
+__global__ __launch_bounds__(256, 2) void chunk_split(ChunkArgs p)
 {
     using C = Cfg<NG>;
     __shared__ __attribute__((aligned(16))) _Float16 ks[TILE * C::KROW];
@@ -307,24 +308,25 @@ __global__ __launch_bounds__(256) void chunk_split(ChunkArgs p)
             }
         }
         // Online softmax per row (lane's row n of tile nt; keys 16mt + 4q + j).
+        // Scores are scaled inside the exp2 argument: c > 0, so the row max
+        // of c*s is c times the max of s.
         h8 pb[C::NTN][2];
 #pragma unroll
         for (int nt = 0; nt < C::NTN; nt++) {
-            float sc[16];
+            if (masked) {
 #pragma unroll
-            for (int mt = 0; mt < 4; mt++)
+                for (int mt = 0; mt < 4; mt++)
 #pragma unroll
-                for (int j = 0; j < 4; j++) {
-                    const int key = t0 + 16 * mt + 4 * q + j;
-                    const float v = st[mt][nt][j] * p.c;
-                    sc[4 * mt + j] = (!masked || key < lim[nt]) ? v : -INFINITY;
-                }
-            float mx = sc[0];
+                    for (int j = 0; j < 4; j++)
+                        if (t0 + 16 * mt + 4 * q + j >= lim[nt]) st[mt][nt][j] = -INFINITY;
+            }
+            float mx = fmaxf(fmaxf(st[0][nt][0], st[0][nt][1]), fmaxf(st[0][nt][2], st[0][nt][3]));
 #pragma unroll
-            for (int e = 1; e < 16; e++) mx = fmaxf(mx, sc[e]);
+            for (int mt = 1; mt < 4; mt++)
+                mx = fmaxf(mx, fmaxf(fmaxf(st[mt][nt][0], st[mt][nt][1]), fmaxf(st[mt][nt][2], st[mt][nt][3])));
             mx = fmaxf(mx, __shfl_xor(mx, 16));
             mx = fmaxf(mx, __shfl_xor(mx, 32));
-            const float m_new = fmaxf(m_run[nt], mx);
+            const float m_new = fmaxf(m_run[nt], mx * p.c);
             // rows with no valid key yet keep m = -inf; use 0 to avoid inf-inf
             const float m_use = (m_new == -INFINITY) ? 0.0f : m_new;
             const float alpha = __builtin_amdgcn_exp2f(m_run[nt] - m_use);
@@ -333,16 +335,20 @@ __global__ __launch_bounds__(256) void chunk_split(ChunkArgs p)
             const h2 ones = {(_Float16)1.0f, (_Float16)1.0f};
 #pragma unroll
             for (int ksx = 0; ksx < 2; ksx++) {
+                // K-step ksx: key tiles 2ksx (positions 0..3) and 2ksx+1 (4..7)
                 h8 o;
 #pragma unroll
-                for (int e = 0; e < 4; e++) {
-                    // K-step ksx covers key tiles 2ksx, 2ksx+1: positions 0..3 then 4..7
-                    const int m0 = 2 * ksx, m1 = 2 * ksx + 1;
-                    const h2 pa = __builtin_convertvector(
-                        f2{__builtin_amdgcn_exp2f(sc[4 * m0 + e] - m_use), __builtin_amdgcn_exp2f(sc[4 * m1 + e] - m_use)}, h2);
-                    o[e] = pa[0];
-                    o[4 + e] = pa[1];
-                    lsum = __builtin_amdgcn_fdot2(pa, ones, lsum, false);
+                for (int hm = 0; hm < 2; hm++) {
+                    const f4 v = st[2 * ksx + hm][nt];
+#pragma unroll
+                    for (int e = 0; e < 4; e += 2) {
+                        const h2 pa = __builtin_convertvector(
+                            f2{__builtin_amdgcn_exp2f(__builtin_fmaf(v[e], p.c, -m_use)),
+                               __builtin_amdgcn_exp2f(__builtin_fmaf(v[e + 1], p.c, -m_use))}, h2);
+                        o[4 * hm + e] = pa[0];
+                        o[4 * hm + e + 1] = pa[1];
+                        lsum = __builtin_amdgcn_fdot2(pa, ones, lsum, false);
+                    }
                 }
                 pb[nt][ksx] = o;
             }

@@ -278,7 +278,7 @@ int kvq_attend_chunk(const kvq_layout *L, const kvq_store *K, const kvq_store *V
     if (workspace_bytes < pl.ws_bytes) return KVQ_ENOSPC;
     if (!workspace || !aligned(workspace, 256)) return KVQ_EINVAL;
 
-    if (pl.ch_ok) {
+    if (pl.ch_ok && softmax_scale > 0.0f) {
         ChunkArgs c{};
         c.t = tables(L);
         c.k = store(K);
