@@ -16,13 +16,14 @@
 //      the chunk order the unpack produces), V transposed (V^T[d][key]) with
 //      keys permuted so a lane's 8 probabilities line up with 8 consecutive
 //      LDS halves; the raw codes of the next tile are already in registers;
-//   2. each wave computes S^T = K.Q^T with v_mfma_f32_16x16x32_f16 (A = 16
-//      keys x 32 dims from LDS, B = the wave's query rows from registers),
-//      so a lane owns one query row and 4 keys per 16-key tile;
+//   2. each wave computes S^T = K.Q^T with v_mfma_f32_32x32x16_f16 (A = 32
+//      keys x 16 dims from LDS, B = the wave's 32 query rows from registers),
+//      so lane l owns query row l%32 and 16 of every 32 keys;
 //   3. online softmax per row in fp32 (exp2), probabilities rounded to fp16
 //      (the running sum adds the rounded values);
-//   4. O^T += V^T.P^T (A = 16 dims x 32 keys from LDS, B = P^T from the
+//   4. O^T += V^T.P^T (A = 32 dims x 16 keys from LDS, B = P^T from the
 //      lane's own registers).
+// The 32x32x16 shape sustains about 1.5x the rate of 16x16x32 here.
 // The causal mask only applies to tiles that reach the new tokens.
 #include "kvq_internal.h"
 #include "unpack.h"
@@ -38,23 +39,23 @@ constexpr int WAVES = 4;
 template <int NG>
 struct Cfg {
     static constexpr int D = 64 * NG;
-    static constexpr int NR = (NG >= 4) ? 16 : 32;       // query rows per wave
-    static constexpr int NTN = NR / 16;                   // 16-row column tiles per wave
+    static constexpr int NR = 32;                         // query rows per wave (one 32-row tile)
     static constexpr int ROWS = WAVES * NR;               // rows per workgroup
-    static constexpr int KS = D / 32;                     // K-steps of Q.K^T
-    static constexpr int DT = D / 16;                     // 16-dim output tiles
+    static constexpr int KS = D / 16;                     // K-steps of S^T = K.Q^T
+    static constexpr int DT = D / 32;                     // 32-dim output tiles
     static constexpr int KROW = D + 8;                    // LDS K row stride (halves)
     static constexpr int VROW = TILE + 8;                 // LDS V^T row stride (halves)
     static constexpr int CPT = D / 32;                    // chunks of 8 dims per dequant lane
 };
 
-// Position of key k (0..63) of a tile in the V^T rows: within each 32-key
-// half, lane quarter q of the P^T operand holds keys 4q..4q+3 (first
-// 16-key tile) and 16+4q..16+4q+3 (second), as 8 consecutive positions.
+// Position of key k (0..63) of a tile in the V^T rows.  In the S^T tile of
+// v_mfma_f32_32x32x16_f16 lane half h holds, for the 16 keys of P.V K-step u,
+// keys 16u + 8a + 4h + b (a, b in 0..1, 0..3) in register order; placing
+// them at 16u + 8h + 4a + b makes them 8 consecutive halves of a V^T row.
 __device__ __forceinline__ int vpos(int k)
 {
-    const int h32 = k & ~31, kk = k & 31;
-    return h32 + 8 * ((kk & 15) >> 2) + 4 * (kk >> 4) + (kk & 3);
+    const int u = k >> 4, kk = k & 15;
+    return 16 * u + 8 * ((kk & 7) >> 2) + 4 * (kk >> 3) + (kk & 3);
 }
 
 // Raw registers of one dequant lane's share of a tile: key = lane (0..63),
@@ -222,18 +223,117 @@ __device__ __forceinline__ void store_tile(const TileRaw<NG> &r, _Float16 *ks, _
     }
 }
 
+typedef float f16x __attribute__((ext_vector_type(16)));
+
+// Per-wave state of the key loop: lane l owns query row l%32; lane half
+// hh = l/32 selects which 8 of every 16 K positions it supplies.
+template <int NG>
+struct Rows {
+    using C = Cfg<NG>;
+    h8 qop[C::KS];                         // B operand of S^T = K.Q^T: chunk 2ks+hh of the row
+    f16x acc[C::DT];                       // O^T tiles: dims 32dt + 8(r/4) + 4hh + r%4
+    float m_run, l_run;
+    int lim;                               // keys this row attends to
+    int lim_min;                           // smallest limit over the wave
+};
+
+// One 64-key tile: S^T from the current LDS buffers, the next tile's
+// dequantize into the other buffers (same basic block, so the scheduler can
+// interleave its vector work with the matrix instructions), then softmax and
+// O^T += V^T.P^T.
+template <int NG>
+__device__ __forceinline__ void tile_step(Rows<NG> &w, const _Float16 *kc, const _Float16 *vc,
+                                          _Float16 *kn, _Float16 *vn, TileRaw<NG> &raw, bool store_next,
+                                          bool load_next, const ChunkArgs &p, int a, int g, int kt,
+                                          int nb, int nw, int T)
+{
+    using C = Cfg<NG>;
+    const int lane = threadIdx.x & 63, m = lane & 31, hh = lane >> 5;
+    const int t0 = kt * TILE;
+    f16x st[2];
+#pragma unroll
+    for (int mt = 0; mt < 2; mt++) {
+#pragma unroll
+        for (int e = 0; e < 16; e++) st[mt][e] = 0.0f;
+#pragma unroll
+        for (int k = 0; k < C::KS; k++) {
+            const h8 av = *reinterpret_cast<const h8 *>(kc + (32 * mt + m) * C::KROW + 16 * k + 8 * hh);
+            st[mt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av, w.qop[k], st[mt], 0, 0, 0);
+        }
+    }
+    if (store_next) {
+        store_tile<NG>(raw, kn, vn);
+        if (load_next) load_raw<NG>(raw, p, a, g, kt + 2, nb, nw, T);
+    }
+
+    // Online softmax of the lane's row: keys 32mt + 8(r/4) + 4hh + r%4.
+    // Scores are scaled inside the exp2 argument: c > 0, so the row max of
+    // c*s is c times the max of s.
+    if (t0 + TILE > w.lim_min) {
+#pragma unroll
+        for (int mt = 0; mt < 2; mt++)
+#pragma unroll
+            for (int r = 0; r < 16; r++)
+                if (t0 + 32 * mt + 8 * (r >> 2) + 4 * hh + (r & 3) >= w.lim) st[mt][r] = -INFINITY;
+    }
+    float mx = st[0][0];
+#pragma unroll
+    for (int mt = 0; mt < 2; mt++)
+#pragma unroll
+        for (int r = (mt == 0 ? 1 : 0); r < 16; r++) mx = fmaxf(mx, st[mt][r]);
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const float m_new = fmaxf(w.m_run, mx * p.c);
+    // rows with no valid key yet keep m = -inf; use 0 to avoid inf-inf
+    const float m_use = (m_new == -INFINITY) ? 0.0f : m_new;
+    const float alpha = __builtin_amdgcn_exp2f(w.m_run - m_use);
+    w.m_run = m_new;
+    float lsum = 0.0f;
+    const h2 ones = {(_Float16)1.0f, (_Float16)1.0f};
+    h8 pb[4];                                  // B operand of K-step u: regs 8(u%2)..+7 of tile u/2
+#pragma unroll
+    for (int u = 0; u < 4; u++) {
+        h8 o;
+#pragma unroll
+        for (int e = 0; e < 8; e += 2) {
+            const int r = 8 * (u & 1) + e;
+            const h2 pa = __builtin_convertvector(
+                f2{__builtin_amdgcn_exp2f(__builtin_fmaf(st[u >> 1][r], p.c, -m_use)),
+                   __builtin_amdgcn_exp2f(__builtin_fmaf(st[u >> 1][r + 1], p.c, -m_use))}, h2);
+            o[e] = pa[0];
+            o[e + 1] = pa[1];
+            lsum = __builtin_amdgcn_fdot2(pa, ones, lsum, false);
+        }
+        pb[u] = o;
+    }
+    w.l_run = w.l_run * alpha + lsum;
+    if (__any(alpha != 1.0f)) {
+#pragma unroll
+        for (int dt = 0; dt < C::DT; dt++) w.acc[dt] *= alpha;
+    }
+    // O^T += V^T . P^T over the 64 keys (4 K-steps of 16).
+#pragma unroll
+    for (int u = 0; u < 4; u++) {
+#pragma unroll
+        for (int dt = 0; dt < C::DT; dt++) {
+            const h8 av = *reinterpret_cast<const h8 *>(vc + (32 * dt + m) * C::VROW + 16 * u + 8 * hh);
+            w.acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av, pb[u], w.acc[dt], 0, 0, 0);
+        }
+    }
+    __syncthreads();                     // next buffers written, current ones no longer read
+}
+
 template <int NG>
 __global__ __launch_bounds__(256, 2) void chunk_split(ChunkArgs p)
 {
     using C = Cfg<NG>;
-    __shared__ __attribute__((aligned(16))) _Float16 ks[TILE * C::KROW];
-    __shared__ __attribute__((aligned(16))) _Float16 vs[C::D * C::VROW];
-    __shared__ int lim_max_s;
+    __shared__ __attribute__((aligned(16))) _Float16 ks0[TILE * C::KROW];
+    __shared__ __attribute__((aligned(16))) _Float16 vs0[C::D * C::VROW];
+    __shared__ __attribute__((aligned(16))) _Float16 ks1[TILE * C::KROW];
+    __shared__ __attribute__((aligned(16))) _Float16 vs1[C::D * C::VROW];
 
     const int s = blockIdx.x, a = blockIdx.z;
     const int g = blockIdx.y / p.n_row_tiles, rt = blockIdx.y % p.n_row_tiles;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-    const int n = lane & 15, q = lane >> 4;
     const int nb = seq_blocks(p.t, a), nw = seq_window(p.t, a);
     const int T = 64 * nb + nw;                          // restored tokens
 
@@ -246,149 +346,58 @@ __global__ __launch_bounds__(256, 2) void chunk_split(ChunkArgs p)
     const int kt1 = min(kt0 + p.split_tiles, n_tiles);
     if (kt0 >= kt1) return;
 
-    // The wave's query rows and their key limits.
-    int lim[C::NTN];
-    bool rv[C::NTN];
-    h8 qop[C::NTN][C::KS];
-#pragma unroll
-    for (int nt = 0; nt < C::NTN; nt++) {
-        const int R = row0 + wave * C::NR + nt * 16 + n;
-        const int i = R / p.G, h = g * p.G + R % p.G;
-        rv[nt] = i < p.n_new;
-        lim[nt] = rv[nt] ? T + i + 1 : 0;
-        const uint16_t *qr = p.q_new + (((size_t)a * p.n_new + (rv[nt] ? i : 0)) * p.Hq + h) * C::D;
+    // The wave's query row (lane l: row l%32) and its key limit.
+    const int m = lane & 31, hh = lane >> 5;
+    Rows<NG> w;
+    const int R = row0 + wave * C::NR + m;
+    const int ti = R / p.G, head = g * p.G + R % p.G;
+    const bool rv = ti < p.n_new;
+    w.lim = rv ? T + ti + 1 : 0;
+    {
+        const uint16_t *qr = p.q_new + (((size_t)a * p.n_new + (rv ? ti : 0)) * p.Hq + head) * C::D;
 #pragma unroll
         for (int k = 0; k < C::KS; k++) {
-            const uint4 v = *reinterpret_cast<const uint4 *>(qr + 8 * (4 * k + q));
+            const uint4 v = *reinterpret_cast<const uint4 *>(qr + 8 * (2 * k + hh));
             const Pairs pr = bf16_pairs(v);
             h8 o;
             o[0] = pr.p[0][0]; o[1] = pr.p[0][1]; o[2] = pr.p[1][0]; o[3] = pr.p[1][1];
             o[4] = pr.p[2][0]; o[5] = pr.p[2][1]; o[6] = pr.p[3][0]; o[7] = pr.p[3][1];
-            if (!rv[nt]) o = h8{0, 0, 0, 0, 0, 0, 0, 0};
-            qop[nt][k] = o;
+            if (!rv) o = h8{0, 0, 0, 0, 0, 0, 0, 0};
+            w.qop[k] = o;
         }
     }
-    int lim_min = 1 << 30;
-#pragma unroll
-    for (int nt = 0; nt < C::NTN; nt++) if (rv[nt]) lim_min = min(lim_min, lim[nt]);
-    // smallest limit over the wave (for the per-tile mask test)
+    int lim_min = rv ? w.lim : (1 << 30);
     for (int o = 1; o < 64; o <<= 1) lim_min = min(lim_min, __shfl_xor(lim_min, o));
-
-    f4 acc[C::NTN][C::DT];
+    w.lim_min = lim_min;
 #pragma unroll
-    for (int nt = 0; nt < C::NTN; nt++)
+    for (int dt = 0; dt < C::DT; dt++)
 #pragma unroll
-        for (int dt = 0; dt < C::DT; dt++) acc[nt][dt] = f4{0.f, 0.f, 0.f, 0.f};
-    float m_run[C::NTN], l_run[C::NTN];
-#pragma unroll
-    for (int nt = 0; nt < C::NTN; nt++) { m_run[nt] = -INFINITY; l_run[nt] = 0.0f; }
+        for (int e = 0; e < 16; e++) w.acc[dt][e] = 0.0f;
+    w.m_run = -INFINITY;
+    w.l_run = 0.0f;
 
     TileRaw<NG> raw;
     load_raw<NG>(raw, p, a, g, kt0, nb, nw, T);
-    for (int kt = kt0; kt < kt1; kt++) {
-        __syncthreads();                                 // previous tile's LDS reads are done
-        store_tile<NG>(raw, ks, vs);
-        if (kt + 1 < kt1) load_raw<NG>(raw, p, a, g, kt + 1, nb, nw, T);
-        __syncthreads();
-
-        const int t0 = kt * TILE;
-        const bool masked = t0 + TILE > lim_min;
-        // S^T tiles: [16 keys][16 rows] for 4 key tiles x NTN row tiles.
-        f4 st[4][C::NTN];
-#pragma unroll
-        for (int mt = 0; mt < 4; mt++) {
-#pragma unroll
-            for (int nt = 0; nt < C::NTN; nt++) st[mt][nt] = f4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int k = 0; k < C::KS; k++) {
-                const h8 av = *reinterpret_cast<const h8 *>(ks + (16 * mt + n) * C::KROW + 32 * k + 8 * q);
-#pragma unroll
-                for (int nt = 0; nt < C::NTN; nt++)
-                    st[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, qop[nt][k], st[mt][nt], 0, 0, 0);
-            }
-        }
-        // Online softmax per row (lane's row n of tile nt; keys 16mt + 4q + j).
-        // Scores are scaled inside the exp2 argument: c > 0, so the row max
-        // of c*s is c times the max of s.
-        h8 pb[C::NTN][2];
-#pragma unroll
-        for (int nt = 0; nt < C::NTN; nt++) {
-            if (masked) {
-#pragma unroll
-                for (int mt = 0; mt < 4; mt++)
-#pragma unroll
-                    for (int j = 0; j < 4; j++)
-                        if (t0 + 16 * mt + 4 * q + j >= lim[nt]) st[mt][nt][j] = -INFINITY;
-            }
-            float mx = fmaxf(fmaxf(st[0][nt][0], st[0][nt][1]), fmaxf(st[0][nt][2], st[0][nt][3]));
-#pragma unroll
-            for (int mt = 1; mt < 4; mt++)
-                mx = fmaxf(mx, fmaxf(fmaxf(st[mt][nt][0], st[mt][nt][1]), fmaxf(st[mt][nt][2], st[mt][nt][3])));
-            mx = fmaxf(mx, __shfl_xor(mx, 16));
-            mx = fmaxf(mx, __shfl_xor(mx, 32));
-            const float m_new = fmaxf(m_run[nt], mx * p.c);
-            // rows with no valid key yet keep m = -inf; use 0 to avoid inf-inf
-            const float m_use = (m_new == -INFINITY) ? 0.0f : m_new;
-            const float alpha = __builtin_amdgcn_exp2f(m_run[nt] - m_use);
-            m_run[nt] = m_new;
-            float lsum = 0.0f;
-            const h2 ones = {(_Float16)1.0f, (_Float16)1.0f};
-#pragma unroll
-            for (int ksx = 0; ksx < 2; ksx++) {
-                // K-step ksx: key tiles 2ksx (positions 0..3) and 2ksx+1 (4..7)
-                h8 o;
-#pragma unroll
-                for (int hm = 0; hm < 2; hm++) {
-                    const f4 v = st[2 * ksx + hm][nt];
-#pragma unroll
-                    for (int e = 0; e < 4; e += 2) {
-                        const h2 pa = __builtin_convertvector(
-                            f2{__builtin_amdgcn_exp2f(__builtin_fmaf(v[e], p.c, -m_use)),
-                               __builtin_amdgcn_exp2f(__builtin_fmaf(v[e + 1], p.c, -m_use))}, h2);
-                        o[4 * hm + e] = pa[0];
-                        o[4 * hm + e + 1] = pa[1];
-                        lsum = __builtin_amdgcn_fdot2(pa, ones, lsum, false);
-                    }
-                }
-                pb[nt][ksx] = o;
-            }
-            l_run[nt] = l_run[nt] * alpha + lsum;
-            if (__any(alpha != 1.0f)) {
-#pragma unroll
-                for (int dt = 0; dt < C::DT; dt++) acc[nt][dt] *= alpha;
-            }
-        }
-        // O^T += V^T . P^T over the 64 keys (2 K-steps of 32).
-#pragma unroll
-        for (int ksx = 0; ksx < 2; ksx++) {
-#pragma unroll
-            for (int dt = 0; dt < C::DT; dt++) {
-                const h8 av = *reinterpret_cast<const h8 *>(vs + (16 * dt + n) * C::VROW + 32 * ksx + 8 * q);
-#pragma unroll
-                for (int nt = 0; nt < C::NTN; nt++)
-                    acc[nt][dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, pb[nt][ksx], acc[nt][dt], 0, 0, 0);
-            }
-        }
+    store_tile<NG>(raw, ks0, vs0);
+    if (kt0 + 1 < kt1) load_raw<NG>(raw, p, a, g, kt0 + 1, nb, nw, T);
+    __syncthreads();
+    for (int kt = kt0; kt < kt1; kt += 2) {
+        tile_step<NG>(w, ks0, vs0, ks1, vs1, raw, kt + 1 < kt1, kt + 2 < kt1, p, a, g, kt, nb, nw, T);
+        if (kt + 1 < kt1)
+            tile_step<NG>(w, ks1, vs1, ks0, vs0, raw, kt + 2 < kt1, kt + 3 < kt1, p, a, g, kt + 1, nb, nw, T);
     }
 
-    // Partials of rows that have a key in this split.
+    // Partial of the lane's row if it has a key in this split.
     const size_t stride = (size_t)(C::D + 2);
+    float l = w.l_run + __shfl_xor(w.l_run, 32);
+    if (rv && kt0 * TILE < w.lim) {
+        const size_t orow = ((size_t)a * p.n_new + ti) * p.Hq + head;
+        float *pr = p.part + (orow * p.n_splits + s) * stride;
+        if (hh == 0) { pr[0] = w.m_run; pr[1] = l; }
 #pragma unroll
-    for (int nt = 0; nt < C::NTN; nt++) {
-        float l = l_run[nt];
-        l += __shfl_xor(l, 16);
-        l += __shfl_xor(l, 32);
-        const int R = row0 + wave * C::NR + nt * 16 + n;
-        const int i = R / p.G, h = g * p.G + R % p.G;
-        if (rv[nt] && kt0 * TILE < lim[nt]) {
-            const size_t orow = ((size_t)a * p.n_new + i) * p.Hq + h;
-            float *pr = p.part + (orow * p.n_splits + s) * stride;
-            if (q == 0) { pr[0] = m_run[nt]; pr[1] = l; }
+        for (int dt = 0; dt < C::DT; dt++)
 #pragma unroll
-            for (int dt = 0; dt < C::DT; dt++)
-#pragma unroll
-                for (int j = 0; j < 4; j++) pr[2 + 16 * dt + 4 * q + j] = acc[nt][dt][j];
-        }
+            for (int r = 0; r < 16; r++) pr[2 + 32 * dt + 8 * (r >> 2) + 4 * hh + (r & 3)] = w.acc[dt][r];
     }
 }
 
@@ -428,7 +437,7 @@ __global__ __launch_bounds__(256) void chunk_merge(ChunkArgs p)
 
 bool chunk_supported(int D) { return D == 64 || D == 128 || D == 256; }
 
-int chunk_rows_per_wg(int D) { return D >= 256 ? WAVES * 16 : WAVES * 32; }
+int chunk_rows_per_wg(int D) { (void)D; return WAVES * 32; }
 
 hipError_t launch_chunk(const ChunkArgs &p, hipStream_t s)
 {

@@ -179,3 +179,23 @@ def test_chunk_llama_32k_restore_512_sampled_rows():
     for r0, r1 in [(0, 2), (255, 256), (510, 512)]:
         want = _ref_chunk(b, 0, qn, kn, vn, w.scale, rows=(r0, r1))
         close(got[r0:r1], want[r0:r1], what=f"chunk rows {r0}:{r1}")
+
+
+@pytest.mark.parametrize("D,G", [(64, 4), (256, 2), (128, 8)])
+def test_chunk_mixed_widths_window(D, G):
+    """Chunk over a cache with 2/3/4/8-bit blocks and a bf16 window, causal
+    new tokens spanning several 64-key tiles and a ragged tail."""
+    rng = np.random.default_rng(D + G)
+    H = 2
+    lengths = [64 * 7 + 45, 64 * 3 + 130]
+    window = [45, 130]
+    nb = [(L - w) // 64 for L, w in zip(lengths, window)]
+    bits = [rng.choice(np.array([2, 3, 4, 8], np.uint8), size=n) for n in nb]
+    b = build(H, D, lengths, bits=bits, window=window, seed=D)
+    A, n_new = 2, 150
+    qn = syn.random_normal_bf16((A, n_new, G * H, D), 51)
+    kn = syn.random_normal_bf16((A, n_new, H, D), 52)
+    vn = syn.random_normal_bf16((A, n_new, H, D), 53)
+    got = _chunk(b, qn, kn, vn, D ** -0.5)
+    for a in range(A):
+        close(got[a], _ref_chunk(b, a, qn[a], kn[a], vn[a], D ** -0.5), what=f"chunk D={D} a={a}")
