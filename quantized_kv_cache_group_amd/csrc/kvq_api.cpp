@@ -105,7 +105,7 @@ int plan_attention(const kvq_layout *L, int n_q_heads, int rope_dim, int n_new, 
         const int64_t tiles = (max_keys + 63) / 64;
         const int64_t units = row_tiles * L->n_heads * L->n_seqs;
         if (row_tiles * L->n_heads <= kMaxGrid) {
-            int64_t ns = (512 + units - 1) / units;
+            int64_t ns = (256 + units - 1) / units;   // about one workgroup per CU
             if (ns > tiles) ns = tiles;
             if (ns < 1) ns = 1;
             const int64_t st = (tiles + ns - 1) / ns;
