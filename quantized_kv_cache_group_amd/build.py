@@ -30,7 +30,8 @@ COMMON = [
 PER_FILE = {
     "quantize.hip": ["-ffp-contract=off"],
 }
-SOURCES = ["kvq_api.cpp", "quantize.hip", "attend_generic.hip", "decode_gqa.hip", "decode_g4.hip", "chunk.hip"]
+SOURCES = ["kvq_api.cpp", "quantize.hip", "attend_generic.hip", "decode_gqa.hip", "decode_g4.hip", "chunk.hip",
+           "mla.hip"]
 
 
 def _compile(src: str) -> str:

@@ -70,6 +70,7 @@ size_t round256(size_t b) { return (b + 255) / 256 * 256; }
 struct Plan {
     int tok_per_tile, split_keys, n_splits, n_row_tiles;
     int sb, dec_splits;         // tuned decode
+    int mla_sb, mla_splits;     // latent decode
     int ch_row_tiles, ch_splits, ch_split_tiles;   // tuned chunk
     bool ch_ok;
     size_t ws_bytes;
@@ -95,8 +96,13 @@ int plan_attention(const kvq_layout *L, int n_q_heads, int rope_dim, int n_new, 
     pl->ws_bytes = round256(rows * (size_t)pl->n_splits * (size_t)(L->head_dim + 2) * sizeof(float));
     if (n_new == 0) {
         decode_gqa_plan(L->n_seqs, L->n_heads, L->max_blocks, L->window_cap, &pl->sb, &pl->dec_splits);
-        const size_t t = round256(rows * (size_t)pl->dec_splits * (size_t)(L->head_dim + 2) * sizeof(float));
+        size_t t = round256(rows * (size_t)pl->dec_splits * (size_t)(L->head_dim + 2) * sizeof(float));
         if (t > pl->ws_bytes) pl->ws_bytes = t;
+        if (mla_supported(L->head_dim, L->n_heads, G, rope_dim)) {
+            mla_plan(L->n_seqs, L->max_blocks, L->window_cap, &pl->mla_sb, &pl->mla_splits);
+            t = round256(rows * (size_t)pl->mla_splits * (size_t)(L->head_dim + 2) * sizeof(float));
+            if (t > pl->ws_bytes) pl->ws_bytes = t;
+        }
     }
     pl->ch_ok = false;
     if (n_new > 0 && chunk_supported(L->head_dim)) {
@@ -220,6 +226,23 @@ int kvq_attend_decode(const kvq_layout *L, const kvq_store *K, const kvq_store *
             return hip_status(launch_decode_merge(d, hs));
         }
         return hip_status(launch_decode_gqa(d, hs));
+    }
+
+    if (!V && mla_supported(L->head_dim, L->n_heads, n_q_heads / L->n_heads, rope_dim)) {
+        DecodeArgs d{};
+        d.t = tables(L);
+        d.k = store(K);
+        d.v = store(K);
+        d.q = q;
+        d.out = out;
+        d.part = static_cast<float *>(workspace);
+        d.Hq = n_q_heads;
+        d.G = n_q_heads;
+        d.SB = pl.mla_sb;
+        d.n_splits = pl.mla_splits;
+        d.c = softmax_scale * 1.4426950408889634f;
+        return hip_status(launch_mla(d, rope, rope_dim, (int64_t)L->max_blocks * 64 + L->window_cap,
+                                     static_cast<hipStream_t>(stream)));
     }
 
     AttnArgs a{};

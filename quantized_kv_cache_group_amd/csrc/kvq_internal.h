@@ -106,6 +106,12 @@ int chunk_rows_per_wg(int D);
 void decode_gqa_plan(int A, int H, int max_blocks, int window_cap, int *SB, int *n_splits);
 bool decode_gqa_supported(int D);
 
+// Latent (MLA) decode: one 512-dim latent KV head, optional 64-dim rope.
+bool mla_supported(int D, int H, int G, int rope_dim);
+void mla_plan(int A, int max_blocks, int window_cap, int *SB, int *n_splits);
+hipError_t launch_mla(const DecodeArgs &a, const uint16_t *rope, int rope_dim, int64_t rope_tokens,
+                      hipStream_t s);                                  // split + merge
+
 // Generic path's split size and workspace.
 void generic_plan(int max_keys, int n_new, int G, int *tok_per_tile, int *split_keys, int *n_splits);
 

@@ -1,0 +1,355 @@
+// Latent (MLA) decode over a quantized latent cache (gfx950, matrix cores).
+//
+// What it computes (DeepSeek-V2-Lite absorbed attention as the pages use
+// it for their MLA model; softmax attention of one query token per head):
+// one latent KV head of 512 dims, quantized in 64-token blocks, with an
+// optional bf16 rope part of 64 dims per token kept beside it.  Query head h
+// (of up to 16) scores key t as q_h . [latent_t ; rope_t] (576 dims) and
+// averages the dequantized latents (512 dims) as values.
+//
+// Work decomposition: a workgroup of four waves takes one sequence and SB
+// consecutive blocks (or the sequence's bf16 window).  Per 64-key tile all
+// 256 lanes dequantize into LDS once -- K rows [key][576] for the scores and
+// the transposed latent V^T [512][key] for the values -- while the codes of
+// the next tile load into registers.  Wave w owns keys 16w..16w+15 of every
+// tile and keeps its own online softmax:
+//   S^T[key][head] = K.Q^T   v_mfma_f32_16x16x32_f16, 18 K-steps over 576 dims
+//   O^T[dim][head] += V^T.P^T v_mfma_f32_16x16x16_f16, 32 tiles of 16 dims
+// The S^T result layout (lane: head l%16, keys 4(l/16)..+3) is exactly the
+// B operand of the P.V product, so probabilities never leave registers.  At
+// the end the four waves' states combine through LDS into one partial
+// (m, l, acc[512]) per head; the decode merge kernel combines the splits.
+#include "kvq_internal.h"
+#include "unpack.h"
+
+namespace kvq {
+namespace {
+
+using namespace dev;
+
+constexpr int DL = 512;                 // latent dims
+constexpr int TILE = 64;                // keys per tile (one block)
+constexpr int VR = TILE + 8;            // LDS V^T row stride (halves)
+constexpr int OT = DL / 16;             // 16-dim output tiles
+constexpr float LAZY = 8.0f;            // running-max slack, log2 units
+
+typedef _Float16 h4 __attribute__((ext_vector_type(4)));
+
+template <int R>
+struct MCfg {
+    static constexpr int DK = DL + R;   // score dims
+    static constexpr int KR = DK + 8;   // LDS K row stride (halves)
+    static constexpr int KS = DK / 32;  // K-steps of S^T
+    static constexpr int LDS_HALVES = TILE * KR + DL * VR;
+};
+
+// One lane's share of a quantized tile: key = tid & 63, latent dims
+// [128q, 128q + 128) for quarter q = tid >> 6 (16 chunks of 8 codes), the two
+// groups' metadata, and rope dims [16q, 16q + 16).
+struct MlaRaw {
+    uint32_t c[32];                     // 16 chunks x B bytes, unused dwords zero
+    uint32_t m0, m1;                    // (scale, bias) of groups 2q, 2q+1
+    uint32_t r[8];                      // 16 bf16 rope values
+    int bits;
+};
+
+template <int B>
+__device__ __forceinline__ void load_share(uint32_t (&c)[32], const uint8_t *p)
+{
+#pragma unroll
+    for (int i = 0; i < B; i++) {
+        const uint4 x = reinterpret_cast<const uint4 *>(p)[i];
+        c[4 * i] = x.x; c[4 * i + 1] = x.y; c[4 * i + 2] = x.z; c[4 * i + 3] = x.w;
+    }
+}
+
+// Codes, metadata and rope of block kt (all fields assigned once, so the
+// record stays in registers across the width branches).
+template <int R>
+__device__ __forceinline__ void load_block(MlaRaw &raw, const DecodeArgs &p, const uint16_t *rope, int64_t rope_tokens,
+                                           int a, int kt)
+{
+    const int tid = threadIdx.x, key = tid & 63, q = tid >> 6;
+    const size_t e = (size_t)a * p.t.max_blocks + kt;
+    const int b = p.t.bits[e];
+    const uint8_t *blk = p.k.pool + p.k.offset[e];
+    const uint32_t row_bytes = (uint32_t)(DL / 8) * b;
+    uint32_t c[32];
+#pragma unroll
+    for (int i = 0; i < 32; i++) c[i] = 0;
+    const uint8_t *share = blk + key * row_bytes + q * (row_bytes / 4);
+    switch (b) {
+    case 2: load_share<2>(c, share); break;
+    case 3: load_share<3>(c, share); break;
+    case 4: load_share<4>(c, share); break;
+    default: load_share<8>(c, share); break;
+    }
+    const uint2 mm = *reinterpret_cast<const uint2 *>(blk + 64 * row_bytes + 4 * (key * (DL / 64) + 2 * q));
+    uint32_t r[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    if (R) {
+        const uint4 *rp = reinterpret_cast<const uint4 *>(rope + ((size_t)a * rope_tokens + (size_t)kt * TILE + key) * R + 16 * q);
+        const uint4 x = rp[0], y = rp[1];
+        r[0] = x.x; r[1] = x.y; r[2] = x.z; r[3] = x.w;
+        r[4] = y.x; r[5] = y.y; r[6] = y.z; r[7] = y.w;
+    }
+#pragma unroll
+    for (int i = 0; i < 32; i++) raw.c[i] = c[i];
+#pragma unroll
+    for (int i = 0; i < 8; i++) raw.r[i] = r[i];
+    raw.m0 = mm.x;
+    raw.m1 = mm.y;
+    raw.bits = b;
+}
+
+// Chunk ch (8 latent dims) of the share, dequantized.
+template <int B>
+__device__ __forceinline__ Pairs share_chunk(const MlaRaw &raw, int ch)
+{
+    Pairs pr;
+    if constexpr (B == 4) {
+        pr = Unpack<4>::run(raw.c[ch]);
+    } else if constexpr (B == 2) {
+        const uint32_t d = raw.c[ch >> 1];
+        pr = Unpack<2>::run((ch & 1) ? (d >> 16) : (d & 0xffffu));
+    } else if constexpr (B == 8) {
+        pr = Unpack<8>::run2(raw.c[2 * ch], raw.c[2 * ch + 1]);
+    } else {
+        const int o = 3 * ch, i = o >> 2;                 // compile-time after unrolling
+        pr = Unpack<3>::run3(raw.c[i], raw.c[i + 1 < 12 ? i + 1 : i], o & 3);
+    }
+    dequant(pr, ch < 8 ? raw.m0 : raw.m1);
+    return pr;
+}
+
+__device__ __forceinline__ h8 row_order(const Pairs &p)
+{
+    h8 o;
+    o[0] = p.p[0][0]; o[1] = p.p[0][1]; o[2] = p.p[1][0]; o[3] = p.p[1][1];
+    o[4] = p.p[2][0]; o[5] = p.p[2][1]; o[6] = p.p[3][0]; o[7] = p.p[3][1];
+    return o;
+}
+
+// Write chunk ch of the lane's share: K row (chunk order, as the query
+// operand uses) and V^T column (true dim order).
+__device__ __forceinline__ void put_chunk(_Float16 *kh, _Float16 *vt, int KR, int key, int q, int ch, const Pairs &pr)
+{
+    const int d0 = 128 * q + 8 * ch;
+    *reinterpret_cast<h8 *>(kh + key * KR + d0) = row_order(pr);
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+        vt[(d0 + i) * VR + key] = pr.p[i][0];
+        vt[(d0 + i + 4) * VR + key] = pr.p[i][1];
+    }
+}
+
+template <int R, int B>
+__device__ __forceinline__ void store_block(const MlaRaw &raw, _Float16 *kh, _Float16 *vt)
+{
+    constexpr int KR = MCfg<R>::KR;
+    const int tid = threadIdx.x, key = tid & 63, q = tid >> 6;
+#pragma unroll
+    for (int ch = 0; ch < 16; ch++) put_chunk(kh, vt, KR, key, q, ch, share_chunk<B>(raw, ch));
+    if (R) {
+        const uint4 x = {raw.r[0], raw.r[1], raw.r[2], raw.r[3]}, y = {raw.r[4], raw.r[5], raw.r[6], raw.r[7]};
+        *reinterpret_cast<h8 *>(kh + key * KR + DL + 16 * q) = row_order(bf16_pairs(x));
+        *reinterpret_cast<h8 *>(kh + key * KR + DL + 16 * q + 8) = row_order(bf16_pairs(y));
+    }
+}
+
+template <int R>
+__device__ __forceinline__ void store_raw(const MlaRaw &raw, _Float16 *kh, _Float16 *vt)
+{
+    switch (raw.bits) {
+    case 2: store_block<R, 2>(raw, kh, vt); break;
+    case 3: store_block<R, 3>(raw, kh, vt); break;
+    case 4: store_block<R, 4>(raw, kh, vt); break;
+    default: store_block<R, 8>(raw, kh, vt); break;
+    }
+}
+
+// bf16 window rows w0.. of sequence a straight into LDS (rows past the
+// window repeat its last row; they are masked).
+template <int R>
+__device__ __forceinline__ void store_window(const DecodeArgs &p, const uint16_t *rope, int64_t rope_tokens, int a,
+                                             int nb, int nw, int w0, _Float16 *kh, _Float16 *vt)
+{
+    constexpr int KR = MCfg<R>::KR;
+    const int tid = threadIdx.x, key = tid & 63, q = tid >> 6;
+    const int w = min(w0 + key, nw - 1);
+    const uint16_t *src = p.k.window + ((size_t)a * p.t.window_cap + w) * DL + 128 * q;
+#pragma unroll
+    for (int ch = 0; ch < 16; ch++)
+        put_chunk(kh, vt, KR, key, q, ch, bf16_pairs(reinterpret_cast<const uint4 *>(src)[ch]));
+    if (R) {
+        const uint4 *rp = reinterpret_cast<const uint4 *>(
+            rope + ((size_t)a * rope_tokens + (size_t)nb * TILE + w) * R + 16 * q);
+        *reinterpret_cast<h8 *>(kh + key * KR + DL + 16 * q) = row_order(bf16_pairs(rp[0]));
+        *reinterpret_cast<h8 *>(kh + key * KR + DL + 16 * q + 8) = row_order(bf16_pairs(rp[1]));
+    }
+}
+
+// Per-wave state: lane l is head l%16; of each tile it scores keys
+// 16w + 4(l/16) + r and holds O^T rows 16t + 4(l/16) + r.
+template <int R>
+struct MlaState {
+    h8 qop[MCfg<R>::KS];
+    f4 acc[OT];
+    float m_run, l_run;
+};
+
+template <int R>
+__device__ __forceinline__ void tile_compute(MlaState<R> &w, const _Float16 *kh, const _Float16 *vt, int valid, float c)
+{
+    constexpr int KR = MCfg<R>::KR, KS = MCfg<R>::KS;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, m = lane & 15, kq = lane >> 4;
+    const int k0 = 16 * wave;
+    f4 st = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < KS; s++) {
+        const h8 av = *reinterpret_cast<const h8 *>(kh + (k0 + m) * KR + 32 * s + 8 * kq);
+        st = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, w.qop[s], st, 0, 0, 0);
+    }
+    if (valid < TILE) {
+#pragma unroll
+        for (int r = 0; r < 4; r++)
+            if (k0 + 4 * kq + r >= valid) st[r] = -INFINITY;
+    }
+    float mx = fmaxf(fmaxf(st[0], st[1]), fmaxf(st[2], st[3]));
+    mx = fmaxf(mx, __shfl_xor(mx, 16));
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const float m_old = w.m_run;
+    const float tmax = mx * c;
+    const float m_new = (tmax > m_old + LAZY) ? tmax : m_old;
+    const float m_use = (m_new == -INFINITY) ? 0.0f : m_new;
+    const float alpha = (m_new == -INFINITY) ? 1.0f : __builtin_amdgcn_exp2f(m_old - m_new);
+    w.m_run = m_new;
+    const h2 p01 = __builtin_convertvector(f2{__builtin_amdgcn_exp2f(__builtin_fmaf(st[0], c, -m_use)),
+                                               __builtin_amdgcn_exp2f(__builtin_fmaf(st[1], c, -m_use))}, h2);
+    const h2 p23 = __builtin_convertvector(f2{__builtin_amdgcn_exp2f(__builtin_fmaf(st[2], c, -m_use)),
+                                               __builtin_amdgcn_exp2f(__builtin_fmaf(st[3], c, -m_use))}, h2);
+    const h2 ones = {(_Float16)1.0f, (_Float16)1.0f};
+    w.l_run = w.l_run * alpha + __builtin_amdgcn_fdot2(p23, ones, __builtin_amdgcn_fdot2(p01, ones, 0.0f, false), false);
+    if (__any(alpha != 1.0f)) {
+#pragma unroll
+        for (int t = 0; t < OT; t++) w.acc[t] *= alpha;
+    }
+    const h4 pb = {p01[0], p01[1], p23[0], p23[1]};
+#pragma unroll
+    for (int t = 0; t < OT; t++) {
+        const h4 av = *reinterpret_cast<const h4 *>(vt + (16 * t + m) * VR + k0 + 4 * kq);
+        w.acc[t] = __builtin_amdgcn_mfma_f32_16x16x16f16(av, pb, w.acc[t], 0, 0, 0);
+    }
+}
+
+template <int R>
+__global__ __launch_bounds__(256, 1) void mla_split(DecodeArgs p, const uint16_t *rope, int64_t rope_tokens)
+{
+    using C = MCfg<R>;
+    __shared__ __attribute__((aligned(16))) _Float16 lds[C::LDS_HALVES];
+    _Float16 *kh = lds, *vt = lds + TILE * C::KR;
+
+    const int s = blockIdx.x, a = blockIdx.z;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, m = lane & 15, kq = lane >> 4;
+    const int nb = seq_blocks(p.t, a), nw = seq_window(p.t, a);
+    const int nsb = (nb + p.SB - 1) / p.SB;
+    const bool win = (s == nsb) && nw > 0;
+    if (s > nsb || (s == nsb && !win)) return;
+
+    MlaState<R> w;
+    const bool hv = m < p.Hq;
+    const uint16_t *qrow = p.q + ((size_t)a * p.Hq + (hv ? m : 0)) * C::DK;
+#pragma unroll
+    for (int k = 0; k < C::KS; k++) {
+        h8 o = row_order(bf16_pairs(*reinterpret_cast<const uint4 *>(qrow + 32 * k + 8 * kq)));
+        if (!hv) o = h8{0, 0, 0, 0, 0, 0, 0, 0};
+        w.qop[k] = o;
+    }
+#pragma unroll
+    for (int t = 0; t < OT; t++) w.acc[t] = f4{0.f, 0.f, 0.f, 0.f};
+    w.m_run = -INFINITY;
+    w.l_run = 0.0f;
+
+    if (!win) {
+        const int j0 = s * p.SB, j1 = min(j0 + p.SB, nb);
+        MlaRaw raw;
+        load_block<R>(raw, p, rope, rope_tokens, a, j0);
+        for (int j = j0; j < j1; j++) {
+            __syncthreads();                             // previous tile no longer read
+            store_raw<R>(raw, kh, vt);
+            if (j + 1 < j1) load_block<R>(raw, p, rope, rope_tokens, a, j + 1);
+            __syncthreads();
+            tile_compute<R>(w, kh, vt, TILE, p.c);
+        }
+    } else {
+        for (int w0 = 0; w0 < nw; w0 += TILE) {
+            __syncthreads();
+            store_window<R>(p, rope, rope_tokens, a, nb, nw, w0, kh, vt);
+            __syncthreads();
+            tile_compute<R>(w, kh, vt, nw - w0, p.c);
+        }
+    }
+
+    // Combine the four waves: (m, l) per head and O^T [512][16] per wave.
+    float l = w.l_run + __shfl_xor(w.l_run, 16);
+    l += __shfl_xor(l, 32);
+    __syncthreads();
+    float *ml = reinterpret_cast<float *>(lds);           // [4][2][16]
+    float *ob = ml + 128;                                  // [4][512][16]
+    if (kq == 0) {
+        ml[(wave * 2) * 16 + m] = w.m_run;
+        ml[(wave * 2 + 1) * 16 + m] = l;
+    }
+#pragma unroll
+    for (int t = 0; t < OT; t++)
+#pragma unroll
+        for (int r = 0; r < 4; r++) ob[(wave * DL + 16 * t + 4 * kq + r) * 16 + m] = w.acc[t][r];
+    __syncthreads();
+    const size_t stride = (size_t)(DL + 2);
+    for (int i = tid; i < 16 * (DL + 2); i += 256) {
+        const int h = i & 15, d = i >> 4;                  // d: 0 m, 1 l, 2.. acc
+        if (h >= p.Hq) continue;
+        float M = -INFINITY;
+#pragma unroll
+        for (int u = 0; u < 4; u++) M = fmaxf(M, ml[(u * 2) * 16 + h]);
+        float v = M;
+        if (d > 0) {
+            v = 0.0f;
+#pragma unroll
+            for (int u = 0; u < 4; u++) {
+                const float mu = ml[(u * 2) * 16 + h];
+                const float f = (mu == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(mu - M);
+                v += f * (d == 1 ? ml[(u * 2 + 1) * 16 + h] : ob[(u * DL + d - 2) * 16 + h]);
+            }
+        }
+        p.part[((size_t)(a * p.Hq + h) * p.n_splits + s) * stride + d] = v;
+    }
+}
+
+}  // namespace
+
+bool mla_supported(int D, int H, int G, int rope_dim)
+{
+    return D == DL && H == 1 && G <= 16 && (rope_dim == 0 || rope_dim == 64);
+}
+
+void mla_plan(int A, int max_blocks, int window_cap, int *SB, int *n_splits)
+{
+    // about one workgroup per compute unit (the kernel holds 145 KB of LDS)
+    int sb = 1;
+    while ((long)A * ((max_blocks + sb - 1) / sb) > 256) sb <<= 1;
+    *SB = sb;
+    *n_splits = (max_blocks + sb - 1) / sb + (window_cap > 0 ? 1 : 0);
+    if (*n_splits < 1) *n_splits = 1;
+}
+
+hipError_t launch_mla(const DecodeArgs &p, const uint16_t *rope, int rope_dim, int64_t rope_tokens, hipStream_t s)
+{
+    dim3 grid(p.n_splits, 1, p.t.A);
+    if (rope_dim == 64) mla_split<64><<<grid, 256, 0, s>>>(p, rope, rope_tokens);
+    else mla_split<0><<<grid, 256, 0, s>>>(p, rope, rope_tokens);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    return launch_decode_merge(p, s);
+}
+
+}  // namespace kvq
