@@ -7,17 +7,20 @@
 // (of up to 16) scores key t as q_h . [latent_t ; rope_t] (576 dims) and
 // averages the dequantized latents (512 dims) as values.
 //
-// Work decomposition: a workgroup of four waves takes one sequence and SB
+// Work decomposition: a workgroup of eight waves takes one sequence and SB
 // consecutive blocks (or the sequence's bf16 window).  Per 64-key tile all
-// 256 lanes dequantize into LDS once -- K rows [key][576] for the scores and
-// the transposed latent V^T [512][key] for the values -- while the codes of
-// the next tile load into registers.  Wave w owns keys 16w..16w+15 of every
-// tile and keeps its own online softmax:
-//   S^T[key][head] = K.Q^T   v_mfma_f32_16x16x32_f16, 18 K-steps over 576 dims
-//   O^T[dim][head] += V^T.P^T v_mfma_f32_16x16x16_f16, 32 tiles of 16 dims
-// The S^T result layout (lane: head l%16, keys 4(l/16)..+3) is exactly the
-// B operand of the P.V product, so probabilities never leave registers.  At
-// the end the four waves' states combine through LDS into one partial
+// 512 lanes dequantize once into LDS as K rows [key][576] (double-buffered,
+// while the codes of the tile after next load into registers).  Wave w owns
+// keys 16(w%4)..+15 of every tile and latent dims 256(w/4)..+255 of the
+// output, with its own online softmax:
+//   S^T[key][head] = K.Q^T    v_mfma_f32_16x16x32_f16, 18 K-steps over 576 dims
+//   O^T[dim][head] += V^T.P^T v_mfma_f32_16x16x16_f16, 16 tiles of 16 dims
+// The V^T operand is read from the same K rows with ds_read_b64_tr_b16 (each
+// lane gets one dim of four consecutive keys), and the S^T result layout
+// (lane: head l%16, keys 4(l/16)..+3) is exactly the B operand of the P.V
+// product, so probabilities never leave registers.  Waves 4-7 dequantize
+// before their matrix work, waves 0-3 after, so the two waves of a SIMD
+// overlap.  At the end the key groups combine through LDS into one partial
 // (m, l, acc[512]) per head; the decode merge kernel combines the splits.
 #include "kvq_internal.h"
 #include "unpack.h"
@@ -29,37 +32,38 @@ using namespace dev;
 
 constexpr int DL = 512;                 // latent dims
 constexpr int TILE = 64;                // keys per tile (one block)
-constexpr int VR = TILE + 8;            // LDS V^T row stride (halves)
-constexpr int OT = DL / 16;             // 16-dim output tiles
+constexpr int OT = 256 / 16;            // 16-dim output tiles per wave
 constexpr float LAZY = 8.0f;            // running-max slack, log2 units
 
 typedef _Float16 h4 __attribute__((ext_vector_type(4)));
+typedef short s4 __attribute__((ext_vector_type(4)));
 
 template <int R>
 struct MCfg {
     static constexpr int DK = DL + R;   // score dims
     static constexpr int KR = DK + 8;   // LDS K row stride (halves)
     static constexpr int KS = DK / 32;  // K-steps of S^T
-    static constexpr int LDS_HALVES = TILE * KR + DL * VR;
+    static constexpr int BUF = TILE * KR;
 };
 
-// One lane's share of a quantized tile: key = tid & 63, latent dims
-// [128q, 128q + 128) for quarter q = tid >> 6 (16 chunks of 8 codes), the two
-// groups' metadata, and rope dims [16q, 16q + 16).
+// One lane's share of a quantized tile: key = tid & 63, latent group
+// e = tid >> 6 (dims 64e..64e+63, 8 chunks of 8 codes), its metadata, and
+// rope dims 8e..8e+7.
 struct MlaRaw {
-    uint32_t c[32];                     // 16 chunks x B bytes, unused dwords zero
-    uint32_t m0, m1;                    // (scale, bias) of groups 2q, 2q+1
-    uint32_t r[8];                      // 16 bf16 rope values
+    uint32_t c[16];                     // 8 chunks x B bytes, unused dwords zero
+    uint32_t m;                         // (scale, bias) of the group
+    uint32_t r[4];                      // 8 bf16 rope values
     int bits;
 };
 
 template <int B>
-__device__ __forceinline__ void load_share(uint32_t (&c)[32], const uint8_t *p)
+__device__ __forceinline__ void load_share(uint32_t (&c)[16], const uint8_t *p)
 {
 #pragma unroll
     for (int i = 0; i < B; i++) {
-        const uint4 x = reinterpret_cast<const uint4 *>(p)[i];
-        c[4 * i] = x.x; c[4 * i + 1] = x.y; c[4 * i + 2] = x.z; c[4 * i + 3] = x.w;
+        const uint2 x = reinterpret_cast<const uint2 *>(p)[i];
+        c[2 * i] = x.x;
+        c[2 * i + 1] = x.y;
     }
 }
 
@@ -69,35 +73,28 @@ template <int R>
 __device__ __forceinline__ void load_block(MlaRaw &raw, const DecodeArgs &p, const uint16_t *rope, int64_t rope_tokens,
                                            int a, int kt)
 {
-    const int tid = threadIdx.x, key = tid & 63, q = tid >> 6;
+    const int tid = threadIdx.x, key = tid & 63, e8 = tid >> 6;
     const size_t e = (size_t)a * p.t.max_blocks + kt;
     const int b = p.t.bits[e];
     const uint8_t *blk = p.k.pool + p.k.offset[e];
     const uint32_t row_bytes = (uint32_t)(DL / 8) * b;
-    uint32_t c[32];
+    uint32_t c[16];
 #pragma unroll
-    for (int i = 0; i < 32; i++) c[i] = 0;
-    const uint8_t *share = blk + key * row_bytes + q * (row_bytes / 4);
+    for (int i = 0; i < 16; i++) c[i] = 0;
+    const uint8_t *share = blk + key * row_bytes + e8 * (row_bytes / 8);
     switch (b) {
     case 2: load_share<2>(c, share); break;
     case 3: load_share<3>(c, share); break;
     case 4: load_share<4>(c, share); break;
     default: load_share<8>(c, share); break;
     }
-    const uint2 mm = *reinterpret_cast<const uint2 *>(blk + 64 * row_bytes + 4 * (key * (DL / 64) + 2 * q));
-    uint32_t r[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-    if (R) {
-        const uint4 *rp = reinterpret_cast<const uint4 *>(rope + ((size_t)a * rope_tokens + (size_t)kt * TILE + key) * R + 16 * q);
-        const uint4 x = rp[0], y = rp[1];
-        r[0] = x.x; r[1] = x.y; r[2] = x.z; r[3] = x.w;
-        r[4] = y.x; r[5] = y.y; r[6] = y.z; r[7] = y.w;
-    }
+    const uint32_t mm = *reinterpret_cast<const uint32_t *>(blk + 64 * row_bytes + 4 * (key * (DL / 64) + e8));
+    uint4 rr = {0, 0, 0, 0};
+    if (R) rr = *reinterpret_cast<const uint4 *>(rope + ((size_t)a * rope_tokens + (size_t)kt * TILE + key) * R + 8 * e8);
 #pragma unroll
-    for (int i = 0; i < 32; i++) raw.c[i] = c[i];
-#pragma unroll
-    for (int i = 0; i < 8; i++) raw.r[i] = r[i];
-    raw.m0 = mm.x;
-    raw.m1 = mm.y;
+    for (int i = 0; i < 16; i++) raw.c[i] = c[i];
+    raw.r[0] = rr.x; raw.r[1] = rr.y; raw.r[2] = rr.z; raw.r[3] = rr.w;
+    raw.m = mm;
     raw.bits = b;
 }
 
@@ -115,12 +112,15 @@ __device__ __forceinline__ Pairs share_chunk(const MlaRaw &raw, int ch)
         pr = Unpack<8>::run2(raw.c[2 * ch], raw.c[2 * ch + 1]);
     } else {
         const int o = 3 * ch, i = o >> 2;                 // compile-time after unrolling
-        pr = Unpack<3>::run3(raw.c[i], raw.c[i + 1 < 12 ? i + 1 : i], o & 3);
+        pr = Unpack<3>::run3(raw.c[i], raw.c[i + 1 < 6 ? i + 1 : i], o & 3);
     }
-    dequant(pr, ch < 8 ? raw.m0 : raw.m1);
+    dequant(pr, raw.m);
     return pr;
 }
 
+// The fp16 pairs (c0,c4) (c1,c5) (c2,c6) (c3,c7) of a chunk as 8 halves in
+// that order: K rows keep each chunk in this order (the query operand is
+// built the same way); stored position k holds dim (k>>1) + 4(k&1).
 __device__ __forceinline__ h8 row_order(const Pairs &p)
 {
     h8 o;
@@ -129,41 +129,31 @@ __device__ __forceinline__ h8 row_order(const Pairs &p)
     return o;
 }
 
-// Write chunk ch of the lane's share: K row (chunk order, as the query
-// operand uses) and V^T column (true dim order).
-__device__ __forceinline__ void put_chunk(_Float16 *kh, _Float16 *vt, int KR, int key, int q, int ch, const Pairs &pr)
-{
-    const int d0 = 128 * q + 8 * ch;
-    *reinterpret_cast<h8 *>(kh + key * KR + d0) = row_order(pr);
-#pragma unroll
-    for (int i = 0; i < 4; i++) {
-        vt[(d0 + i) * VR + key] = pr.p[i][0];
-        vt[(d0 + i + 4) * VR + key] = pr.p[i][1];
-    }
-}
+__device__ __forceinline__ int true_dim(int k) { return (k & ~7) | ((k & 7) >> 1) | ((k & 1) << 2); }
 
 template <int R, int B>
-__device__ __forceinline__ void store_block(const MlaRaw &raw, _Float16 *kh, _Float16 *vt)
+__device__ __forceinline__ void store_block(const MlaRaw &raw, _Float16 *kh)
 {
     constexpr int KR = MCfg<R>::KR;
-    const int tid = threadIdx.x, key = tid & 63, q = tid >> 6;
+    const int tid = threadIdx.x, key = tid & 63, e8 = tid >> 6;
+    _Float16 *row = kh + key * KR;
 #pragma unroll
-    for (int ch = 0; ch < 16; ch++) put_chunk(kh, vt, KR, key, q, ch, share_chunk<B>(raw, ch));
+    for (int ch = 0; ch < 8; ch++)
+        *reinterpret_cast<h8 *>(row + 64 * e8 + 8 * ch) = row_order(share_chunk<B>(raw, ch));
     if (R) {
-        const uint4 x = {raw.r[0], raw.r[1], raw.r[2], raw.r[3]}, y = {raw.r[4], raw.r[5], raw.r[6], raw.r[7]};
-        *reinterpret_cast<h8 *>(kh + key * KR + DL + 16 * q) = row_order(bf16_pairs(x));
-        *reinterpret_cast<h8 *>(kh + key * KR + DL + 16 * q + 8) = row_order(bf16_pairs(y));
+        const uint4 x = {raw.r[0], raw.r[1], raw.r[2], raw.r[3]};
+        *reinterpret_cast<h8 *>(row + DL + 8 * e8) = row_order(bf16_pairs(x));
     }
 }
 
 template <int R>
-__device__ __forceinline__ void store_raw(const MlaRaw &raw, _Float16 *kh, _Float16 *vt)
+__device__ __forceinline__ void store_raw(const MlaRaw &raw, _Float16 *kh)
 {
     switch (raw.bits) {
-    case 2: store_block<R, 2>(raw, kh, vt); break;
-    case 3: store_block<R, 3>(raw, kh, vt); break;
-    case 4: store_block<R, 4>(raw, kh, vt); break;
-    default: store_block<R, 8>(raw, kh, vt); break;
+    case 2: store_block<R, 2>(raw, kh); break;
+    case 3: store_block<R, 3>(raw, kh); break;
+    case 4: store_block<R, 4>(raw, kh); break;
+    default: store_block<R, 8>(raw, kh); break;
     }
 }
 
@@ -171,25 +161,25 @@ __device__ __forceinline__ void store_raw(const MlaRaw &raw, _Float16 *kh, _Floa
 // window repeat its last row; they are masked).
 template <int R>
 __device__ __forceinline__ void store_window(const DecodeArgs &p, const uint16_t *rope, int64_t rope_tokens, int a,
-                                             int nb, int nw, int w0, _Float16 *kh, _Float16 *vt)
+                                             int nb, int nw, int w0, _Float16 *kh)
 {
     constexpr int KR = MCfg<R>::KR;
-    const int tid = threadIdx.x, key = tid & 63, q = tid >> 6;
+    const int tid = threadIdx.x, key = tid & 63, e8 = tid >> 6;
     const int w = min(w0 + key, nw - 1);
-    const uint16_t *src = p.k.window + ((size_t)a * p.t.window_cap + w) * DL + 128 * q;
+    const uint4 *src = reinterpret_cast<const uint4 *>(p.k.window + ((size_t)a * p.t.window_cap + w) * DL + 64 * e8);
+    _Float16 *row = kh + key * KR;
 #pragma unroll
-    for (int ch = 0; ch < 16; ch++)
-        put_chunk(kh, vt, KR, key, q, ch, bf16_pairs(reinterpret_cast<const uint4 *>(src)[ch]));
+    for (int ch = 0; ch < 8; ch++) *reinterpret_cast<h8 *>(row + 64 * e8 + 8 * ch) = row_order(bf16_pairs(src[ch]));
     if (R) {
         const uint4 *rp = reinterpret_cast<const uint4 *>(
-            rope + ((size_t)a * rope_tokens + (size_t)nb * TILE + w) * R + 16 * q);
-        *reinterpret_cast<h8 *>(kh + key * KR + DL + 16 * q) = row_order(bf16_pairs(rp[0]));
-        *reinterpret_cast<h8 *>(kh + key * KR + DL + 16 * q + 8) = row_order(bf16_pairs(rp[1]));
+            rope + ((size_t)a * rope_tokens + (size_t)nb * TILE + w) * R + 8 * e8);
+        *reinterpret_cast<h8 *>(row + DL + 8 * e8) = row_order(bf16_pairs(rp[0]));
     }
 }
 
 // Per-wave state: lane l is head l%16; of each tile it scores keys
-// 16w + 4(l/16) + r and holds O^T rows 16t + 4(l/16) + r.
+// 16(w%4) + 4(l/16) + r and holds O^T rows (stored positions)
+// 256(w/4) + 16t + 4(l/16) + r.
 template <int R>
 struct MlaState {
     h8 qop[MCfg<R>::KS];
@@ -198,11 +188,11 @@ struct MlaState {
 };
 
 template <int R>
-__device__ __forceinline__ void tile_compute(MlaState<R> &w, const _Float16 *kh, const _Float16 *vt, int valid, float c)
+__device__ __forceinline__ void tile_compute(MlaState<R> &w, const _Float16 *kh, int valid, float c, int kg, int dh)
 {
     constexpr int KR = MCfg<R>::KR, KS = MCfg<R>::KS;
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, m = lane & 15, kq = lane >> 4;
-    const int k0 = 16 * wave;
+    const int lane = threadIdx.x & 63, m = lane & 15, kq = lane >> 4;
+    const int k0 = 16 * kg;
     f4 st = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int s = 0; s < KS; s++) {
@@ -234,22 +224,28 @@ __device__ __forceinline__ void tile_compute(MlaState<R> &w, const _Float16 *kh,
         for (int t = 0; t < OT; t++) w.acc[t] *= alpha;
     }
     const h4 pb = {p01[0], p01[1], p23[0], p23[1]};
+    // V^T operand: lane j of each 16-lane group addresses key k0 + 4(l/16) + j/4,
+    // positions n0 + 4(j%4)..+3; the transposed read hands lane l position
+    // n0 + l%16 of those four keys.
+    const _Float16 *vb = kh + (k0 + 4 * kq + (m >> 2)) * KR + 256 * dh + 4 * (m & 3);
 #pragma unroll
     for (int t = 0; t < OT; t++) {
-        const h4 av = *reinterpret_cast<const h4 *>(vt + (16 * t + m) * VR + k0 + 4 * kq);
-        w.acc[t] = __builtin_amdgcn_mfma_f32_16x16x16f16(av, pb, w.acc[t], 0, 0, 0);
+        const s4 raw = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) s4 *)(vb + 16 * t));
+        w.acc[t] = __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(h4, raw), pb, w.acc[t], 0, 0, 0);
     }
 }
 
 template <int R>
-__global__ __launch_bounds__(256, 1) void mla_split(DecodeArgs p, const uint16_t *rope, int64_t rope_tokens)
+__global__ __launch_bounds__(512, 1) void mla_split(DecodeArgs p, const uint16_t *rope, int64_t rope_tokens)
 {
     using C = MCfg<R>;
-    __shared__ __attribute__((aligned(16))) _Float16 lds[C::LDS_HALVES];
-    _Float16 *kh = lds, *vt = lds + TILE * C::KR;
+    __shared__ __attribute__((aligned(16))) _Float16 lds[2 * C::BUF];
 
     const int s = blockIdx.x, a = blockIdx.z;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, m = lane & 15, kq = lane >> 4;
+    const int tid = threadIdx.x, lane = tid & 63, m = lane & 15, kq = lane >> 4;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int kg = wave & 3, dh = wave >> 2;
     const int nb = seq_blocks(p.t, a), nw = seq_window(p.t, a);
     const int nsb = (nb + p.SB - 1) / p.SB;
     const bool win = (s == nsb) && nw > 0;
@@ -270,42 +266,53 @@ __global__ __launch_bounds__(256, 1) void mla_split(DecodeArgs p, const uint16_t
     w.l_run = 0.0f;
 
     if (!win) {
-        const int j0 = s * p.SB, j1 = min(j0 + p.SB, nb);
+        // Tile j in buffer j&1; between barriers the tile j+1 is stored into
+        // the other buffer (last read before the previous barrier).
+        const int j0 = s * p.SB, n = min(j0 + p.SB, nb) - j0;
         MlaRaw raw;
         load_block<R>(raw, p, rope, rope_tokens, a, j0);
-        for (int j = j0; j < j1; j++) {
-            __syncthreads();                             // previous tile no longer read
-            store_raw<R>(raw, kh, vt);
-            if (j + 1 < j1) load_block<R>(raw, p, rope, rope_tokens, a, j + 1);
+        store_raw<R>(raw, lds);
+        if (n > 1) load_block<R>(raw, p, rope, rope_tokens, a, j0 + 1);
+        __syncthreads();
+        for (int j = 0; j < n; j++) {
+            _Float16 *cur = lds + (j & 1) * C::BUF, *nxt = lds + ((j + 1) & 1) * C::BUF;
+            if (dh && j + 1 < n) {
+                store_raw<R>(raw, nxt);
+                if (j + 2 < n) load_block<R>(raw, p, rope, rope_tokens, a, j0 + j + 2);
+            }
+            tile_compute<R>(w, cur, TILE, p.c, kg, dh);
+            if (!dh && j + 1 < n) {
+                store_raw<R>(raw, nxt);
+                if (j + 2 < n) load_block<R>(raw, p, rope, rope_tokens, a, j0 + j + 2);
+            }
             __syncthreads();
-            tile_compute<R>(w, kh, vt, TILE, p.c);
         }
     } else {
         for (int w0 = 0; w0 < nw; w0 += TILE) {
+            store_window<R>(p, rope, rope_tokens, a, nb, nw, w0, lds);
             __syncthreads();
-            store_window<R>(p, rope, rope_tokens, a, nb, nw, w0, kh, vt);
+            tile_compute<R>(w, lds, nw - w0, p.c, kg, dh);
             __syncthreads();
-            tile_compute<R>(w, kh, vt, nw - w0, p.c);
         }
     }
 
-    // Combine the four waves: (m, l) per head and O^T [512][16] per wave.
+    // Combine the four key groups: (m, l) per head and O^T [512][16].
     float l = w.l_run + __shfl_xor(w.l_run, 16);
     l += __shfl_xor(l, 32);
-    __syncthreads();
     float *ml = reinterpret_cast<float *>(lds);           // [4][2][16]
-    float *ob = ml + 128;                                  // [4][512][16]
-    if (kq == 0) {
-        ml[(wave * 2) * 16 + m] = w.m_run;
-        ml[(wave * 2 + 1) * 16 + m] = l;
+    float *ob = ml + 128;                                  // [4][512][16], true dims
+    if (kq == 0 && dh == 0) {
+        ml[(kg * 2) * 16 + m] = w.m_run;
+        ml[(kg * 2 + 1) * 16 + m] = l;
     }
 #pragma unroll
     for (int t = 0; t < OT; t++)
 #pragma unroll
-        for (int r = 0; r < 4; r++) ob[(wave * DL + 16 * t + 4 * kq + r) * 16 + m] = w.acc[t][r];
+        for (int r = 0; r < 4; r++)
+            ob[(kg * DL + true_dim(256 * dh + 16 * t + 4 * kq + r)) * 16 + m] = w.acc[t][r];
     __syncthreads();
     const size_t stride = (size_t)(DL + 2);
-    for (int i = tid; i < 16 * (DL + 2); i += 256) {
+    for (int i = tid; i < 16 * (DL + 2); i += 512) {
         const int h = i & 15, d = i >> 4;                  // d: 0 m, 1 l, 2.. acc
         if (h >= p.Hq) continue;
         float M = -INFINITY;
@@ -334,7 +341,7 @@ bool mla_supported(int D, int H, int G, int rope_dim)
 
 void mla_plan(int A, int max_blocks, int window_cap, int *SB, int *n_splits)
 {
-    // about one workgroup per compute unit (the kernel holds 145 KB of LDS)
+    // about one workgroup per compute unit (the kernel holds 146 KB of LDS)
     int sb = 1;
     while ((long)A * ((max_blocks + sb - 1) / sb) > 256) sb <<= 1;
     *SB = sb;
@@ -345,8 +352,8 @@ void mla_plan(int A, int max_blocks, int window_cap, int *SB, int *n_splits)
 hipError_t launch_mla(const DecodeArgs &p, const uint16_t *rope, int rope_dim, int64_t rope_tokens, hipStream_t s)
 {
     dim3 grid(p.n_splits, 1, p.t.A);
-    if (rope_dim == 64) mla_split<64><<<grid, 256, 0, s>>>(p, rope, rope_tokens);
-    else mla_split<0><<<grid, 256, 0, s>>>(p, rope, rope_tokens);
+    if (rope_dim == 64) mla_split<64><<<grid, 512, 0, s>>>(p, rope, rope_tokens);
+    else mla_split<0><<<grid, 512, 0, s>>>(p, rope, rope_tokens);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     return launch_decode_merge(p, s);
