@@ -18,17 +18,19 @@
 //   P.V    for each 4-token slice s, A = P[heads][tokens 4s..4s+3], which is
 //          exactly what the lanes of block s hold after the softmax, broadcast
 //          to all 16 blocks by the instruction's CBSZ/ABID fields; B = V rows
-//          of those 4 tokens for 4 output dims per block, read from a
-//          transposed fp16 copy of V in LDS.  No lane shuffles move
-//          probabilities.
+//          of those 4 tokens for 4 output dims per block: each lane writes its
+//          dequantized V row to LDS and ds_read_b64_tr_b16 hands lane l dim
+//          l of four consecutive tokens.  No lane shuffles move probabilities.
 // Codes become fp16 with an and_or magic-exponent unpack and two packed
 // fmas (exact code, then code*scale+bias).  The softmax runs in fp32 (exp2);
 // probabilities rounded to fp16 feed P.V and the running sum adds those same
 // rounded values.
 //
 // Work decomposition: one wave per (key split, KV head, sequence); a split is
-// SB 64-token blocks or the bf16 window.  Partials (max, sum, unnormalised
-// output) are combined by the decode merge kernel.
+// SB 64-token blocks or the bf16 window; many small waves per SIMD hide the
+// load latency.  The split's widths and pool offsets sit one per lane
+// (v_readlane), so no block's loads wait on a scalar load.  Partials (max,
+// sum, unnormalised output) are combined by the decode merge kernel.
 #include "kvq_internal.h"
 #include "unpack.h"
 
@@ -38,8 +40,7 @@ namespace {
 using namespace dev;
 
 typedef _Float16 h4 __attribute__((ext_vector_type(4)));
-
-constexpr int VTS = 68;        // LDS stride of one V^T row (64 tokens + 4 pad), in halves
+typedef short s4 __attribute__((ext_vector_type(4)));
 
 // A lane's full token row of codes: D*B/8 bytes as dwords (sized for 8 bits).
 template <int B, int NG>
@@ -109,11 +110,14 @@ __device__ __forceinline__ f4 scores(const h4 (*qs)[4], KF kdeq)
 
 // Online softmax on the scores of one 64-token round (lane (b, j): tokens
 // 4b..4b+3 of head j), then O += P.V for every 64-dim output set; vdeq(c)
-// yields the dequantized pairs of chunk c of the lane's value row.
+// yields the dequantized pairs of chunk c of the lane's value row.  V rows go
+// to LDS in chunk order (position k of a chunk holds dim (k>>1) + 4(k&1)),
+// so lane l accumulates output dim 64hh + that permutation of l.
 template <int NG, typename VF>
 __device__ __forceinline__ void softmax_pv(State<NG> &st, f4 s, int n_valid, float c,
-                                           _Float16 *vt, VF vdeq)
+                                           _Float16 *vr, VF vdeq)
 {
+    constexpr int VS = 64 + 8;                // LDS row stride of one 64-dim set (halves)
     const int lane = threadIdx.x, b = lane >> 2, j = lane & 3;
     float sc[4];
 #pragma unroll
@@ -142,53 +146,85 @@ __device__ __forceinline__ void softmax_pv(State<NG> &st, f4 s, int n_valid, flo
     }
     const h4 pa = {p01[0], p01[1], p23[0], p23[1]};   // A operand: head j, tokens 4b..4b+3
 
+    // Per 64-dim set: the lane's V row (token = lane) into LDS, then 16
+    // slices of 4 tokens.  One wave owns the buffer: its LDS instructions
+    // execute in order, so only the compiler needs a barrier between the
+    // writes and the reads (and before the next set's writes).
+    // Transposed read for slice S: lane i of each 16-lane group addresses
+    // token 4S + i/4, positions 16(l/16) + 4(i%4)..+3 of the set.
+    const _Float16 *vb = vr + ((lane & 15) >> 2) * VS + 16 * (lane >> 4) + 4 * (lane & 3);
 #pragma unroll
     for (int hh = 0; hh < NG; hh++) {
-        // V^T of dims 64hh..64hh+63: this lane writes its token's column.
 #pragma unroll
         for (int cc = 0; cc < 8; cc++) {
             const Pairs pr = vdeq(8 * hh + cc);
-#pragma unroll
-            for (int i = 0; i < 4; i++) {
-                vt[(8 * cc + i) * VTS + lane] = pr.p[i][0];
-                vt[(8 * cc + i + 4) * VTS + lane] = pr.p[i][1];
-            }
+            *reinterpret_cast<h8 *>(vr + lane * VS + 8 * cc) =
+                h8{pr.p[0][0], pr.p[0][1], pr.p[1][0], pr.p[1][1], pr.p[2][0], pr.p[2][1], pr.p[3][0], pr.p[3][1]};
         }
-        __syncthreads();
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
         f4 acc = st.o[hh];
-        const _Float16 *vrow = vt + (4 * b + j) * VTS;
-#define KVQ_PV(S) acc = __builtin_amdgcn_mfma_f32_4x4x4f16(pa, *reinterpret_cast<const h4 *>(vrow + 4 * (S)), acc, 4, S, 0)
+#define KVQ_PV(S)                                                                                     \
+    acc = __builtin_amdgcn_mfma_f32_4x4x4f16(                                                         \
+        pa,                                                                                           \
+        __builtin_bit_cast(h4, __builtin_amdgcn_ds_read_tr16_b64_v4i16(                               \
+                                   (__attribute__((address_space(3))) s4 *)(vb + 4 * (S) * VS))),   \
+        acc, 4, S, 0)
         KVQ_PV(0); KVQ_PV(1); KVQ_PV(2); KVQ_PV(3); KVQ_PV(4); KVQ_PV(5); KVQ_PV(6); KVQ_PV(7);
         KVQ_PV(8); KVQ_PV(9); KVQ_PV(10); KVQ_PV(11); KVQ_PV(12); KVQ_PV(13); KVQ_PV(14); KVQ_PV(15);
 #undef KVQ_PV
         st.o[hh] = acc;
-        __syncthreads();
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    }
+}
+
+// Widths and pool offsets of up to 64 consecutive blocks, one per lane, so
+// a block's loads never wait on a dependent scalar load.
+struct SplitMeta {
+    int base, bits;
+    uint32_t klo, khi, vlo, vhi;
+};
+
+__device__ __forceinline__ void split_meta(SplitMeta &sm, const DecodeArgs &p, int a, int j0, int j1)
+{
+    const int jb = j0 + (int)threadIdx.x;
+    sm.base = j0;
+    sm.bits = 0;
+    sm.klo = sm.khi = sm.vlo = sm.vhi = 0;
+    if (jb < j1) {
+        const size_t e = (size_t)a * p.t.max_blocks + jb;
+        sm.bits = p.t.bits[e];
+        const uint64_t ko = p.k.offset[e], vo = p.v.offset[e];
+        sm.klo = (uint32_t)ko; sm.khi = (uint32_t)(ko >> 32);
+        sm.vlo = (uint32_t)vo; sm.vhi = (uint32_t)(vo >> 32);
     }
 }
 
 template <int B, int NG>
 __device__ __forceinline__ void round_block(State<NG> &st, const h4 (*qs)[4], const uint8_t *kblk,
-                                            const uint8_t *vblk, int H, int g, float c, _Float16 *vt)
+                                            const uint8_t *vblk, int H, int g, float c, _Float16 *vr)
 {
-    constexpr int CODE_ROW = 8 * NG * B;
+    constexpr uint32_t CODE_ROW = 8 * NG * B;
     constexpr int NDW = FullRow<B, NG>::NDW;
-    const int lane = threadIdx.x;
-    const size_t row = (size_t)g * 64 + lane;
-    const size_t meta0 = (size_t)H * 64 * CODE_ROW;
+    const uint32_t row = (uint32_t)g * 64 + threadIdx.x;
+    const uint32_t moff = (uint32_t)H * 64 * CODE_ROW + 4 * NG * row;
     uint32_t kw[NDW], vw[NDW], km[NG], vm[NG];
     FullRow<B, NG>::load(kw, kblk + row * CODE_ROW);
     FullRow<B, NG>::load(vw, vblk + row * CODE_ROW);
 #pragma unroll
     for (int i = 0; i < NG; i++) {
-        km[i] = reinterpret_cast<const uint32_t *>(kblk + meta0)[row * NG + i];
-        vm[i] = reinterpret_cast<const uint32_t *>(vblk + meta0)[row * NG + i];
+        km[i] = reinterpret_cast<const uint32_t *>(kblk + moff)[i];
+        vm[i] = reinterpret_cast<const uint32_t *>(vblk + moff)[i];
     }
     const f4 s = scores<NG>(qs, [&](int cidx) {
         Pairs pr = FullRow<B, NG>::chunk(kw, cidx);
         dequant(pr, km[cidx >> 3]);
         return pr;
     });
-    softmax_pv<NG>(st, s, 64, c, vt, [&](int cidx) {
+    softmax_pv<NG>(st, s, 64, c, vr, [&](int cidx) {
         Pairs pr = FullRow<B, NG>::chunk(vw, cidx);
         dequant(pr, vm[cidx >> 3]);
         return pr;
@@ -214,7 +250,7 @@ __global__ __launch_bounds__(64) void decode_g4_split(DecodeArgs p)
 {
     constexpr int D = 64 * NG, NCH = 8 * NG;
     __shared__ __attribute__((aligned(16))) h4 qs[2 * NCH][4];      // [slice][head], permuted dims
-    __shared__ __attribute__((aligned(16))) _Float16 vt[64 * VTS];  // V^T of one 64-dim set
+    __shared__ __attribute__((aligned(16))) _Float16 vt[64 * 72];  // V rows, one 64-dim set
     const int s = blockIdx.x, g = blockIdx.y, a = blockIdx.z;
     const int lane = threadIdx.x, b = lane >> 2, j = lane & 3;
     const int nb = seq_blocks(p.t, a), nw = seq_window(p.t, a);
@@ -244,12 +280,17 @@ __global__ __launch_bounds__(64) void decode_g4_split(DecodeArgs p)
     st.l_lane = 0.0f;
 
     if (!win) {
-        const int j1 = min((s + 1) * p.SB, nb);
-        for (int jb = s * p.SB; jb < j1; jb++) {
-            const size_t e = (size_t)a * p.t.max_blocks + jb;
-            const int bw = p.t.bits[e];
-            const uint8_t *kb = p.k.pool + p.k.offset[e];
-            const uint8_t *vb = p.v.pool + p.v.offset[e];
+        const int j0 = s * p.SB, j1 = min(j0 + p.SB, nb);
+        SplitMeta sm;
+        sm.base = -(1 << 20);
+        for (int jb = j0; jb < j1; jb++) {
+            if (jb - sm.base >= 64) split_meta(sm, p, a, jb, j1);   // blocks are visited in order
+            const int i = jb - sm.base;
+            const int bw = __builtin_amdgcn_readlane(sm.bits, i);
+            const uint8_t *kb = p.k.pool + (((uint64_t)(uint32_t)__builtin_amdgcn_readlane(sm.khi, i) << 32) |
+                                            (uint32_t)__builtin_amdgcn_readlane(sm.klo, i));
+            const uint8_t *vb = p.v.pool + (((uint64_t)(uint32_t)__builtin_amdgcn_readlane(sm.vhi, i) << 32) |
+                                            (uint32_t)__builtin_amdgcn_readlane(sm.vlo, i));
             switch (bw) {
             case 2: round_block<2, NG>(st, qs, kb, vb, p.t.H, g, p.c, vt); break;
             case 3: round_block<3, NG>(st, qs, kb, vb, p.t.H, g, p.c, vt); break;
@@ -278,8 +319,10 @@ __global__ __launch_bounds__(64) void decode_g4_split(DecodeArgs p)
     for (int i = 0; i < 4; i++) {
         if (i < p.G) {
             float *pr = p.part + ((rbase + i) * p.n_splits + s) * stride + 2;
+            // lane l holds dim 64hh + (chunk-order position l)
+            const int d = ((4 * b + j) & ~7) | (((4 * b + j) & 7) >> 1) | (((4 * b + j) & 1) << 2);
 #pragma unroll
-            for (int hh = 0; hh < NG; hh++) pr[64 * hh + 4 * b + j] = st.o[hh][i];
+            for (int hh = 0; hh < NG; hh++) pr[64 * hh + d] = st.o[hh][i];
         }
     }
 }
@@ -287,6 +330,21 @@ __global__ __launch_bounds__(64) void decode_g4_split(DecodeArgs p)
 }  // namespace
 
 bool decode_g4_supported(int D, int G) { return G <= 4 && (D == 64 || D == 128 || D == 256); }
+
+void decode_g4_plan(int A, int H, int max_blocks, int window_cap, int *SB, int *n_splits)
+{
+    // Longest splits that still give about KVQ_G4_WAVES waves (latency is
+    // hidden by waves in flight; longer splits keep the merge's partials small).
+#ifndef KVQ_G4_WAVES
+#define KVQ_G4_WAVES 2048
+#endif
+    int sb = 64;
+    while (sb > 1 && (long)A * H * ((max_blocks + sb - 1) / sb) < KVQ_G4_WAVES) sb >>= 1;
+    while ((max_blocks + sb - 1) / sb + 1 > 512) sb <<= 1;     // merge limit on splits
+    *SB = sb;
+    *n_splits = (max_blocks + sb - 1) / sb + (window_cap > 0 ? 1 : 0);
+    if (*n_splits < 1) *n_splits = 1;
+}
 
 hipError_t launch_decode_g4(const DecodeArgs &p, hipStream_t s)
 {

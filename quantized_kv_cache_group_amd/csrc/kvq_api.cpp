@@ -70,6 +70,7 @@ size_t round256(size_t b) { return (b + 255) / 256 * 256; }
 struct Plan {
     int tok_per_tile, split_keys, n_splits, n_row_tiles;
     int sb, dec_splits;         // tuned decode
+    int g4_sb, g4_splits;       // tuned decode, <= 4 query heads per KV head
     int mla_sb, mla_splits;     // latent decode
     int ch_row_tiles, ch_splits, ch_split_tiles;   // tuned chunk
     bool ch_ok;
@@ -98,6 +99,11 @@ int plan_attention(const kvq_layout *L, int n_q_heads, int rope_dim, int n_new, 
         decode_gqa_plan(L->n_seqs, L->n_heads, L->max_blocks, L->window_cap, &pl->sb, &pl->dec_splits);
         size_t t = round256(rows * (size_t)pl->dec_splits * (size_t)(L->head_dim + 2) * sizeof(float));
         if (t > pl->ws_bytes) pl->ws_bytes = t;
+        if (decode_g4_supported(L->head_dim, G)) {
+            decode_g4_plan(L->n_seqs, L->n_heads, L->max_blocks, L->window_cap, &pl->g4_sb, &pl->g4_splits);
+            t = round256(rows * (size_t)pl->g4_splits * (size_t)(L->head_dim + 2) * sizeof(float));
+            if (t > pl->ws_bytes) pl->ws_bytes = t;
+        }
         if (mla_supported(L->head_dim, L->n_heads, G, rope_dim)) {
             mla_plan(L->n_seqs, L->max_blocks, L->window_cap, &pl->mla_sb, &pl->mla_splits);
             t = round256(rows * (size_t)pl->mla_splits * (size_t)(L->head_dim + 2) * sizeof(float));
@@ -221,6 +227,8 @@ int kvq_attend_decode(const kvq_layout *L, const kvq_store *K, const kvq_store *
         d.c = softmax_scale * 1.4426950408889634f;
         hipStream_t hs = static_cast<hipStream_t>(stream);
         if (decode_g4_supported(L->head_dim, d.G)) {
+            d.SB = pl.g4_sb;
+            d.n_splits = pl.g4_splits;
             hipError_t e = launch_decode_g4(d, hs);
             if (e != hipSuccess) return KVQ_EHIP;
             return hip_status(launch_decode_merge(d, hs));

@@ -100,6 +100,7 @@ hipError_t launch_decode_gqa(const DecodeArgs &a, hipStream_t s);     // split +
 hipError_t launch_decode_g4(const DecodeArgs &a, hipStream_t s);      // split only (G <= 4)
 hipError_t launch_decode_merge(const DecodeArgs &a, hipStream_t s);
 bool decode_g4_supported(int D, int G);
+void decode_g4_plan(int A, int H, int max_blocks, int window_cap, int *SB, int *n_splits);
 hipError_t launch_chunk(const ChunkArgs &a, hipStream_t s);          // split + merge
 bool chunk_supported(int D);
 int chunk_rows_per_wg(int D);
