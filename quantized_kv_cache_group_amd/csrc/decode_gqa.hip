@@ -401,7 +401,7 @@ __global__ __launch_bounds__(64) void decode_gqa_split(DecodeArgs p)
 // Combine the splits of one (sequence, query head): max-rescaled sums in the
 // log2 domain of the split kernel.  One wave per row: lanes first reduce the
 // split maxima and sums, keep the split weights in LDS, then stream the
-// partial outputs of a 128-dim slice (grid.y) with independent loads.
+// partial outputs of a 64-dim slice (grid.y) with independent loads.
 constexpr int MERGE_ROWS = 4;
 constexpr int MAX_SPLITS = 512;
 
@@ -433,28 +433,20 @@ __global__ __launch_bounds__(64 * MERGE_ROWS) void decode_gqa_merge(DecodeArgs p
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     const float inv = L > 0.0f ? 1.0f / L : 0.0f;
     float *o = p.out + (size_t)row * D;
-    // grid.y splits the dims into 128-wide slices (one float2 per lane)
-    const int d = 128 * blockIdx.y + 2 * lane;
+    // grid.y splits the dims into 64-wide slices (one dim per lane)
+    const int d = 64 * blockIdx.y + lane;
     if (d < D) {
-        float ax = 0.0f, ay = 0.0f;
+        float ax = 0.0f;
         int s = 0;
         for (; s + 8 <= ns; s += 8) {
-            float2 v[8];
+            float v[8];
 #pragma unroll
-            for (int u = 0; u < 8; u++) v[u] = *reinterpret_cast<const float2 *>(pr + (s + u) * stride + 2 + d);
+            for (int u = 0; u < 8; u++) v[u] = pr[(s + u) * stride + 2 + d];
 #pragma unroll
-            for (int u = 0; u < 8; u++) {
-                const float w = wsh[wave][s + u];
-                ax += w * v[u].x;
-                ay += w * v[u].y;
-            }
+            for (int u = 0; u < 8; u++) ax += wsh[wave][s + u] * v[u];
         }
-        for (; s < ns; s++) {
-            const float2 v = *reinterpret_cast<const float2 *>(pr + s * stride + 2 + d);
-            ax += wsh[wave][s] * v.x;
-            ay += wsh[wave][s] * v.y;
-        }
-        *reinterpret_cast<float2 *>(o + d) = make_float2(ax * inv, ay * inv);
+        for (; s < ns; s++) ax += wsh[wave][s] * pr[s * stride + 2 + d];
+        o[d] = ax * inv;
     }
 }
 
@@ -491,7 +483,7 @@ hipError_t launch_decode_gqa(const DecodeArgs &p, hipStream_t s)
 
 hipError_t launch_decode_merge(const DecodeArgs &p, hipStream_t s)
 {
-    decode_gqa_merge<<<dim3((p.t.A * p.Hq + MERGE_ROWS - 1) / MERGE_ROWS, (p.t.D + 127) / 128), 64 * MERGE_ROWS, 0,
+    decode_gqa_merge<<<dim3((p.t.A * p.Hq + MERGE_ROWS - 1) / MERGE_ROWS, (p.t.D + 63) / 64), 64 * MERGE_ROWS, 0,
                        s>>>(p);
     return hipGetLastError();
 }

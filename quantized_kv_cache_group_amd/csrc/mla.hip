@@ -67,34 +67,58 @@ __device__ __forceinline__ void load_share(uint32_t (&c)[16], const uint8_t *p)
     }
 }
 
+// Widths and pool offsets of up to 64 consecutive blocks, one per lane, so
+// a tile's loads never wait on a dependent scalar load.
+struct MlaMeta {
+    int base, bits;
+    uint32_t lo, hi;
+};
+
+__device__ __forceinline__ void mla_meta(MlaMeta &mm, const DecodeArgs &p, int a, int j0, int j1)
+{
+    const int jb = j0 + (int)(threadIdx.x & 63);
+    mm.base = j0;
+    mm.bits = 0;
+    mm.lo = mm.hi = 0;
+    if (jb < j1) {
+        const size_t e = (size_t)a * p.t.max_blocks + jb;
+        mm.bits = p.t.bits[e];
+        const uint64_t o = p.k.offset[e];
+        mm.lo = (uint32_t)o;
+        mm.hi = (uint32_t)(o >> 32);
+    }
+}
+
 // Codes, metadata and rope of block kt (all fields assigned once, so the
 // record stays in registers across the width branches).
 template <int R>
-__device__ __forceinline__ void load_block(MlaRaw &raw, const DecodeArgs &p, const uint16_t *rope, int64_t rope_tokens,
-                                           int a, int kt)
+__device__ __forceinline__ void load_block(MlaRaw &raw, MlaMeta &mm, const DecodeArgs &p, const uint16_t *rope,
+                                           int64_t rope_tokens, int a, int kt, int j1)
 {
     const int tid = threadIdx.x, key = tid & 63, e8 = tid >> 6;
-    const size_t e = (size_t)a * p.t.max_blocks + kt;
-    const int b = p.t.bits[e];
-    const uint8_t *blk = p.k.pool + p.k.offset[e];
+    if (kt - mm.base >= 64) mla_meta(mm, p, a, kt, j1);   // blocks are visited in order
+    const int i = kt - mm.base;
+    const int b = __builtin_amdgcn_readlane(mm.bits, i);
+    const uint8_t *blk = p.k.pool + (((uint64_t)(uint32_t)__builtin_amdgcn_readlane(mm.hi, i) << 32) |
+                                     (uint32_t)__builtin_amdgcn_readlane(mm.lo, i));
     const uint32_t row_bytes = (uint32_t)(DL / 8) * b;
     uint32_t c[16];
 #pragma unroll
-    for (int i = 0; i < 16; i++) c[i] = 0;
-    const uint8_t *share = blk + key * row_bytes + e8 * (row_bytes / 8);
+    for (int x = 0; x < 16; x++) c[x] = 0;
+    const uint8_t *share = blk + (key * row_bytes + e8 * (row_bytes / 8));
     switch (b) {
     case 2: load_share<2>(c, share); break;
     case 3: load_share<3>(c, share); break;
     case 4: load_share<4>(c, share); break;
     default: load_share<8>(c, share); break;
     }
-    const uint32_t mm = *reinterpret_cast<const uint32_t *>(blk + 64 * row_bytes + 4 * (key * (DL / 64) + e8));
+    const uint32_t mw = *reinterpret_cast<const uint32_t *>(blk + (64 * row_bytes + 4 * (key * (DL / 64) + e8)));
     uint4 rr = {0, 0, 0, 0};
     if (R) rr = *reinterpret_cast<const uint4 *>(rope + ((size_t)a * rope_tokens + (size_t)kt * TILE + key) * R + 8 * e8);
 #pragma unroll
-    for (int i = 0; i < 16; i++) raw.c[i] = c[i];
+    for (int x = 0; x < 16; x++) raw.c[x] = c[x];
     raw.r[0] = rr.x; raw.r[1] = rr.y; raw.r[2] = rr.z; raw.r[3] = rr.w;
-    raw.m = mm;
+    raw.m = mw;
     raw.bits = b;
 }
 
@@ -193,12 +217,16 @@ __device__ __forceinline__ void tile_compute(MlaState<R> &w, const _Float16 *kh,
     constexpr int KR = MCfg<R>::KR, KS = MCfg<R>::KS;
     const int lane = threadIdx.x & 63, m = lane & 15, kq = lane >> 4;
     const int k0 = 16 * kg;
-    f4 st = {0.f, 0.f, 0.f, 0.f};
+    // two independent accumulator chains over the K-steps
+    f4 sa = {0.f, 0.f, 0.f, 0.f}, sb = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int s = 0; s < KS; s++) {
-        const h8 av = *reinterpret_cast<const h8 *>(kh + (k0 + m) * KR + 32 * s + 8 * kq);
-        st = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, w.qop[s], st, 0, 0, 0);
+    for (int s = 0; s < KS; s += 2) {
+        const h8 a0 = *reinterpret_cast<const h8 *>(kh + (k0 + m) * KR + 32 * s + 8 * kq);
+        const h8 a1 = *reinterpret_cast<const h8 *>(kh + (k0 + m) * KR + 32 * (s + 1) + 8 * kq);
+        sa = __builtin_amdgcn_mfma_f32_16x16x32_f16(a0, w.qop[s], sa, 0, 0, 0);
+        sb = __builtin_amdgcn_mfma_f32_16x16x32_f16(a1, w.qop[s + 1], sb, 0, 0, 0);
     }
+    f4 st = sa + sb;
     if (valid < TILE) {
 #pragma unroll
         for (int r = 0; r < 4; r++)
@@ -251,6 +279,11 @@ __global__ __launch_bounds__(512, 1) void mla_split(DecodeArgs p, const uint16_t
     const bool win = (s == nsb) && nw > 0;
     if (s > nsb || (s == nsb && !win)) return;
 
+    // the split's block table first, so its loads overlap the query loads
+    MlaMeta mm;
+    mm.base = -(1 << 20);
+    if (!win) mla_meta(mm, p, a, s * p.SB, min(s * p.SB + p.SB, nb));
+
     MlaState<R> w;
     const bool hv = m < p.Hq;
     const uint16_t *qrow = p.q + ((size_t)a * p.Hq + (hv ? m : 0)) * C::DK;
@@ -268,22 +301,23 @@ __global__ __launch_bounds__(512, 1) void mla_split(DecodeArgs p, const uint16_t
     if (!win) {
         // Tile j in buffer j&1; between barriers the tile j+1 is stored into
         // the other buffer (last read before the previous barrier).
-        const int j0 = s * p.SB, n = min(j0 + p.SB, nb) - j0;
-        MlaRaw raw;
-        load_block<R>(raw, p, rope, rope_tokens, a, j0);
+        const int j0 = s * p.SB, j1 = min(j0 + p.SB, nb), n = j1 - j0;
+        MlaRaw raw, raw1;
+        load_block<R>(raw, mm, p, rope, rope_tokens, a, j0, j1);
+        if (n > 1) load_block<R>(raw1, mm, p, rope, rope_tokens, a, j0 + 1, j1);
         store_raw<R>(raw, lds);
-        if (n > 1) load_block<R>(raw, p, rope, rope_tokens, a, j0 + 1);
+        if (n > 1) raw = raw1;
         __syncthreads();
         for (int j = 0; j < n; j++) {
             _Float16 *cur = lds + (j & 1) * C::BUF, *nxt = lds + ((j + 1) & 1) * C::BUF;
             if (dh && j + 1 < n) {
                 store_raw<R>(raw, nxt);
-                if (j + 2 < n) load_block<R>(raw, p, rope, rope_tokens, a, j0 + j + 2);
+                if (j + 2 < n) load_block<R>(raw, mm, p, rope, rope_tokens, a, j0 + j + 2, j1);
             }
             tile_compute<R>(w, cur, TILE, p.c, kg, dh);
             if (!dh && j + 1 < n) {
                 store_raw<R>(raw, nxt);
-                if (j + 2 < n) load_block<R>(raw, p, rope, rope_tokens, a, j0 + j + 2);
+                if (j + 2 < n) load_block<R>(raw, mm, p, rope, rope_tokens, a, j0 + j + 2, j1);
             }
             __syncthreads();
         }
