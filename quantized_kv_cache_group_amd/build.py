@@ -28,7 +28,7 @@ COMMON = [
     "-munsafe-fp-atomics",
 ]
 PER_FILE = {
-    "quantize.hip": ["-ffp-contract=off"],
+    "quantize.hip": ["-ffp-contract=off", "-fno-honor-nans", "-mno-amdgpu-ieee"],
 }
 SOURCES = ["kvq_api.cpp", "quantize.hip", "attend_generic.hip", "decode_gqa.hip", "decode_g4.hip", "chunk.hip",
            "mla.hip"]

@@ -10,11 +10,16 @@
 // scales and biases it writes are bit-for-bit the documented sequence of IEEE
 // binary32 operations (its two divisions are computed by sequences proven
 // equal to the correctly rounded quotient on every input they can receive).
+// It is also compiled with the IEEE mode bit off (-mno-amdgpu-ieee,
+// -fno-honor-nans): NaN and Inf inputs are a precondition violation, and for
+// finite operands min/max then need no canonicalising instruction.
 //
-// Layout of the work: one workgroup (256 lanes, 4 wave64s) per (block,
-// head, sequence).  A group of 64 bf16 values (128 contiguous bytes) belongs
-// to 8 lanes, 8 values (16 bytes) each, so a wave covers 8 groups per step and
-// its global loads are full 128-byte segments.  min/max use 3 xor-shuffles
+// Layout of the work: one workgroup (256 lanes, 4 wave64s) per (head,
+// block, sequence), heads fastest in the grid, so workgroups running side by
+// side read neighbouring slices of the same token rows.  A group of 64 bf16
+// values (128 contiguous bytes) belongs to 8 lanes, 8 values (16 bytes) each,
+// so a wave covers 8 groups per step and its global loads are full 128-byte
+// segments.  min/max use 3 DPP exchanges
 // inside each 8-lane slice.  Every lane loads all of its data before the
 // arithmetic, to keep several 16-byte loads in flight per lane.
 #include "kvq_internal.h"
@@ -34,6 +39,25 @@ __device__ __forceinline__ float f16_bits_to_f32(uint16_t b)
 {
     return (float)__builtin_bit_cast(_Float16, b);
 }
+
+// Lane exchanges inside 8-lane slices through DPP, which the compiler fuses
+// into the consuming min/max: xor 1 and xor 2 are quad permutations; once a
+// quad holds one value, the half-row mirror (lane i <- lane 7-i) brings the
+// other quad's.
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v)
+{
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u(uint32_t v)
+{
+    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, false);
+}
+constexpr int DPP_XOR1 = 0xB1;                  // quad_perm [1,0,3,2]
+constexpr int DPP_XOR2 = 0x4E;                  // quad_perm [2,3,0,1]
+constexpr int DPP_NEXT = 0xF9;                  // quad_perm [1,2,3,3]: lane j <- j+1 (j < 3)
+constexpr int DPP_HALF_MIRROR = 0x141;          // row_half_mirror
 
 // bf16 round to nearest even of a finite fp32 value.
 __device__ __forceinline__ uint32_t f32_to_bf16_bits(float f)
@@ -90,11 +114,12 @@ __device__ __forceinline__ void quant_block(const uint16_t *__restrict__ src_blk
         float mn = x[0], mx = x[0];
 #pragma unroll
         for (int i = 1; i < 8; i++) { mn = fminf(mn, x[i]); mx = fmaxf(mx, x[i]); }
-#pragma unroll
-        for (int o = 1; o < 8; o <<= 1) {
-            mn = fminf(mn, __shfl_xor(mn, o));
-            mx = fmaxf(mx, __shfl_xor(mx, o));
-        }
+        mn = fminf(mn, dpp_f<DPP_XOR1>(mn));
+        mx = fmaxf(mx, dpp_f<DPP_XOR1>(mx));
+        mn = fminf(mn, dpp_f<DPP_XOR2>(mn));
+        mx = fmaxf(mx, dpp_f<DPP_XOR2>(mx));
+        mn = fminf(mn, dpp_f<DPP_HALF_MIRROR>(mn));
+        mx = fmaxf(mx, dpp_f<DPP_HALF_MIRROR>(mx));
         mn = mn + 0.0f;                             // a zero extreme is +0
         mx = mx + 0.0f;
         // s = (mx - mn) / N, correctly rounded: reciprocal multiply plus one
@@ -141,11 +166,11 @@ __device__ __forceinline__ void quant_block(const uint16_t *__restrict__ src_blk
             reinterpret_cast<uint2 *>(gc)[sub] = make_uint2((uint32_t)v, (uint32_t)(v >> 32));
         } else if constexpr (B == 2) {
             uint32_t mine = (uint32_t)v;            // 16 bits
-            uint32_t other = __shfl_xor(mine, 1);
+            uint32_t other = dpp_u<DPP_XOR1>(mine);
             if ((sub & 1) == 0) reinterpret_cast<uint32_t *>(gc)[sub >> 1] = mine | (other << 16);
         } else {                                    // B == 3: 24 bits, 4 lanes -> 3 words
             uint32_t mine = (uint32_t)v;
-            uint32_t next = __shfl(mine, (lane + 1) & 63);
+            uint32_t next = dpp_u<DPP_NEXT>(mine);  // lane j+1 of the same quad
             int j = sub & 3;
             if (j < 3) {
                 uint32_t w = (mine >> (8 * j)) | (next << (24 - 8 * j));
@@ -160,7 +185,7 @@ __device__ __forceinline__ void quant_block(const uint16_t *__restrict__ src_blk
 template <int NG>
 __global__ __launch_bounds__(256) void quantize_kernel(QuantArgs a)
 {
-    const int j = blockIdx.x, h = blockIdx.y, s = blockIdx.z;
+    const int h = blockIdx.x, j = blockIdx.y, s = blockIdx.z;
     if (j >= seq_blocks(a.t, s)) return;
     const int b = a.t.bits[(size_t)s * a.t.max_blocks + j];
     uint8_t *blk = a.pool + a.offset[(size_t)s * a.t.max_blocks + j];
@@ -287,7 +312,7 @@ __global__ __launch_bounds__(256) void dequantize_kernel(DequantArgs a)
 hipError_t launch_quantize(const QuantArgs &a, hipStream_t s)
 {
     if (a.t.max_blocks == 0) return hipSuccess;
-    dim3 grid(a.t.max_blocks, a.t.H, a.t.A);
+    dim3 grid(a.t.H, a.t.max_blocks, a.t.A);
     switch (a.t.D / 64) {
     case 1: quantize_kernel<1><<<grid, 256, 0, s>>>(a); break;
     case 2: quantize_kernel<2><<<grid, 256, 0, s>>>(a); break;
