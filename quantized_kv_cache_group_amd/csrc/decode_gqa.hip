@@ -399,9 +399,11 @@ __global__ __launch_bounds__(64) void decode_gqa_split(DecodeArgs p)
 }
 
 // Combine the splits of one (sequence, query head): max-rescaled sums in the
-// log2 domain of the split kernel.  One wave per row: lanes first reduce the
-// split maxima and sums, keep the split weights in LDS, then stream the
-// partial outputs of a 64-dim slice (grid.y) with independent loads.
+// log2 domain of the split kernel.  One wave per row and 64-dim slice
+// (grid.y).  Up to 64 splits, lane s reads split s's (max, sum) and every
+// lane reads its dim of all the partial outputs, all before the first use,
+// so the row costs one memory round trip; longer rows keep the split weights
+// in LDS and stream the partials.
 constexpr int MERGE_ROWS = 4;
 constexpr int MAX_SPLITS = 512;
 
@@ -417,6 +419,43 @@ __global__ __launch_bounds__(64 * MERGE_ROWS) void decode_gqa_merge(DecodeArgs p
     const int ns = (nb + p.SB - 1) / p.SB + (nw > 0 ? 1 : 0);
     const size_t stride = (size_t)(D + 2);
     const float *pr = p.part + (size_t)row * p.n_splits * stride;
+    float *o = p.out + (size_t)row * D;
+    const int d = 64 * blockIdx.y + lane;
+    if (ns <= 64) {
+        if (ns == 0) {
+            if (d < D) o[d] = 0.0f;
+            return;
+        }
+        const int sl = min(lane, ns - 1), dd = min(d, D - 1);
+        const float mv = pr[sl * stride], lv = pr[sl * stride + 1];
+        float v[64];
+#pragma unroll
+        for (int c = 0; c < 4; c++) {
+            if (16 * c < ns) {
+#pragma unroll
+                for (int u = 0; u < 16; u++) v[16 * c + u] = pr[min(16 * c + u, ns - 1) * stride + 2 + dd];
+            }
+        }
+        float M = lane < ns ? mv : -INFINITY;
+#pragma unroll
+        for (int x = 32; x > 0; x >>= 1) M = fmaxf(M, __shfl_xor(M, x));
+        const float w = (lane < ns && M > -INFINITY) ? __builtin_amdgcn_exp2f(mv - M) : 0.0f;
+        float L = w * lv;
+#pragma unroll
+        for (int x = 32; x > 0; x >>= 1) L += __shfl_xor(L, x);
+        float ax = 0.0f;
+#pragma unroll
+        for (int c = 0; c < 4; c++) {
+            if (16 * c < ns) {
+#pragma unroll
+                for (int u = 0; u < 16; u++)
+                    ax = __builtin_fmaf(__builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, w), 16 * c + u)),
+                                        v[16 * c + u], ax);
+            }
+        }
+        if (d < D) o[d] = L > 0.0f ? ax * (1.0f / L) : 0.0f;
+        return;
+    }
     float M = -INFINITY;
     for (int s = lane; s < ns; s += 64) M = fmaxf(M, pr[s * stride]);
 #pragma unroll
@@ -432,9 +471,6 @@ __global__ __launch_bounds__(64 * MERGE_ROWS) void decode_gqa_merge(DecodeArgs p
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     const float inv = L > 0.0f ? 1.0f / L : 0.0f;
-    float *o = p.out + (size_t)row * D;
-    // grid.y splits the dims into 64-wide slices (one dim per lane)
-    const int d = 64 * blockIdx.y + lane;
     if (d < D) {
         float ax = 0.0f;
         int s = 0;
