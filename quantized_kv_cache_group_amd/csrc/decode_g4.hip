@@ -288,32 +288,22 @@ __device__ __forceinline__ f2 meta_of(uint32_t packed)
     return f2{(float)sb[0], (float)sb[1]};
 }
 
+// A 64-token block in three phases: the Q.K products (width-specific
+// unpack of the lane's K row), the scores and the online softmax, then P.V
+// (width-specific unpack of the V row).
 template <int B, int NG>
-__device__ __forceinline__ void round_block(State<NG> &st, const h4 (*qs)[4], const float (&qg)[NG],
-                                            const uint8_t *kblk, const uint8_t *vblk, int H, int g, float c,
-                                            _Float16 *vr)
+__device__ __forceinline__ void dots_phase(f4 (&T)[NG], const h4 (*qs)[4], const uint32_t *kw)
 {
-    constexpr uint32_t CODE_ROW = 8 * NG * B;
-    constexpr int NDW = FullRow<B, NG>::NDW;
-#ifndef KVQ_G4_VLATE_NG
-#define KVQ_G4_VLATE_NG 2
-#endif
-    constexpr bool V_LATE = NG >= KVQ_G4_VLATE_NG;
-    const uint32_t row = (uint32_t)g * 64 + threadIdx.x;
-    const uint32_t moff = (uint32_t)H * 64 * CODE_ROW + 4 * NG * row;
-    uint32_t kw[NDW], vw[NDW], km[NG], vm[NG];
-    FullRow<B, NG>::load(kw, kblk + row * CODE_ROW);
-#pragma unroll
-    for (int i = 0; i < NG; i++) km[i] = reinterpret_cast<const uint32_t *>(kblk + moff)[i];
-    if constexpr (!V_LATE) FullRow<B, NG>::load(vw, vblk + row * CODE_ROW);
     const uint32_t mv = opaque_magic();
-    f4 T[NG];
     group_dots<NG>(T, qs, [&](int cidx) { return FullRow<B, NG>::chunk(kw, cidx, mv); });
-    // wide rows: the V row is fetched once the K row's registers are free
-    if constexpr (V_LATE) FullRow<B, NG>::load(vw, vblk + row * CODE_ROW);
-#pragma unroll
-    for (int i = 0; i < NG; i++) vm[i] = reinterpret_cast<const uint32_t *>(vblk + moff)[i];
-    // scores: sum_g s (T - 1024 Q_g) + b Q_g, with token 4b+r's (s, b)
+}
+
+// scores: sum_g s (T - 1024 Q_g) + b Q_g, with token 4b+r's (s, b) from km;
+// returns P' = fp16(p s_v) per group and adds the bias and P' sums.
+template <int NG>
+__device__ __forceinline__ void score_phase(State<NG> &st, h4 (&pg)[NG], const f4 (&T)[NG], const uint32_t *km,
+                                            const uint32_t *vm, const float (&qg)[NG], float c)
+{
     f4 s = {0.f, 0.f, 0.f, 0.f};
     f2 vsb[NG][4];
 #pragma unroll
@@ -327,8 +317,6 @@ __device__ __forceinline__ void round_block(State<NG> &st, const h4 (*qs)[4], co
         }
     }
     const h4 p = softmax_round<NG>(st, s, 64, c);
-    // P' of each group and the bias term
-    h4 pg[NG];
     const f4 pf = {(float)p[0], (float)p[1], (float)p[2], (float)p[3]};
 #pragma unroll
     for (int gg = 0; gg < NG; gg++) {
@@ -338,8 +326,41 @@ __device__ __forceinline__ void round_block(State<NG> &st, const h4 (*qs)[4], co
         st.pb_lane[gg] += __builtin_fmaf(pf[0], vsb[gg][0][1], pf[1] * vsb[gg][1][1]) +
                           __builtin_fmaf(pf[2], vsb[gg][2][1], pf[3] * vsb[gg][3][1]);
     }
+}
+
+template <int B, int NG>
+__device__ __forceinline__ void pv_phase(State<NG> &st, const h4 (&pg)[NG], const uint32_t *vw, _Float16 *vr)
+{
+    const uint32_t mv = opaque_magic();
     pv_round<NG>(st, [&](int hh) { return pg[hh]; }, vr,
                  [&](int cidx) { return FullRow<B, NG>::chunk(vw, cidx, mv); });
+}
+
+// The V row is fetched once the K row's registers are free (a scheduling
+// barrier keeps its loads after the K row's last use), so a row's two
+// halves are never live together.
+template <int B, int NG>
+__device__ __forceinline__ void round_block(State<NG> &st, const h4 (*qs)[4], const float (&qg)[NG],
+                                            const uint8_t *kblk, const uint8_t *vblk, int H, int g, float c,
+                                            _Float16 *vr)
+{
+    constexpr uint32_t CODE_ROW = 8 * NG * B;
+    const uint32_t row = (uint32_t)g * 64 + threadIdx.x;
+    const uint32_t moff = (uint32_t)H * 64 * CODE_ROW + 4 * NG * row;
+    uint32_t kw[FullRow<B, NG>::NDW], km[NG], vm[NG];
+    FullRow<B, NG>::load(kw, kblk + row * CODE_ROW);
+#pragma unroll
+    for (int i = 0; i < NG; i++) km[i] = reinterpret_cast<const uint32_t *>(kblk + moff)[i];
+    f4 T[NG];
+    dots_phase<B, NG>(T, qs, kw);
+    __builtin_amdgcn_sched_barrier(0);
+    uint32_t vw[FullRow<B, NG>::NDW];
+    FullRow<B, NG>::load(vw, vblk + row * CODE_ROW);
+#pragma unroll
+    for (int i = 0; i < NG; i++) vm[i] = reinterpret_cast<const uint32_t *>(vblk + moff)[i];
+    h4 pg[NG];
+    score_phase<NG>(st, pg, T, km, vm, qg, c);
+    pv_phase<B, NG>(st, pg, vw, vr);
 }
 
 // 64 window tokens w0 .. w0+63 (rows past nw read row nw-1 and are masked):
@@ -363,7 +384,7 @@ __device__ __forceinline__ void round_window(State<NG> &st, const h4 (*qs)[4], c
 }
 
 template <int NG>
-__global__ __launch_bounds__(64) void decode_g4_split(DecodeArgs p)
+__global__ __launch_bounds__(64, (NG <= 2 ? 3 : 2)) void decode_g4_split(DecodeArgs p)
 {
     constexpr int D = 64 * NG, NCH = 8 * NG;
     __shared__ __attribute__((aligned(16))) h4 qs[2 * NCH][4];      // [slice][head], permuted dims
