@@ -268,7 +268,7 @@ def main():
         cs = [kvq.LayerCache(H, D, w.n_blocks, w.n_window, bits, latent=latent, rope_dim=w.rope_dim)
               for bits in caches_per_layer]
         sets.append(cs)
-    n_src = 2 if len(layers) == 1 else 1
+    n_src = 3 if len(layers) == 1 else 1            # >= 2 x 256 MB between reads of one source
     srcs = [[gpu_inputs(w, torch, 1000 * r + li) for li in range(len(layers))] for r in range(n_src)]
     gq = torch.Generator(device="cuda")
     gq.manual_seed(7)

@@ -109,6 +109,43 @@ uint64_t kvq_block_bytes(int32_t bits, int32_t n_heads, int32_t head_dim);
 int kvq_quantize(const kvq_layout *L, const kvq_store *dst, const uint16_t *src,
                  int64_t src_seq_tokens, void *stream);
 
+/* Quantize on append, the window roll (CoMixKV, Abstract: a width is chosen
+ * only for newly quantized blocks and the most recent states stay in native
+ * precision; AgentMem, Abstract: each agent's cache keeps growing as the agent
+ * works).  For every sequence a, with nb = n_blocks[a] and W = n_window[a],
+ * the token stream
+ *     T = window[a][0 .. W) ++ new[a][0 .. n_new)
+ * is cut into k = (W + n_new - keep_recent) / 64 new blocks (integer
+ * division; none when W + n_new <= keep_recent), T[64i .. 64i+63] becoming
+ * block nb + i at width bits[a][nb+i] and pool offset offset[a][nb+i] (table
+ * entries the caller fills beforehand), and a window holding the remaining
+ * W + n_new - 64k tokens T[64k ..] (keep_recent .. keep_recent+63 of them
+ * once a block has been cut).  Then n_blocks_out[a] = nb + k and
+ * n_window_out[a] = W + n_new - 64k.  Block payloads are bit-exact to
+ * kvq_quantize of the same rows; window rows are copied unchanged.
+ *   k_new, v_new  bf16 [A][n_new][H][D], 16-byte aligned; V NULL for a latent
+ *                 cache (K only; v_new ignored).
+ *   rope          NULL, or bf16 [A][64*max_blocks + window_cap][H][rope_dim]
+ *                 (rope_dim 64): raw key dims, one row per token position as
+ *                 kvq_attend_decode reads them (token t of sequence a at row
+ *                 t), so the roll moves none of them: new token i is written
+ *                 at row 64*nb + W + i from rope_new bf16 [A][n_new][H][rope_dim].
+ *   n_blocks_out, n_window_out  device int32 [A]; they may be L->n_blocks and
+ *                 L->n_window (written after every read); n_window_out may
+ *                 be NULL when window_cap == 0.
+ *   keep_recent   >= 0 with keep_recent + 63 <= window_cap, so the window
+ *                 always fits; with window_cap == 0, keep_recent must be 0
+ *                 and n_new a multiple of 64.
+ * Device preconditions: nb + k <= max_blocks and W <= window_cap.  Blocks past
+ * max_blocks and window rows past window_cap are never written.
+ * Errors: KVQ_EINVAL, KVQ_EUNSUPPORTED (rope_dim other than 0 or 64),
+ *         KVQ_EHIP. */
+int kvq_append(const kvq_layout *L, const kvq_store *K, const kvq_store *V,
+               const uint16_t *k_new, const uint16_t *v_new,
+               uint16_t *rope, const uint16_t *rope_new, int32_t rope_dim,
+               int32_t n_new, int32_t keep_recent,
+               int32_t *n_blocks_out, int32_t *n_window_out, void *stream);
+
 /* Restore (QKVShare injection path: rebuild 16-bit key/value rows).  For
  * every sequence a write dst[a][t][H][D] for t < 64*n_blocks[a] + n_window[a]:
  * dequantized blocks first (fma(code, scale, bias) in fp32, then rounded to
@@ -137,7 +174,9 @@ int kvq_decode_workspace(const kvq_layout *L, int32_t n_q_heads, int32_t rope_di
  *   V    NULL for latent attention: the values are the restored K rows (the
  *        first D dims of each key), as in a multi-head latent cache.
  *   rope NULL or bf16 [A][64*max_blocks + window_cap][H][rope_dim]: raw key
- *        dims appended after the D quantized ones (rope_dim 0 or 64).
+ *        dims appended after the D quantized ones (rope_dim 0 or 64), one row
+ *        per token position (token t of sequence a, blocks then window, at
+ *        row t).
  *   n_q_heads: a multiple of H with n_q_heads/H <= 16.
  *   workspace: >= kvq_decode_workspace bytes, 256-byte aligned.
  * Errors: KVQ_EINVAL, KVQ_ENOSPC, KVQ_EUNSUPPORTED, KVQ_EHIP. */

@@ -78,6 +78,9 @@ def lib() -> ctypes.CDLL:
         L.kvq_ref_attend_chunk_seq.argtypes = [P, P, P, P, i32, P, P, i32, i32, i32, P, P, P,
                                                i32, i32, f32, i32, i32, P]
         L.kvq_ref_attend_chunk_seq.restype = i32
+        L.kvq_ref_append_seq.argtypes = [P, P, P, P, P, i32, i32, P, P, i32, i32, i32, i32, P, P, i32,
+                                         i32, P, P, i32, P, P]
+        L.kvq_ref_append_seq.restype = i32
         L.kvq_ref_max_threads.argtypes = []
         L.kvq_ref_max_threads.restype = i32
         _lib = L
@@ -259,6 +262,38 @@ def attend_chunk_seq(pool, bits, k_offset, v_offset, k_window, v_window, n_kv_he
     if rc:
         raise ValueError("kvq_ref_attend_chunk_seq failed")
     return out
+
+
+def append_seq(k_pool, v_pool, bits, k_offset, v_offset, n_blocks, k_window, v_window, n_window,
+               n_heads, head_dim, k_new, v_new, keep, rope=None, rope_new=None):
+    """Window roll of one sequence, in place.  ``bits``/``*_offset`` are the
+    sequence's full table rows [max_blocks]; ``k_window``/``v_window`` uint16
+    [window_cap][H][D]; ``rope`` uint16 [64*max_blocks + window_cap][H][R].
+    Returns the new (n_blocks, n_window)."""
+    bits = _c(bits, np.uint8)
+    k_offset = _c(k_offset, np.uint64)
+    v_offset = _c(v_offset, np.uint64)
+    for a in (k_pool, v_pool, k_window, v_window, rope):
+        assert a is None or a.flags.c_contiguous
+    max_blocks = bits.size
+    window_cap = 0 if k_window is None else k_window.size // (n_heads * head_dim)
+    k_new = _c(k_new, np.uint16)
+    v_new = _c(v_new, np.uint16)
+    rope_new = _c(rope_new, np.uint16)
+    n_new = 0 if k_new is None else k_new.size // (n_heads * head_dim)
+    rope_dim = 0
+    if rope is not None:
+        rope_dim = rope.size // ((64 * max_blocks + window_cap) * n_heads)
+    nb_out = ctypes.c_int(0)
+    nw_out = ctypes.c_int(0)
+    rc = lib().kvq_ref_append_seq(_p(k_pool), _p(v_pool), _p(bits), _p(k_offset), _p(v_offset),
+                                  max_blocks, int(n_blocks), _p(k_window), _p(v_window), window_cap,
+                                  int(n_window), n_heads, head_dim, _p(k_new), _p(v_new), n_new,
+                                  int(keep), _p(rope), _p(rope_new), rope_dim, ctypes.byref(nb_out),
+                                  ctypes.byref(nw_out))
+    if rc:
+        raise ValueError("kvq_ref_append_seq: result does not fit or bad arguments")
+    return nb_out.value, nw_out.value
 
 
 def max_threads() -> int:

@@ -278,6 +278,56 @@ int kvq_ref_quantize_seq(const uint16_t *x, int n_heads, int head_dim, int n_blo
     return 0;
 }
 
+/* Rows [0, n) of the stream window[0 .. n_window) ++ x_new[0 .. n_new) of
+ * row width w (elements) into dst [n][w]. */
+static void stream_rows(uint16_t *dst, const uint16_t *window, int n_window, const uint16_t *x_new,
+                        int n, size_t w)
+{
+    for (int t = 0; t < n; t++) {
+        const uint16_t *src = t < n_window ? window + (size_t)t * w : x_new + (size_t)(t - n_window) * w;
+        memcpy(dst + (size_t)t * w, src, w * sizeof(uint16_t));
+    }
+}
+
+int kvq_ref_append_seq(uint8_t *k_pool, uint8_t *v_pool, const uint8_t *bits,
+                       const uint64_t *k_offset, const uint64_t *v_offset,
+                       int max_blocks, int n_blocks, uint16_t *k_window, uint16_t *v_window,
+                       int window_cap, int n_window, int n_heads, int head_dim,
+                       const uint16_t *k_new, const uint16_t *v_new, int n_new, int keep,
+                       uint16_t *rope, const uint16_t *rope_new, int rope_dim,
+                       int *n_blocks_out, int *n_window_out)
+{
+    if (!dims_ok(n_heads, head_dim) || n_new < 0 || keep < 0 || n_window < 0 || n_blocks < 0) return -1;
+    const int total = n_window + n_new;                    /* stream length */
+    const int k = total > keep ? (total - keep) / 64 : 0;   /* new blocks */
+    const int rest = total - 64 * k;                        /* new window */
+    if (n_blocks + k > max_blocks || rest > window_cap) return -1;
+    for (int i = 0; i < k; i++)
+        if (!width_ok(bits[n_blocks + i])) return -1;
+    const size_t w = (size_t)n_heads * head_dim, wr = (size_t)n_heads * rope_dim;
+    const int n_kv = v_pool ? 2 : 1;
+    for (int kv = 0; kv < n_kv; kv++) {
+        uint8_t *pool = kv ? v_pool : k_pool;
+        uint16_t *window = kv ? v_window : k_window;
+        const uint64_t *offset = kv ? v_offset : k_offset;
+        uint16_t *T = malloc(((size_t)total + 1) * w * sizeof(uint16_t));
+        if (!T) return -1;
+        stream_rows(T, window, n_window, kv ? v_new : k_new, total, w);
+        /* the first 64k rows become blocks n_blocks .. n_blocks+k-1 */
+        kvq_ref_quantize_seq(T, n_heads, head_dim, k, bits + n_blocks, offset + n_blocks, pool);
+        /* the rest becomes the window */
+        if (rest > 0) memcpy(window, T + (size_t)64 * k * w, (size_t)rest * w * sizeof(uint16_t));
+        free(T);
+    }
+    if (rope_dim > 0) {
+        /* rows are token positions: new token i is position 64*n_blocks + n_window + i */
+        memcpy(rope + ((size_t)64 * n_blocks + n_window) * wr, rope_new, (size_t)n_new * wr * sizeof(uint16_t));
+    }
+    *n_blocks_out = n_blocks + k;
+    *n_window_out = rest;
+    return 0;
+}
+
 int kvq_ref_restore_seq(const uint8_t *pool, const uint8_t *bits, const uint64_t *offset,
                         int n_blocks, const uint16_t *window, int n_window,
                         int n_heads, int head_dim, float *out)

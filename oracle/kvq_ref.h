@@ -86,6 +86,28 @@ uint64_t kvq_ref_block_bytes(int bits, int n_heads, int head_dim);
 int kvq_ref_quantize_seq(const uint16_t *x, int n_heads, int head_dim, int n_blocks,
                          const uint8_t *bits, const uint64_t *offset, uint8_t *pool);
 
+/* Append n_new tokens to one sequence, the window roll (Coordinated
+ * Mixed-Precision KV Cache Quantization, arXiv 2611.10096, Abstract: widths
+ * are chosen only for newly quantized blocks and recent states stay in native
+ * precision).  The stream T = window[0 .. n_window) ++ x_new[0 .. n_new) is
+ * cut into k = (n_window + n_new - keep) / 64 new blocks (none when
+ * n_window + n_new <= keep): block n_blocks + i receives T[64i .. 64i+63] at
+ * width bits[n_blocks + i], at pool + offset[n_blocks + i]; the window then
+ * holds T[64k ..].  v_pool NULL: a latent cache (K only).  With rope_dim > 0,
+ * rope [64*max_blocks + window_cap][H][rope_dim] holds one row per token
+ * position (as the decode reads it), so only the new tokens' rows are written:
+ * new token i at row 64*n_blocks + n_window + i, from rope_new
+ * [n_new][H][rope_dim].  Writes the new counts.
+ * Returns 0, or -1 when the result would not fit max_blocks or window_cap
+ * (nothing is written then). */
+int kvq_ref_append_seq(uint8_t *k_pool, uint8_t *v_pool, const uint8_t *bits,
+                       const uint64_t *k_offset, const uint64_t *v_offset,
+                       int max_blocks, int n_blocks, uint16_t *k_window, uint16_t *v_window,
+                       int window_cap, int n_window, int n_heads, int head_dim,
+                       const uint16_t *k_new, const uint16_t *v_new, int n_new, int keep,
+                       uint16_t *rope, const uint16_t *rope_new, int rope_dim,
+                       int *n_blocks_out, int *n_window_out);
+
 /* Restore one sequence to fp32 rows out [64*n_blocks + n_window][H][D]:
  * dequantized blocks first, then the bf16 window. */
 int kvq_ref_restore_seq(const uint8_t *pool, const uint8_t *bits, const uint64_t *offset,

@@ -24,7 +24,7 @@ KVQ_OK, KVQ_EINVAL, KVQ_ENOSPC, KVQ_EUNSUPPORTED, KVQ_EHIP = 0, -1, -2, -3, -4
 OUT_BF16, OUT_F32 = 0, 1
 WIDTHS = (2, 3, 4, 8)
 
-SYMBOLS = ("kvq_block_bytes", "kvq_quantize", "kvq_dequantize", "kvq_decode_workspace",
+SYMBOLS = ("kvq_block_bytes", "kvq_quantize", "kvq_append", "kvq_dequantize", "kvq_decode_workspace",
            "kvq_attend_decode", "kvq_chunk_workspace", "kvq_attend_chunk", "kvq_strerror")
 
 
@@ -62,6 +62,8 @@ def lib() -> ctypes.CDLL:
         L.kvq_block_bytes.restype = ctypes.c_uint64
         L.kvq_quantize.argtypes = [P, P, P, ctypes.c_int64, P]
         L.kvq_quantize.restype = ctypes.c_int
+        L.kvq_append.argtypes = [P, P, P, P, P, P, P, i32, i32, i32, P, P, P]
+        L.kvq_append.restype = ctypes.c_int
         L.kvq_dequantize.argtypes = [P, P, i32, P, ctypes.c_int64, P]
         L.kvq_dequantize.restype = ctypes.c_int
         L.kvq_decode_workspace.argtypes = [P, i32, i32, ctypes.POINTER(sz)]
@@ -116,12 +118,14 @@ class LayerCache:
     back (256-byte aligned) plus a bf16 window buffer.  ``latent=True`` keeps
     only K (values are the K latent) and an optional bf16 rope buffer.
     All tensors live on ``device``; the block offsets are computed on the host
-    from kvq_block_bytes.
+    from kvq_block_bytes.  ``future_bits`` (an int, or per sequence the widths
+    of blocks n_blocks[a] .. max_blocks-1) reserves pool slots, placed after
+    every existing block, for blocks that ``append`` will create.
     """
 
     def __init__(self, n_heads: int, head_dim: int, n_blocks, n_window=None, bits=None,
                  max_blocks: int | None = None, window_cap: int | None = None,
-                 latent: bool = False, rope_dim: int = 0, device="cuda"):
+                 latent: bool = False, rope_dim: int = 0, device="cuda", future_bits=None):
         A = len(n_blocks)
         self.A, self.H, self.D = A, int(n_heads), int(head_dim)
         self.n_blocks_host = [int(v) for v in n_blocks]
@@ -134,16 +138,25 @@ class LayerCache:
             b = np.full(self.n_blocks_host[a], 4, np.uint8) if bits is None else np.asarray(bits[a], np.uint8)
             assert b.size == self.n_blocks_host[a]
             bits_tab[a, : b.size] = b
+        if future_bits is not None:
+            for a in range(A):
+                rest = self.max_blocks - self.n_blocks_host[a]
+                fb = np.full(rest, future_bits, np.uint8) if np.isscalar(future_bits) \
+                    else np.asarray(future_bits[a], np.uint8)
+                assert fb.size == rest
+                bits_tab[a, self.n_blocks_host[a]:self.max_blocks] = fb
         self.bits_host = bits_tab
         off = np.zeros_like(bits_tab, dtype=np.uint64)
         pos = 0
-        for a in range(A):
-            for j in range(self.n_blocks_host[a]):
-                off[a, j] = pos
-                nb = block_bytes(int(bits_tab[a, j]), self.H, self.D)
-                if nb == 0:
-                    raise ValueError("unsupported width or head_dim")
-                pos += _round_up(nb, 256)
+        slots = [[(a, j) for j in range(self.n_blocks_host[a])] for a in range(A)]
+        if future_bits is not None:
+            slots.append([(a, j) for a in range(A) for j in range(self.n_blocks_host[a], self.max_blocks)])
+        for a, j in (s for group in slots for s in group):
+            off[a, j] = pos
+            nb = block_bytes(int(bits_tab[a, j]), self.H, self.D)
+            if nb == 0:
+                raise ValueError("unsupported width or head_dim")
+            pos += _round_up(nb, 256)
         self.offset_host = off
         self.pool_bytes = max(pos, 256)
         dev = torch.device(device)
@@ -187,6 +200,35 @@ class LayerCache:
         st = self.store(which)
         _check(lib().kvq_quantize(ctypes.byref(self._layout), ctypes.byref(st), _ptr(src),
                                   src.shape[1], _stream(stream)), "kvq_quantize")
+
+    def append(self, k_new: torch.Tensor, v_new: torch.Tensor | None = None, keep_recent: int = 128,
+               rope_new: torch.Tensor | None = None, stream=None):
+        """Append k_new/v_new bf16 [A][n][H][D] (rope_new [A][n][H][rope_dim])
+        to the windows; every full 64-token block beyond the keep_recent newest
+        tokens is quantized into the next block slot (its width and offset are
+        the table entries set at construction).  Updates the device counts in
+        place and the host mirrors by the same rule."""
+        n = int(k_new.shape[1])
+        for t in (k_new, v_new, rope_new):
+            if t is not None:
+                assert t.dtype == torch.bfloat16 and t.is_contiguous() and t.shape[0] == self.A
+                assert t.shape[1] == n
+        if not self.latent:
+            assert v_new is not None
+        kst, vst = self.store("k"), self.store("v")
+        _check(lib().kvq_append(ctypes.byref(self._layout), ctypes.byref(kst),
+                                None if vst is None else ctypes.byref(vst), _ptr(k_new),
+                                _ptr(v_new if not self.latent else None), _ptr(self.rope),
+                                _ptr(rope_new), self.rope_dim, n, int(keep_recent),
+                                _ptr(self.n_blocks), _ptr(self.n_window), _stream(stream)),
+               "kvq_append")
+        for a in range(self.A):
+            nb, w = self.n_blocks_host[a], self.n_window_host[a]
+            total = w + n
+            k = (total - keep_recent) // 64 if total > keep_recent else 0
+            k = min(k, self.max_blocks - nb)
+            self.n_blocks_host[a] = nb + k
+            self.n_window_host[a] = min(total - 64 * k, self.window_cap)
 
     def dequantize(self, which: str, out: torch.Tensor, stream=None):
         """Restore into out [A][S][H][D] (bf16 or fp32), S >= 64*max_blocks + window_cap."""

@@ -167,6 +167,55 @@ int kvq_quantize(const kvq_layout *L, const kvq_store *dst, const uint16_t *src,
     return hip_status(launch_quantize(a, static_cast<hipStream_t>(stream)));
 }
 
+int kvq_append(const kvq_layout *L, const kvq_store *K, const kvq_store *V,
+               const uint16_t *k_new, const uint16_t *v_new,
+               uint16_t *rope, const uint16_t *rope_new, int32_t rope_dim,
+               int32_t n_new, int32_t keep_recent,
+               int32_t *n_blocks_out, int32_t *n_window_out, void *stream)
+{
+    int st = check_layout(L);
+    if (st) return st;
+    if ((st = check_store(L, K))) return st;
+    if (V && (st = check_store(L, V))) return st;
+    if (n_new < 0 || keep_recent < 0) return KVQ_EINVAL;
+    if (n_new > 0) {
+        if (!k_new || !aligned(k_new, 16)) return KVQ_EINVAL;
+        if (V && (!v_new || !aligned(v_new, 16))) return KVQ_EINVAL;
+    }
+    if (rope_dim != 0 && rope_dim != 64) return KVQ_EUNSUPPORTED;
+    if (rope_dim) {
+        if (!rope || !aligned(rope, 16)) return KVQ_EINVAL;
+        if (n_new > 0 && (!rope_new || !aligned(rope_new, 16))) return KVQ_EINVAL;
+    }
+    if (L->window_cap > 0) {
+        if ((int64_t)keep_recent + 63 > L->window_cap) return KVQ_EINVAL;
+        if (!n_window_out || !aligned(n_window_out, 4)) return KVQ_EINVAL;
+    } else if (keep_recent != 0 || n_new % 64 != 0) {
+        return KVQ_EINVAL;
+    }
+    if (!n_blocks_out || !aligned(n_blocks_out, 4)) return KVQ_EINVAL;
+    // a stream of window + new tokens is indexed in int32
+    if ((int64_t)L->window_cap + n_new > (int64_t)1 << 30) return KVQ_EUNSUPPORTED;
+    AppendArgs a;
+    a.t = tables(L);
+    a.k_offset = K->offset;
+    a.v_offset = V ? V->offset : nullptr;
+    a.k_pool = K->pool;
+    a.v_pool = V ? V->pool : nullptr;
+    a.k_window = L->window_cap > 0 ? K->window : nullptr;
+    a.v_window = (V && L->window_cap > 0) ? V->window : nullptr;
+    a.k_new = k_new;
+    a.v_new = V ? v_new : nullptr;
+    a.rope = rope_dim ? rope : nullptr;
+    a.rope_new = rope_dim ? rope_new : nullptr;
+    a.rope_dim = rope_dim;
+    a.n_new = n_new;
+    a.keep = keep_recent;
+    a.n_blocks_out = n_blocks_out;
+    a.n_window_out = L->window_cap > 0 ? n_window_out : nullptr;
+    return hip_status(launch_append(a, static_cast<hipStream_t>(stream)));
+}
+
 int kvq_dequantize(const kvq_layout *L, const kvq_store *src, int32_t out_dtype, void *dst,
                    int64_t dst_seq_tokens, void *stream)
 {

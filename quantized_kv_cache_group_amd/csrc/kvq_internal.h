@@ -92,8 +92,24 @@ struct ChunkArgs {
     float *out;                 // [A][n_new][Hq][D]
 };
 
+// Append new tokens to the windows, quantizing every full 64-token block
+// that leaves the kept recent window.
+struct AppendArgs {
+    Tables t;
+    const uint64_t *k_offset, *v_offset;  // v_offset null: latent cache (K only)
+    uint8_t *k_pool, *v_pool;
+    uint16_t *k_window, *v_window;
+    const uint16_t *k_new, *v_new;      // [A][n_new][H][D]
+    uint16_t *rope;                     // [A][64*max_blocks + window_cap][H][rope_dim] or null
+    const uint16_t *rope_new;           // [A][n_new][H][rope_dim]
+    int rope_dim;
+    int n_new, keep;
+    int32_t *n_blocks_out, *n_window_out;
+};
+
 // Launchers (return hipError_t of the launch).
 hipError_t launch_quantize(const QuantArgs &a, hipStream_t s);
+hipError_t launch_append(const AppendArgs &a, hipStream_t s);          // append + counts
 hipError_t launch_dequantize(const DequantArgs &a, hipStream_t s);
 hipError_t launch_attend_generic(const AttnArgs &a, hipStream_t s);
 hipError_t launch_decode_gqa(const DecodeArgs &a, hipStream_t s);     // split + merge

@@ -78,13 +78,95 @@ __device__ __forceinline__ int seq_window(const Tables &t, int a)
     return nw < 0 ? 0 : (nw > t.window_cap ? t.window_cap : nw);
 }
 
+// One lane's share of a group: 8 bf16 values (raw) at positions 8*sub ..
+// 8*sub+7, sub = lane & 7; the 8 lanes of an aligned 8-lane slice hold one
+// group and must all be active.  Writes the lane's codes into the group's
+// 2B code words at gc and, from sub 0, the packed {fp16 scale, fp16 bias}.
+template <int B>
+__device__ __forceinline__ void quant_lane(const uint4 raw, int lane, uint8_t *gc, uint32_t *meta_word)
+{
+    constexpr int N = (1 << B) - 1;
+    const int sub = lane & 7;
+    float x[8];
+    x[0] = bf16_lo(raw.x); x[1] = bf16_hi(raw.x);
+    x[2] = bf16_lo(raw.y); x[3] = bf16_hi(raw.y);
+    x[4] = bf16_lo(raw.z); x[5] = bf16_hi(raw.z);
+    x[6] = bf16_lo(raw.w); x[7] = bf16_hi(raw.w);
+    float mn = x[0], mx = x[0];
+#pragma unroll
+    for (int i = 1; i < 8; i++) { mn = fminf(mn, x[i]); mx = fmaxf(mx, x[i]); }
+    mn = fminf(mn, dpp_f<DPP_XOR1>(mn));
+    mx = fmaxf(mx, dpp_f<DPP_XOR1>(mx));
+    mn = fminf(mn, dpp_f<DPP_XOR2>(mn));
+    mx = fmaxf(mx, dpp_f<DPP_XOR2>(mx));
+    mn = fminf(mn, dpp_f<DPP_HALF_MIRROR>(mn));
+    mx = fmaxf(mx, dpp_f<DPP_HALF_MIRROR>(mx));
+    mn = mn + 0.0f;                             // a zero extreme is +0
+    mx = mx + 0.0f;
+    // s = (mx - mn) / N, correctly rounded: reciprocal multiply plus one
+    // fma correction.  For N = 3, 7, 15, 255 this equals the IEEE
+    // quotient for every non-negative finite dividend (an exhaustive
+    // check over all 2^31 such floats is in the test suite).
+    const float range = mx - mn;
+    constexpr float RN = 1.0f / (float)N;
+    const float q0 = range * RN;
+    float s = __builtin_fmaf(__builtin_fmaf(-q0, (float)N, range), RN, q0);
+    // keep the binary32 rounding of s: without this barrier the compiler
+    // may fuse the fma with the fp16 conversion (one rounding, not two)
+    asm volatile("" : "+v"(s));
+    const uint16_t sh = f32_to_f16_bits(s);
+    const uint16_t bh = f32_to_f16_bits(mn);
+    const float sf = f16_bits_to_f32(sh);
+    const float bf = f16_bits_to_f32(bh);
+    // 1/sf, correctly rounded: hardware reciprocal (within 1 ulp) and one
+    // Newton step; exact for every positive finite fp16 sf from any start
+    // within 2 ulp (checked exhaustively in the test suite).
+    const float y0 = __builtin_amdgcn_rcpf(sf);
+    const float inv = (sf == 0.0f) ? 0.0f : __builtin_fmaf(__builtin_fmaf(-sf, y0, 1.0f), y0, y0);
+
+    // This lane's 8 codes, b bits each: codes 0..3 in lo, 4..7 in hi
+    // (for b <= 4 the caller only uses lo | hi << 4b, formed below).
+    uint32_t lo = 0, hi = 0;
+#pragma unroll
+    for (int i = 0; i < 8; i++) {
+        const float t = (x[i] - bf) * inv;
+        // round half to even, then clamp to [0, N] (one med3; the clamp
+        // equals max(0, min(N, r)) for every non-NaN r)
+        const float r = __builtin_amdgcn_fmed3f(__builtin_rintf(t), 0.0f, (float)N);
+        const uint32_t cq = (uint32_t)r;
+        if (i < 4) lo |= cq << (B * i);
+        else hi |= cq << (B * (i - 4));
+    }
+    const uint64_t v = (B == 8) ? ((uint64_t)lo | ((uint64_t)hi << 32))
+                                : (uint64_t)(lo | (hi << (4 * B)));
+
+    if constexpr (B == 4) {
+        reinterpret_cast<uint32_t *>(gc)[sub] = (uint32_t)v;
+    } else if constexpr (B == 8) {
+        reinterpret_cast<uint2 *>(gc)[sub] = make_uint2((uint32_t)v, (uint32_t)(v >> 32));
+    } else if constexpr (B == 2) {
+        uint32_t mine = (uint32_t)v;                // 16 bits
+        uint32_t other = dpp_u<DPP_XOR1>(mine);
+        if ((sub & 1) == 0) reinterpret_cast<uint32_t *>(gc)[sub >> 1] = mine | (other << 16);
+    } else {                                        // B == 3: 24 bits, 4 lanes -> 3 words
+        uint32_t mine = (uint32_t)v;
+        uint32_t next = dpp_u<DPP_NEXT>(mine);      // lane j+1 of the same quad
+        int j = sub & 3;
+        if (j < 3) {
+            uint32_t w = (mine >> (8 * j)) | (next << (24 - 8 * j));
+            reinterpret_cast<uint32_t *>(gc)[3 * (sub >> 2) + j] = w;
+        }
+    }
+    if (sub == 0) *meta_word = (uint32_t)sh | ((uint32_t)bh << 16);
+    (void)lane;
+}
+
 // Quantize the 64 tokens x D dims of (block j, head h) at width B.
 template <int B, int NG>
 __device__ __forceinline__ void quant_block(const uint16_t *__restrict__ src_blk, int H,
                                             uint8_t *__restrict__ blk, int h)
 {
     constexpr int D = NG * 64;
-    constexpr int N = (1 << B) - 1;
     constexpr int ITER = 2 * NG;                    // 64*NG groups / 32 per step
     constexpr int CODE_ROW = D * B / 8;             // bytes per (head, token)
     const int lane = threadIdx.x & 63;
@@ -101,84 +183,11 @@ __device__ __forceinline__ void quant_block(const uint16_t *__restrict__ src_blk
     }
 
     uint8_t *codes = blk + (size_t)h * 64 * CODE_ROW;
-    uint8_t *meta = blk + (size_t)H * 64 * CODE_ROW + (size_t)h * 64 * NG * 4;
-
+    uint32_t *meta = reinterpret_cast<uint32_t *>(blk + (size_t)H * 64 * CODE_ROW + (size_t)h * 64 * NG * 4);
 #pragma unroll
     for (int k = 0; k < ITER; k++) {
         const int gi = wave * 8 + gl + 32 * k;
-        float x[8];
-        x[0] = bf16_lo(raw[k].x); x[1] = bf16_hi(raw[k].x);
-        x[2] = bf16_lo(raw[k].y); x[3] = bf16_hi(raw[k].y);
-        x[4] = bf16_lo(raw[k].z); x[5] = bf16_hi(raw[k].z);
-        x[6] = bf16_lo(raw[k].w); x[7] = bf16_hi(raw[k].w);
-        float mn = x[0], mx = x[0];
-#pragma unroll
-        for (int i = 1; i < 8; i++) { mn = fminf(mn, x[i]); mx = fmaxf(mx, x[i]); }
-        mn = fminf(mn, dpp_f<DPP_XOR1>(mn));
-        mx = fmaxf(mx, dpp_f<DPP_XOR1>(mx));
-        mn = fminf(mn, dpp_f<DPP_XOR2>(mn));
-        mx = fmaxf(mx, dpp_f<DPP_XOR2>(mx));
-        mn = fminf(mn, dpp_f<DPP_HALF_MIRROR>(mn));
-        mx = fmaxf(mx, dpp_f<DPP_HALF_MIRROR>(mx));
-        mn = mn + 0.0f;                             // a zero extreme is +0
-        mx = mx + 0.0f;
-        // s = (mx - mn) / N, correctly rounded: reciprocal multiply plus one
-        // fma correction.  For N = 3, 7, 15, 255 this equals the IEEE
-        // quotient for every non-negative finite dividend (an exhaustive
-        // check over all 2^31 such floats is in the test suite).
-        const float range = mx - mn;
-        constexpr float RN = 1.0f / (float)N;
-        const float q0 = range * RN;
-        float s = __builtin_fmaf(__builtin_fmaf(-q0, (float)N, range), RN, q0);
-        // keep the binary32 rounding of s: without this barrier the compiler
-        // may fuse the fma with the fp16 conversion (one rounding, not two)
-        asm volatile("" : "+v"(s));
-        const uint16_t sh = f32_to_f16_bits(s);
-        const uint16_t bh = f32_to_f16_bits(mn);
-        const float sf = f16_bits_to_f32(sh);
-        const float bf = f16_bits_to_f32(bh);
-        // 1/sf, correctly rounded: hardware reciprocal (within 1 ulp) and one
-        // Newton step; exact for every positive finite fp16 sf from any start
-        // within 2 ulp (checked exhaustively in the test suite).
-        const float y0 = __builtin_amdgcn_rcpf(sf);
-        const float inv = (sf == 0.0f) ? 0.0f : __builtin_fmaf(__builtin_fmaf(-sf, y0, 1.0f), y0, y0);
-
-        // This lane's 8 codes, b bits each: codes 0..3 in lo, 4..7 in hi
-        // (for b <= 4 the caller only uses lo | hi << 4b, formed below).
-        uint32_t lo = 0, hi = 0;
-#pragma unroll
-        for (int i = 0; i < 8; i++) {
-            const float t = (x[i] - bf) * inv;
-            // round half to even, then clamp to [0, N] (one med3; the clamp
-            // equals max(0, min(N, r)) for every non-NaN r)
-            const float r = __builtin_amdgcn_fmed3f(__builtin_rintf(t), 0.0f, (float)N);
-            const uint32_t cq = (uint32_t)r;
-            if (i < 4) lo |= cq << (B * i);
-            else hi |= cq << (B * (i - 4));
-        }
-        const uint64_t v = (B == 8) ? ((uint64_t)lo | ((uint64_t)hi << 32))
-                                    : (uint64_t)(lo | (hi << (4 * B)));
-
-        uint8_t *gc = codes + (size_t)gi * (8 * B);  // group's code words (2B of them)
-        if constexpr (B == 4) {
-            reinterpret_cast<uint32_t *>(gc)[sub] = (uint32_t)v;
-        } else if constexpr (B == 8) {
-            reinterpret_cast<uint2 *>(gc)[sub] = make_uint2((uint32_t)v, (uint32_t)(v >> 32));
-        } else if constexpr (B == 2) {
-            uint32_t mine = (uint32_t)v;            // 16 bits
-            uint32_t other = dpp_u<DPP_XOR1>(mine);
-            if ((sub & 1) == 0) reinterpret_cast<uint32_t *>(gc)[sub >> 1] = mine | (other << 16);
-        } else {                                    // B == 3: 24 bits, 4 lanes -> 3 words
-            uint32_t mine = (uint32_t)v;
-            uint32_t next = dpp_u<DPP_NEXT>(mine);  // lane j+1 of the same quad
-            int j = sub & 3;
-            if (j < 3) {
-                uint32_t w = (mine >> (8 * j)) | (next << (24 - 8 * j));
-                reinterpret_cast<uint32_t *>(gc)[3 * (sub >> 2) + j] = w;
-            }
-        }
-        if (sub == 0)
-            reinterpret_cast<uint32_t *>(meta)[gi] = (uint32_t)sh | ((uint32_t)bh << 16);
+        quant_lane<B>(raw[k], lane, codes + (size_t)gi * (8 * B), meta + gi);
     }
 }
 
@@ -197,6 +206,135 @@ __global__ __launch_bounds__(256) void quantize_kernel(QuantArgs a)
     case 8: quant_block<8, NG>(src_blk, a.t.H, blk, h); break;
     default: break;                                 // precondition violation: nothing written
     }
+}
+
+// ---- append (quantize on append / window roll) ------------------------------
+// For sequence a with W window tokens, the stream T = window[0..W) ++
+// new[0..n_new) ends as: k = (W + n_new - keep) / 64 new blocks (when W +
+// n_new > keep) made of T[0 .. 64k), then the window T[64k ..).  Widths and
+// pool offsets of the new blocks are the caller's table entries nb .. nb+k-1.
+// Blocks past max_blocks and window tokens past window_cap are never written
+// (either would be a precondition violation).
+__device__ __forceinline__ void append_plan(const AppendArgs &p, int a, int &nb, int &W, int &k, int &W2)
+{
+    nb = seq_blocks(p.t, a);
+    W = seq_window(p.t, a);
+    const int T = W + p.n_new;
+    k = T > p.keep ? (T - p.keep) / 64 : 0;
+    if (k > p.t.max_blocks - nb) k = p.t.max_blocks - nb;
+    W2 = T - 64 * k;
+    if (W2 > p.t.window_cap) W2 = p.t.window_cap;
+}
+
+// A 64-element slice (16-byte piece c of 8) of stream token t of head h:
+// from the window (base win_a, token stride ts) or from the new rows.
+__device__ __forceinline__ const uint16_t *stream_piece(const uint16_t *win_a, const uint16_t *new_a, size_t ts,
+                                                         int W, int t, int h, int width, int col)
+{
+    return (t < W ? win_a + (size_t)t * ts : new_a + (size_t)(t - W) * ts) + (size_t)h * width + col;
+}
+
+// One workgroup per (slice, head, sequence): slice g < D/64 is the 64-dim
+// group g of K and V; slice D/64 (when rope_dim is 64) writes the new tokens'
+// rope rows, which are indexed by token position and so never move.  Phase 1
+// turns the stream's first 64k tokens into blocks; phase 2 moves the rest to
+// the window front in rounds of 64 tokens.  A round writes positions
+// [r0, r0+64) and reads [64k + r0, 64k + r0 + 64): every location a round
+// overwrites was read by an earlier round (or this one) and is never read
+// again, so a barrier between rounds is the only ordering needed.  Slices of
+// different workgroups are disjoint.
+__global__ __launch_bounds__(256) void append_kernel(AppendArgs p)
+{
+    const int g = blockIdx.x, h = blockIdx.y, a = blockIdx.z;
+    const int H = p.t.H, D = p.t.D, NG = D / 64, R = p.rope_dim;
+    const int tid = threadIdx.x, lane = tid & 63;
+    int nb, W, k, W2;
+    append_plan(p, a, nb, W, k, W2);
+    if (g >= NG) {
+        // rope rows of the new tokens: token W + i of the stream is sequence
+        // position 64*nb + W + i
+        const size_t rope_tokens = (size_t)64 * p.t.max_blocks + p.t.window_cap;
+        const int64_t room = (int64_t)rope_tokens - (64 * (int64_t)nb + W);
+        const int n = (int)min((int64_t)p.n_new, room);
+        uint16_t *dst = p.rope + ((size_t)a * rope_tokens + (size_t)64 * nb + W) * H * R;
+        const uint16_t *src = p.rope_new + (size_t)a * p.n_new * H * R;
+        for (int idx = tid; idx < n * 8; idx += 256) {
+            const int i = idx >> 3, col = 8 * (idx & 7);
+            *reinterpret_cast<uint4 *>(dst + ((size_t)i * H + h) * R + col) =
+                *reinterpret_cast<const uint4 *>(src + ((size_t)i * H + h) * R + col);
+        }
+        return;
+    }
+
+    // Phase 1: blocks nb .. nb+k-1.
+    for (int i = 0; i < k; i++) {
+        const size_t e = (size_t)a * p.t.max_blocks + nb + i;
+        const int B = p.t.bits[e];
+        const int code_row = D * B / 8;
+        for (int kv = 0; kv < 2; kv++) {
+            uint8_t *pool = kv ? p.v_pool : p.k_pool;
+            if (!pool) continue;
+            const uint16_t *win_a = (kv ? p.v_window : p.k_window);
+            if (win_a) win_a += (size_t)a * p.t.window_cap * H * D;
+            const uint16_t *new_a = (kv ? p.v_new : p.k_new) + (size_t)a * p.n_new * H * D;
+            uint8_t *blk = pool + (kv ? p.v_offset : p.k_offset)[e];
+            uint4 raw[2];
+#pragma unroll
+            for (int st = 0; st < 2; st++) {
+                const int r = 32 * st + (tid >> 3);
+                raw[st] = *reinterpret_cast<const uint4 *>(
+                    stream_piece(win_a, new_a, (size_t)H * D, W, 64 * i + r, h, D, 64 * g + 8 * (tid & 7)));
+            }
+#pragma unroll
+            for (int st = 0; st < 2; st++) {
+                const int r = 32 * st + (tid >> 3);
+                uint8_t *gc = blk + ((size_t)h * 64 + r) * code_row + (size_t)g * 8 * B;
+                uint32_t *mw = reinterpret_cast<uint32_t *>(blk + (size_t)H * 64 * code_row) +
+                               ((size_t)h * 64 + r) * NG + g;
+                switch (B) {
+                case 2: quant_lane<2>(raw[st], lane, gc, mw); break;
+                case 3: quant_lane<3>(raw[st], lane, gc, mw); break;
+                case 4: quant_lane<4>(raw[st], lane, gc, mw); break;
+                case 8: quant_lane<8>(raw[st], lane, gc, mw); break;
+                default: break;                 // precondition violation: nothing written
+                }
+            }
+        }
+    }
+    __syncthreads();
+
+    // Phase 2: window[u] = T[64k + u] for u < W2 (already in place when k == 0
+    // and the token is an old window token).
+    for (int r0 = 0; r0 < W2; r0 += 64) {
+#pragma unroll
+        for (int rep = 0; rep < 2; rep++) {
+            const int idx = tid + 256 * rep;
+            const int u = r0 + (idx >> 3), col = 8 * (idx & 7);
+            const int t = 64 * k + u;
+            if (u >= W2 || (k == 0 && t < W)) continue;
+            for (int kv = 0; kv < 2; kv++) {
+                uint16_t *win = kv ? p.v_window : p.k_window;
+                if (!win || (kv && !p.v_pool)) continue;
+                uint16_t *win_a = win + (size_t)a * p.t.window_cap * H * D;
+                const uint16_t *new_a = (kv ? p.v_new : p.k_new) + (size_t)a * p.n_new * H * D;
+                const uint4 v = *reinterpret_cast<const uint4 *>(
+                    stream_piece(win_a, new_a, (size_t)H * D, W, t, h, D, 64 * g + col));
+                *reinterpret_cast<uint4 *>(win_a + ((size_t)u * H + h) * D + 64 * g + col) = v;
+            }
+        }
+        __syncthreads();
+    }
+}
+
+// New counts, after every slice has read the old ones.
+__global__ void append_counts(AppendArgs p)
+{
+    const int a = blockIdx.x * blockDim.x + threadIdx.x;
+    if (a >= p.t.A) return;
+    int nb, W, k, W2;
+    append_plan(p, a, nb, W, k, W2);
+    p.n_blocks_out[a] = nb + k;
+    if (p.n_window_out) p.n_window_out[a] = W2;
 }
 
 // ---- restore ---------------------------------------------------------------
@@ -324,6 +462,16 @@ hipError_t launch_quantize(const QuantArgs &a, hipStream_t s)
     case 8: quantize_kernel<8><<<grid, 256, 0, s>>>(a); break;
     default: return hipErrorInvalidValue;
     }
+    return hipGetLastError();
+}
+
+hipError_t launch_append(const AppendArgs &a, hipStream_t s)
+{
+    dim3 grid(a.t.D / 64 + (a.rope_dim ? 1 : 0), a.t.H, a.t.A);
+    append_kernel<<<grid, 256, 0, s>>>(a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    append_counts<<<(a.t.A + 255) / 256, 256, 0, s>>>(a);
     return hipGetLastError();
 }
 

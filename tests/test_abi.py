@@ -174,3 +174,31 @@ def test_chunk_rejects():
     assert call(Hq=3) == kvq.KVQ_EINVAL
     assert call(wsb=16) == kvq.KVQ_ENOSPC
     assert call(n=0) == kvq.KVQ_OK                            # nothing to do, nothing launched
+
+
+def test_append_rejects():
+    L, K, V = _layout(window_cap=191), _store(), _store()
+    ap = kvq.lib().kvq_append
+    P = lambda x: None if x is None else ctypes.c_void_p(x)
+
+    def call(Lx=L, Vs=V, k=FAKE, v=FAKE, rope=None, rope_new=None, rope_dim=0, n=1, keep=128,
+             nbo=FAKE, nwo=FAKE):
+        return ap(ctypes.byref(Lx), ctypes.byref(K), None if Vs is None else ctypes.byref(Vs), P(k),
+                  P(v), P(rope), P(rope_new), rope_dim, n, keep, P(nbo), P(nwo), None)
+    assert call(n=-1) == kvq.KVQ_EINVAL
+    assert call(keep=-1) == kvq.KVQ_EINVAL
+    assert call(keep=129) == kvq.KVQ_EINVAL                  # keep + 63 > window_cap
+    assert call(k=None) == kvq.KVQ_EINVAL
+    assert call(v=None) == kvq.KVQ_EINVAL
+    assert call(k=FAKE + 2) == kvq.KVQ_EINVAL
+    assert call(nbo=None) == kvq.KVQ_EINVAL
+    assert call(nwo=None) == kvq.KVQ_EINVAL
+    assert call(nbo=FAKE + 2) == kvq.KVQ_EINVAL
+    assert call(rope_dim=32, rope=FAKE, rope_new=FAKE) == kvq.KVQ_EUNSUPPORTED
+    assert call(rope_dim=64) == kvq.KVQ_EINVAL                # no rope buffers
+    assert call(rope_dim=64, rope=FAKE) == kvq.KVQ_EINVAL
+    L0 = _layout(window_cap=0)
+    assert call(Lx=L0, keep=0, n=5) == kvq.KVQ_EINVAL        # no window: whole blocks only
+    assert call(Lx=L0, keep=1, n=64) == kvq.KVQ_EINVAL
+    assert ap(None, ctypes.byref(K), ctypes.byref(V), P(FAKE), P(FAKE), None, None, 0, 1, 0, P(FAKE),
+              P(FAKE), None) == kvq.KVQ_EINVAL
