@@ -45,6 +45,9 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--copy-calibration", action="store_true",
                    help="only run a plain 1 GiB device copy (the reference for the HBM byte counters)")
+    p.add_argument("--append", type=int, default=0, metavar="N_NEW",
+                   help="time kvq_append of N_NEW tokens per agent on the Llama 10-agent shape "
+                        "(windows of 128..191 tokens, keep 128) instead of the workload step")
     return p.parse_args()
 
 
@@ -227,10 +230,88 @@ class _FakeCache:
 
 
 # ---------------------------------------------------------------------------
+def append_bench(args):
+    """kvq_append (window roll) on the Llama-3.1-8B layer shape, 10 agents:
+    windows start at 128..191 bf16 tokens (keep 128) over 64 Q4 blocks, and
+    each call appends N_NEW tokens of K and V per agent, back to back on one
+    cache whose blocks advance through the pool (as in a decode or prefill
+    loop).  Algorithmic bytes per call: the new rows read, the old window
+    rows moved or cut (read, when a block is cut), the window rows written
+    and the block payloads written, for K and V, from the host copy of the
+    counts before each call.  New-row buffers rotate past the 256 MB
+    last-level cache."""
+    import torch
+    import kvq_synth as syn
+    import quantized_kv_cache_group_amd as kvq
+
+    kvq.lib()
+    torch.cuda.set_device(0)
+    w = syn.workload(1)
+    A, H, D, n = w.n_agents, w.n_kv_heads, w.head_dim, args.append
+    keep, cap = 128, 191
+    r = syn.rng(1, syn.TAG_LEN)
+    win0 = [int(v) for v in r.integers(keep, cap, size=A, endpoint=True)]
+    nb0 = [64] * A
+    calls = args.warmup + args.steps
+    mb = 64 + (cap + n * calls) // 64 + 1
+    blk = kvq.block_bytes(4, H, D)
+    row = H * D * 2
+    c = kvq.LayerCache(H, D, nb0, win0, None, max_blocks=mb, window_cap=cap, future_bits=4)
+    g = torch.Generator(device="cuda")
+    g.manual_seed(11)
+    c.k_window.normal_(generator=g)
+    c.v_window.normal_(generator=g)
+    R = min(16, max(2, int(np.ceil(2 * MALL_BYTES / max(2 * A * n * row, 1))) + 1))
+    news = [(torch.randn((A, n, H, D), generator=g, device="cuda").to(torch.bfloat16),
+             torch.randn((A, n, H, D), generator=g, device="cuda").to(torch.bfloat16)) for _ in range(R)]
+
+    def call_bytes():
+        b = 0
+        for a in range(A):
+            W = c.n_window_host[a]
+            T = W + n
+            k = (T - keep) // 64 if T > keep else 0
+            moved, written = (W, T - 64 * k) if k else (0, n)
+            b += 2 * ((n + moved + written) * row + k * blk)
+        return b
+
+    for i in range(args.warmup):
+        c.append(*news[i % R], keep_recent=keep)
+    torch.cuda.synchronize()
+    total = 0
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for i in range(args.steps):
+        total += call_bytes()
+        c.append(*news[(args.warmup + i) % R], keep_recent=keep)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / args.steps
+    gbs = total / args.steps / (us * 1e-6) / 1e9
+    res = {"metric": "kvq_append (quantize on append) GB/s", "value": round(gbs, 2), "unit": "GB/s",
+           "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "us_per_call": round(us, 3),
+           "higher_is_better": True, "dtype": "bf16->u4", "data": "synthetic",
+           "config": {"workload": f"llama8b-10agent-append-{n}", "agents": A, "kv_heads": H, "head_dim": D,
+                      "window_start": win0, "keep_recent": keep, "window_cap": cap, "n_new": n,
+                      "bits": 4, "rotated_inputs": R},
+           "bytes_per_call": round(total / args.steps),
+           "roofline": {"kernel": "kvq append", "bound": "hbm", "achieved": round(gbs, 2),
+                        "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
+                        "traffic": None}}
+    print(json.dumps(res), flush=True)
+
+
 def main():
     args = parse()
     if args.copy_calibration:
         copy_calibration()
+        return
+    if args.append:
+        if args.gpus != 1:
+            print("bench.py measures one GPU only", file=sys.stderr)
+            sys.exit(2)
+        append_bench(args)
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}); "

@@ -109,7 +109,7 @@ struct AppendArgs {
 
 // Launchers (return hipError_t of the launch).
 hipError_t launch_quantize(const QuantArgs &a, hipStream_t s);
-hipError_t launch_append(const AppendArgs &a, hipStream_t s);          // append + counts
+hipError_t launch_append(const AppendArgs &a, hipStream_t s);          // blocks, window, counts
 hipError_t launch_dequantize(const DequantArgs &a, hipStream_t s);
 hipError_t launch_attend_generic(const AttnArgs &a, hipStream_t s);
 hipError_t launch_decode_gqa(const DecodeArgs &a, hipStream_t s);     // split + merge

@@ -161,34 +161,47 @@ __device__ __forceinline__ void quant_lane(const uint4 raw, int lane, uint8_t *g
     (void)lane;
 }
 
-// Quantize the 64 tokens x D dims of (block j, head h) at width B.
+// Group index of this lane's k-th 16-byte piece inside a (block, head): a
+// group of 64 bf16 values (128 contiguous bytes) belongs to 8 lanes, so a
+// wave covers 8 groups per step and the 4 waves 32.
+__device__ __forceinline__ int piece_group(int k)
+{
+    return (int)(threadIdx.x >> 6) * 8 + (int)((threadIdx.x & 63) >> 3) + 32 * k;
+}
+
+// Codes and scale/bias of the 64 tokens x D dims of head h of a block of
+// width B, from this lane's pieces raw[k] (group piece_group(k)).
+template <int B, int NG>
+__device__ __forceinline__ void quant_rows(const uint4 (&raw)[2 * NG], uint8_t *__restrict__ blk, int H, int h)
+{
+    constexpr int D = NG * 64;
+    constexpr int CODE_ROW = D * B / 8;             // bytes per (head, token)
+    const int lane = threadIdx.x & 63;
+    uint8_t *codes = blk + (size_t)h * 64 * CODE_ROW;
+    uint32_t *meta = reinterpret_cast<uint32_t *>(blk + (size_t)H * 64 * CODE_ROW + (size_t)h * 64 * NG * 4);
+#pragma unroll
+    for (int k = 0; k < 2 * NG; k++) {
+        const int gi = piece_group(k);
+        quant_lane<B>(raw[k], lane, codes + (size_t)gi * (8 * B), meta + gi);
+    }
+}
+
+// Quantize the 64 tokens x D dims of (block j, head h) at width B.  Every
+// lane loads all of its data before the arithmetic.
 template <int B, int NG>
 __device__ __forceinline__ void quant_block(const uint16_t *__restrict__ src_blk, int H,
                                             uint8_t *__restrict__ blk, int h)
 {
     constexpr int D = NG * 64;
-    constexpr int ITER = 2 * NG;                    // 64*NG groups / 32 per step
-    constexpr int CODE_ROW = D * B / 8;             // bytes per (head, token)
-    const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
-    const int sub = lane & 7;                       // lane within the group
-    const int gl = lane >> 3;                       // group within the wave step
-
-    uint4 raw[ITER];
+    const int sub = threadIdx.x & 7;
+    uint4 raw[2 * NG];
 #pragma unroll
-    for (int k = 0; k < ITER; k++) {
-        int gi = wave * 8 + gl + 32 * k;            // group index inside the (block, head)
-        int r = gi / NG, g = gi % NG;
+    for (int k = 0; k < 2 * NG; k++) {
+        const int gi = piece_group(k);
+        const int r = gi / NG, g = gi % NG;
         raw[k] = *reinterpret_cast<const uint4 *>(src_blk + ((size_t)r * H + h) * D + g * 64 + sub * 8);
     }
-
-    uint8_t *codes = blk + (size_t)h * 64 * CODE_ROW;
-    uint32_t *meta = reinterpret_cast<uint32_t *>(blk + (size_t)H * 64 * CODE_ROW + (size_t)h * 64 * NG * 4);
-#pragma unroll
-    for (int k = 0; k < ITER; k++) {
-        const int gi = wave * 8 + gl + 32 * k;
-        quant_lane<B>(raw[k], lane, codes + (size_t)gi * (8 * B), meta + gi);
-    }
+    quant_rows<B, NG>(raw, blk, H, h);
 }
 
 template <int NG>
@@ -234,25 +247,111 @@ __device__ __forceinline__ const uint16_t *stream_piece(const uint16_t *win_a, c
     return (t < W ? win_a + (size_t)t * ts : new_a + (size_t)(t - W) * ts) + (size_t)h * width + col;
 }
 
-// One workgroup per (slice, head, sequence): slice g < D/64 is the 64-dim
-// group g of K and V; slice D/64 (when rope_dim is 64) writes the new tokens'
-// rope rows, which are indexed by token position and so never move.  Phase 1
-// turns the stream's first 64k tokens into blocks; phase 2 moves the rest to
-// the window front in rounds of 64 tokens.  A round writes positions
-// [r0, r0+64) and reads [64k + r0, 64k + r0 + 64): every location a round
-// overwrites was read by an earlier round (or this one) and is never read
-// again, so a barrier between rounds is the only ordering needed.  Slices of
-// different workgroups are disjoint.
-__global__ __launch_bounds__(256) void append_kernel(AppendArgs p)
+// Blocks: one workgroup per (new block i, head h, sequence a), all groups of
+// the head, K and V loads issued together.  Blocks only read the stream, so
+// they run side by side; the window moves in the next launch.
+template <int NG>
+__global__ __launch_bounds__(256) void append_blocks(AppendArgs p)
+{
+    constexpr int D = NG * 64;
+    const int i = blockIdx.x, h = blockIdx.y, a = blockIdx.z;
+    const int H = p.t.H;
+    int nb, W, k, W2;
+    append_plan(p, a, nb, W, k, W2);
+    if (i >= k) return;
+    const size_t e = (size_t)a * p.t.max_blocks + nb + i;
+    const int B = p.t.bits[e];
+    const int sub = threadIdx.x & 7;
+    const int n_kv = p.v_pool ? 2 : 1;
+    uint4 raw[2][2 * NG];
+#pragma unroll
+    for (int kv = 0; kv < 2; kv++) {
+        if (kv >= n_kv) break;
+        const uint16_t *win_a = kv ? p.v_window : p.k_window;
+        if (win_a) win_a += (size_t)a * p.t.window_cap * H * D;
+        const uint16_t *new_a = (kv ? p.v_new : p.k_new) + (size_t)a * p.n_new * H * D;
+#pragma unroll
+        for (int kk = 0; kk < 2 * NG; kk++) {
+            const int gi = piece_group(kk);
+            const int r = gi / NG, g = gi % NG;
+            raw[kv][kk] = *reinterpret_cast<const uint4 *>(
+                stream_piece(win_a, new_a, (size_t)H * D, W, 64 * i + r, h, D, 64 * g + 8 * sub));
+        }
+    }
+#pragma unroll
+    for (int kv = 0; kv < 2; kv++) {
+        if (kv >= n_kv) break;
+        uint8_t *blk = (kv ? p.v_pool : p.k_pool) + (kv ? p.v_offset : p.k_offset)[e];
+        switch (B) {
+        case 2: quant_rows<2, NG>(raw[kv], blk, H, h); break;
+        case 3: quant_rows<3, NG>(raw[kv], blk, H, h); break;
+        case 4: quant_rows<4, NG>(raw[kv], blk, H, h); break;
+        case 8: quant_rows<8, NG>(raw[kv], blk, H, h); break;
+        default: break;                             // precondition violation: nothing written
+        }
+    }
+}
+
+// Window: one workgroup per (slice, head, sequence), slice g < D/64 the
+// 64-dim group g of K and V.  window[u] = T[64k + u] for u < W2, in rounds of
+// WR tokens: a round loads all of its source pieces into registers, waits at
+// a barrier, then stores.  A round writes positions [r0, r0+WR) and reads
+// [64k + r0, 64k + r0 + WR): its own overlap is ordered by the barrier, and
+// it never writes what a later round reads (those start at 64k + r0 + WR >=
+// r0 + WR), so one barrier per round suffices (one round for windows of up to
+// WR tokens).  When k == 0 the old window rows are already in place and only
+// the new tokens are written, with no overlap.  The last slice (rope_dim 64)
+// writes the new tokens' rope rows, which are indexed by token position and
+// so never move.
+constexpr int WR = 192;                              // window rows per round
+constexpr int WR_PER = WR * 8 / 256;                 // 16-byte pieces per lane and round
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));   // plain vector: no struct copies
+
+template <int NKV>
+__device__ __forceinline__ void window_rounds(const AppendArgs &p, int a, int h, int g, int W, int k, int W2)
+{
+    const int H = p.t.H, D = p.t.D, tid = threadIdx.x;
+    const uint16_t *src_w[2] = {p.k_window + (size_t)a * p.t.window_cap * H * D,
+                                NKV > 1 ? p.v_window + (size_t)a * p.t.window_cap * H * D : nullptr};
+    const uint16_t *src_n[2] = {p.k_new + (size_t)a * p.n_new * H * D,
+                                NKV > 1 ? p.v_new + (size_t)a * p.n_new * H * D : nullptr};
+    uint16_t *dst_w[2] = {p.k_window + (size_t)a * p.t.window_cap * H * D,
+                          NKV > 1 ? p.v_window + (size_t)a * p.t.window_cap * H * D : nullptr};
+    for (int r0 = (k == 0 ? W : 0); r0 < W2; r0 += WR) {
+        u32x4 v[WR_PER][NKV];
+#pragma unroll
+        for (int rep = 0; rep < WR_PER; rep++) {
+            const int idx = tid + 256 * rep;
+            const int u = min(r0 + (idx >> 3), W2 - 1), col = 8 * (idx & 7);   // clamped: in bounds
+#pragma unroll
+            for (int kv = 0; kv < NKV; kv++)
+                v[rep][kv] = *reinterpret_cast<const u32x4 *>(
+                    stream_piece(src_w[kv], src_n[kv], (size_t)H * D, W, 64 * k + u, h, D, 64 * g + col));
+        }
+        if (k > 0) __syncthreads();                 // every source piece is in registers
+#pragma unroll
+        for (int rep = 0; rep < WR_PER; rep++) {
+            const int idx = tid + 256 * rep;
+            const int u = r0 + (idx >> 3), col = 8 * (idx & 7);
+            if (u < W2) {
+#pragma unroll
+                for (int kv = 0; kv < NKV; kv++)
+                    *reinterpret_cast<u32x4 *>(dst_w[kv] + ((size_t)u * H + h) * D + 64 * g + col) = v[rep][kv];
+            }
+        }
+    }
+}
+
+__global__ __launch_bounds__(256) void append_window(AppendArgs p)
 {
     const int g = blockIdx.x, h = blockIdx.y, a = blockIdx.z;
     const int H = p.t.H, D = p.t.D, NG = D / 64, R = p.rope_dim;
-    const int tid = threadIdx.x, lane = tid & 63;
+    const int tid = threadIdx.x;
     int nb, W, k, W2;
     append_plan(p, a, nb, W, k, W2);
     if (g >= NG) {
-        // rope rows of the new tokens: token W + i of the stream is sequence
-        // position 64*nb + W + i
+        // token W + i of the stream is sequence position 64*nb + W + i
         const size_t rope_tokens = (size_t)64 * p.t.max_blocks + p.t.window_cap;
         const int64_t room = (int64_t)rope_tokens - (64 * (int64_t)nb + W);
         const int n = (int)min((int64_t)p.n_new, room);
@@ -265,65 +364,8 @@ __global__ __launch_bounds__(256) void append_kernel(AppendArgs p)
         }
         return;
     }
-
-    // Phase 1: blocks nb .. nb+k-1.
-    for (int i = 0; i < k; i++) {
-        const size_t e = (size_t)a * p.t.max_blocks + nb + i;
-        const int B = p.t.bits[e];
-        const int code_row = D * B / 8;
-        for (int kv = 0; kv < 2; kv++) {
-            uint8_t *pool = kv ? p.v_pool : p.k_pool;
-            if (!pool) continue;
-            const uint16_t *win_a = (kv ? p.v_window : p.k_window);
-            if (win_a) win_a += (size_t)a * p.t.window_cap * H * D;
-            const uint16_t *new_a = (kv ? p.v_new : p.k_new) + (size_t)a * p.n_new * H * D;
-            uint8_t *blk = pool + (kv ? p.v_offset : p.k_offset)[e];
-            uint4 raw[2];
-#pragma unroll
-            for (int st = 0; st < 2; st++) {
-                const int r = 32 * st + (tid >> 3);
-                raw[st] = *reinterpret_cast<const uint4 *>(
-                    stream_piece(win_a, new_a, (size_t)H * D, W, 64 * i + r, h, D, 64 * g + 8 * (tid & 7)));
-            }
-#pragma unroll
-            for (int st = 0; st < 2; st++) {
-                const int r = 32 * st + (tid >> 3);
-                uint8_t *gc = blk + ((size_t)h * 64 + r) * code_row + (size_t)g * 8 * B;
-                uint32_t *mw = reinterpret_cast<uint32_t *>(blk + (size_t)H * 64 * code_row) +
-                               ((size_t)h * 64 + r) * NG + g;
-                switch (B) {
-                case 2: quant_lane<2>(raw[st], lane, gc, mw); break;
-                case 3: quant_lane<3>(raw[st], lane, gc, mw); break;
-                case 4: quant_lane<4>(raw[st], lane, gc, mw); break;
-                case 8: quant_lane<8>(raw[st], lane, gc, mw); break;
-                default: break;                 // precondition violation: nothing written
-                }
-            }
-        }
-    }
-    __syncthreads();
-
-    // Phase 2: window[u] = T[64k + u] for u < W2 (already in place when k == 0
-    // and the token is an old window token).
-    for (int r0 = 0; r0 < W2; r0 += 64) {
-#pragma unroll
-        for (int rep = 0; rep < 2; rep++) {
-            const int idx = tid + 256 * rep;
-            const int u = r0 + (idx >> 3), col = 8 * (idx & 7);
-            const int t = 64 * k + u;
-            if (u >= W2 || (k == 0 && t < W)) continue;
-            for (int kv = 0; kv < 2; kv++) {
-                uint16_t *win = kv ? p.v_window : p.k_window;
-                if (!win || (kv && !p.v_pool)) continue;
-                uint16_t *win_a = win + (size_t)a * p.t.window_cap * H * D;
-                const uint16_t *new_a = (kv ? p.v_new : p.k_new) + (size_t)a * p.n_new * H * D;
-                const uint4 v = *reinterpret_cast<const uint4 *>(
-                    stream_piece(win_a, new_a, (size_t)H * D, W, t, h, D, 64 * g + col));
-                *reinterpret_cast<uint4 *>(win_a + ((size_t)u * H + h) * D + 64 * g + col) = v;
-            }
-        }
-        __syncthreads();
-    }
+    if (p.v_pool) window_rounds<2>(p, a, h, g, W, k, W2);
+    else window_rounds<1>(p, a, h, g, W, k, W2);
 }
 
 // New counts, after every slice has read the old ones.
@@ -467,10 +509,33 @@ hipError_t launch_quantize(const QuantArgs &a, hipStream_t s)
 
 hipError_t launch_append(const AppendArgs &a, hipStream_t s)
 {
-    dim3 grid(a.t.D / 64 + (a.rope_dim ? 1 : 0), a.t.H, a.t.A);
-    append_kernel<<<grid, 256, 0, s>>>(a);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
+    // A call cuts at most (window_cap + n_new - keep) / 64 blocks per sequence.
+    const int64_t kmax = a.t.window_cap + (int64_t)a.n_new > a.keep
+                             ? (a.t.window_cap + (int64_t)a.n_new - a.keep) / 64 : 0;
+    const int64_t kgrid = kmax < a.t.max_blocks ? kmax : a.t.max_blocks;
+    if (kgrid > 0x7fffffff) return hipErrorInvalidValue;
+    if (kgrid > 0) {
+        dim3 grid((unsigned)kgrid, a.t.H, a.t.A);
+        switch (a.t.D / 64) {
+        case 1: append_blocks<1><<<grid, 256, 0, s>>>(a); break;
+        case 2: append_blocks<2><<<grid, 256, 0, s>>>(a); break;
+        case 3: append_blocks<3><<<grid, 256, 0, s>>>(a); break;
+        case 4: append_blocks<4><<<grid, 256, 0, s>>>(a); break;
+        case 5: append_blocks<5><<<grid, 256, 0, s>>>(a); break;
+        case 6: append_blocks<6><<<grid, 256, 0, s>>>(a); break;
+        case 7: append_blocks<7><<<grid, 256, 0, s>>>(a); break;
+        case 8: append_blocks<8><<<grid, 256, 0, s>>>(a); break;
+        default: return hipErrorInvalidValue;
+        }
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    if (a.t.window_cap > 0 || a.rope_dim) {
+        dim3 grid(a.t.D / 64 + (a.rope_dim ? 1 : 0), a.t.H, a.t.A);
+        append_window<<<grid, 256, 0, s>>>(a);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
     append_counts<<<(a.t.A + 255) / 256, 256, 0, s>>>(a);
     return hipGetLastError();
 }
