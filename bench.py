@@ -45,6 +45,9 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--copy-calibration", action="store_true",
                    help="only run a plain 1 GiB device copy (the reference for the HBM byte counters)")
+    p.add_argument("--card", action="store_true",
+                   help="time CacheCard gather and scatter of the Llama 10-agent caches "
+                        "(device image <-> cache) instead of the workload step")
     p.add_argument("--append", type=int, default=0, metavar="N_NEW",
                    help="time kvq_append of N_NEW tokens per agent on the Llama 10-agent shape "
                         "(windows of 128..191 tokens, keep 128) instead of the workload step")
@@ -302,8 +305,82 @@ def append_bench(args):
     print(json.dumps(res), flush=True)
 
 
+def card_bench(args):
+    """CacheCard gather (cache -> contiguous device image) and scatter (image
+    -> cache) for each of the 10 agents of the Llama-3.1-8B layer shape (4096
+    tokens, 64 Q4 blocks, K and V).  Bytes moved per call: the image read plus
+    written.  Copies rotate past the 256 MB last-level cache.  Host file
+    framing is timed separately (host I/O, not a GPU figure)."""
+    import tempfile
+    import torch
+    import kvq_synth as syn
+    import quantized_kv_cache_group_amd as kvq
+    from quantized_kv_cache_group_amd import card
+
+    kvq.lib()
+    torch.cuda.set_device(0)
+    w = syn.workload(1)
+    A, H, D = w.n_agents, w.n_kv_heads, w.head_dim
+    one = A * 2 * w.n_blocks[0] * kvq.block_bytes(4, H, D)
+    R = min(8, max(2, int(np.ceil(2 * MALL_BYTES / (2 * one))) + 1))
+    caches = [kvq.LayerCache(H, D, w.n_blocks, w.n_window, None) for _ in range(R)]
+    for c in caches:
+        c.k_pool.random_(0, 256)
+        c.v_pool.random_(0, 256)
+    n = caches[0].card_bytes(0)
+    imgs = [[torch.empty(n, dtype=torch.uint8, device="cuda") for _ in range(A)] for _ in range(R)]
+    stream = torch.cuda.current_stream()
+    strm = kvq._stream()
+    stores = [(c.store("k"), c.store("v")) for c in caches]
+
+    def run(kind, steps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for i in range(steps):
+            c = caches[i % R]
+            for a in range(A):
+                # C ABI directly (sizes precomputed; for scatter the tables already
+                # hold the card's counts and widths)
+                fn = kvq.lib().kvq_card_gather if kind == "gather" else kvq.lib().kvq_card_scatter
+                kvq._check(fn(kvq.ctypes.byref(c.layout()), kvq.ctypes.byref(stores[i % R][0]),
+                              kvq.ctypes.byref(stores[i % R][1]), None, 0, a, kvq._ptr(imgs[i % R][a]), n,
+                              strm), kind)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / (steps * A)
+    run("gather", args.warmup)
+    g_us = run("gather", args.steps)
+    run("scatter", args.warmup)
+    s_us = run("scatter", args.steps)
+    t0 = time.perf_counter()
+    with tempfile.TemporaryDirectory() as d:
+        for a in range(A):
+            card.save_card(caches[0], a, f"{d}/{a}.kvqcard")
+        t1 = time.perf_counter()
+        c2, _ = card.cache_from_cards([f"{d}/{a}.kvqcard" for a in range(A)])
+        torch.cuda.synchronize()
+        t2 = time.perf_counter()
+    g_gbs = 2 * n / (g_us * 1e-6) / 1e9
+    s_gbs = 2 * n / (s_us * 1e-6) / 1e9
+    res = {"metric": "CacheCard gather GB/s", "value": round(g_gbs, 2), "unit": "GB/s", "n_gpus": 1,
+           "steps": args.steps, "warmup": args.warmup, "higher_is_better": True, "dtype": "u8",
+           "data": "synthetic",
+           "config": {"workload": "llama8b-10agent-q4-cachecard", "agents": A, "kv_heads": H, "head_dim": D,
+                      "tokens": w.lengths[0], "bits": 4, "image_bytes": n, "rotated_copies": R},
+           "gather_us_per_agent": round(g_us, 3), "scatter_us_per_agent": round(s_us, 3),
+           "scatter_GBps": round(s_gbs, 2),
+           "host_file_save_s_10_agents": round(t1 - t0, 4), "host_file_load_s_10_agents": round(t2 - t1, 4),
+           "roofline": {"kernel": "kvq card gather", "bound": "hbm", "achieved": round(g_gbs, 2),
+                        "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(g_gbs / HBM_PEAK_GBS, 4),
+                        "traffic": None}}
+    print(json.dumps(res), flush=True)
+
+
 def main():
     args = parse()
+    if args.card:
+        card_bench(args)
+        return
     if args.copy_calibration:
         copy_calibration()
         return

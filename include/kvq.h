@@ -157,6 +157,38 @@ int kvq_append(const kvq_layout *L, const kvq_store *K, const kvq_store *V,
 int kvq_dequantize(const kvq_layout *L, const kvq_store *src, int32_t out_dtype, void *dst,
                    int64_t dst_seq_tokens, void *stream);
 
+/* CacheCard image of one sequence (QKVShare, Metodologia: a CacheCard packs
+ * an agent's quantized KV groups with their widths and metadata for handoff;
+ * AgentMem, Abstract: per-agent 4-bit caches persisted and reloaded).  The
+ * image concatenates, in this order: the K block payloads (block j is
+ * kvq_block_bytes(bits[j], H, D) bytes, j < n_blocks, no padding), the V
+ * block payloads (absent for a latent cache), the K window rows bf16
+ * [n_window][H][D], the V window rows (absent for a latent cache), the rope
+ * rows bf16 [64*n_blocks + n_window][H][rope_dim] (absent when rope_dim is 0),
+ * and the widths uint8 [n_blocks].  Every segment but the last is a multiple
+ * of 128 bytes.
+ *
+ * kvq_card_bytes: the image size for these counts, from host copies of the
+ * sequence's widths (bits_host [n_blocks]); 0 for unsupported arguments. */
+uint64_t kvq_card_bytes(int32_t n_heads, int32_t head_dim, int32_t rope_dim, int32_t has_v,
+                        int32_t n_blocks, const uint8_t *bits_host, int32_t n_window);
+
+/* Gather sequence seq of the cache into image (device memory, 16-byte
+ * aligned), with the counts and widths the device tables hold.  Bytes past
+ * image_bytes are not written.  V NULL: latent cache.  rope as in
+ * kvq_attend_decode (rows by token position).
+ * Errors: KVQ_EINVAL, KVQ_EUNSUPPORTED (rope_dim), KVQ_EHIP. */
+int kvq_card_gather(const kvq_layout *L, const kvq_store *K, const kvq_store *V, const uint16_t *rope,
+                    int32_t rope_dim, int32_t seq, void *image, uint64_t image_bytes, void *stream);
+
+/* Scatter an image back into sequence seq: the caller first sets the
+ * sequence's counts and widths (and pool offsets sized for those widths) in
+ * the device tables to the card's; the image's own width segment is not read.
+ * Bytes past image_bytes are not read.
+ * Errors: KVQ_EINVAL, KVQ_EUNSUPPORTED (rope_dim), KVQ_EHIP. */
+int kvq_card_scatter(const kvq_layout *L, const kvq_store *K, const kvq_store *V, uint16_t *rope,
+                     int32_t rope_dim, int32_t seq, const void *image, uint64_t image_bytes, void *stream);
+
 /* Workspace bytes kvq_attend_decode needs for this layout and head count
  * (written to *bytes).  Errors: KVQ_EINVAL, KVQ_EUNSUPPORTED. */
 int kvq_decode_workspace(const kvq_layout *L, int32_t n_q_heads, int32_t rope_dim, size_t *bytes);

@@ -296,5 +296,26 @@ def append_seq(k_pool, v_pool, bits, k_offset, v_offset, n_blocks, k_window, v_w
     return nb_out.value, nw_out.value
 
 
+def card_image(pool, bits, k_offset, v_offset, k_window, v_window, rope, n_heads, head_dim) -> np.ndarray:
+    """A sequence's CacheCard image, by concatenation: K block payloads, V
+    block payloads (v_offset None: latent), K window rows, V window rows,
+    rope rows by token position, widths (uint8)."""
+    bits = np.asarray(bits, np.uint8)
+    parts = []
+    for off in (k_offset, v_offset):
+        if off is None:
+            continue
+        for j, b in enumerate(bits):
+            o = int(off[j])
+            parts.append(pool[o:o + block_bytes(int(b), n_heads, head_dim)])
+    for w in (k_window, v_window):
+        if w is not None:
+            parts.append(np.ascontiguousarray(w, np.uint16).view(np.uint8).ravel())
+    if rope is not None:
+        parts.append(np.ascontiguousarray(rope, np.uint16).view(np.uint8).ravel())
+    parts.append(bits)
+    return np.concatenate([np.asarray(p, np.uint8).ravel() for p in parts])
+
+
 def max_threads() -> int:
     return int(lib().kvq_ref_max_threads())

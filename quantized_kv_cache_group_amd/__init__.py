@@ -24,8 +24,9 @@ KVQ_OK, KVQ_EINVAL, KVQ_ENOSPC, KVQ_EUNSUPPORTED, KVQ_EHIP = 0, -1, -2, -3, -4
 OUT_BF16, OUT_F32 = 0, 1
 WIDTHS = (2, 3, 4, 8)
 
-SYMBOLS = ("kvq_block_bytes", "kvq_quantize", "kvq_append", "kvq_dequantize", "kvq_decode_workspace",
-           "kvq_attend_decode", "kvq_chunk_workspace", "kvq_attend_chunk", "kvq_strerror")
+SYMBOLS = ("kvq_block_bytes", "kvq_quantize", "kvq_append", "kvq_dequantize", "kvq_card_bytes",
+           "kvq_card_gather", "kvq_card_scatter", "kvq_decode_workspace", "kvq_attend_decode",
+           "kvq_chunk_workspace", "kvq_attend_chunk", "kvq_strerror")
 
 
 class KVQError(RuntimeError):
@@ -64,6 +65,13 @@ def lib() -> ctypes.CDLL:
         L.kvq_quantize.restype = ctypes.c_int
         L.kvq_append.argtypes = [P, P, P, P, P, P, P, i32, i32, i32, P, P, P]
         L.kvq_append.restype = ctypes.c_int
+        u64 = ctypes.c_uint64
+        L.kvq_card_bytes.argtypes = [i32, i32, i32, i32, i32, P, i32]
+        L.kvq_card_bytes.restype = u64
+        L.kvq_card_gather.argtypes = [P, P, P, P, i32, i32, P, u64, P]
+        L.kvq_card_gather.restype = ctypes.c_int
+        L.kvq_card_scatter.argtypes = [P, P, P, P, i32, i32, P, u64, P]
+        L.kvq_card_scatter.restype = ctypes.c_int
         L.kvq_dequantize.argtypes = [P, P, i32, P, ctypes.c_int64, P]
         L.kvq_dequantize.restype = ctypes.c_int
         L.kvq_decode_workspace.argtypes = [P, i32, i32, ctypes.POINTER(sz)]
@@ -158,6 +166,7 @@ class LayerCache:
                 raise ValueError("unsupported width or head_dim")
             pos += _round_up(nb, 256)
         self.offset_host = off
+        self.slots_host = [self.max_blocks if future_bits is not None else n for n in self.n_blocks_host]
         self.pool_bytes = max(pos, 256)
         dev = torch.device(device)
         self.n_blocks = torch.tensor(self.n_blocks_host, dtype=torch.int32, device=dev)
@@ -229,6 +238,43 @@ class LayerCache:
             k = min(k, self.max_blocks - nb)
             self.n_blocks_host[a] = nb + k
             self.n_window_host[a] = min(total - 64 * k, self.window_cap)
+
+    # ---- CacheCards (one sequence as a safetensors-compatible file) --------
+    def card_bytes(self, seq: int) -> int:
+        nb = self.n_blocks_host[seq]
+        bits = np.ascontiguousarray(self.bits_host[seq, :nb])
+        return int(lib().kvq_card_bytes(self.H, self.D, self.rope_dim, 0 if self.latent else 1, nb,
+                                        bits.ctypes.data_as(ctypes.c_void_p), self.n_window_host[seq]))
+
+    def card_gather(self, seq: int, image: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+        """Device image (uint8) of sequence seq."""
+        n = self.card_bytes(seq)
+        if image is None:
+            image = torch.empty(max(n, 16), dtype=torch.uint8, device=self.k_pool.device)
+        kst, vst = self.store("k"), self.store("v")
+        _check(lib().kvq_card_gather(ctypes.byref(self._layout), ctypes.byref(kst),
+                                     None if vst is None else ctypes.byref(vst), _ptr(self.rope),
+                                     self.rope_dim, seq, _ptr(image), n, _stream(stream)), "kvq_card_gather")
+        return image[:n]
+
+    def card_scatter(self, seq: int, image: torch.Tensor, n_blocks: int, n_window: int, bits,
+                     stream=None):
+        """Load a device image into sequence seq, whose pool slots must have been
+        allocated with exactly these widths."""
+        bits = np.asarray(bits, np.uint8)
+        if n_blocks > self.slots_host[seq] or n_window > self.window_cap or bits.size != n_blocks:
+            raise ValueError("card does not fit this sequence's slots")
+        if not np.array_equal(self.bits_host[seq, :n_blocks], bits):
+            raise ValueError("card widths differ from this sequence's slot widths")
+        self.n_blocks_host[seq], self.n_window_host[seq] = int(n_blocks), int(n_window)
+        self.n_blocks[seq] = int(n_blocks)
+        self.n_window[seq] = int(n_window)
+        assert image.dtype == torch.uint8 and image.is_contiguous()
+        kst, vst = self.store("k"), self.store("v")
+        _check(lib().kvq_card_scatter(ctypes.byref(self._layout), ctypes.byref(kst),
+                                      None if vst is None else ctypes.byref(vst), _ptr(self.rope),
+                                      self.rope_dim, seq, _ptr(image), image.numel(), _stream(stream)),
+               "kvq_card_scatter")
 
     def dequantize(self, which: str, out: torch.Tensor, stream=None):
         """Restore into out [A][S][H][D] (bf16 or fp32), S >= 64*max_blocks + window_cap."""

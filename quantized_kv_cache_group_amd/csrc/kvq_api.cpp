@@ -216,6 +216,57 @@ int kvq_append(const kvq_layout *L, const kvq_store *K, const kvq_store *V,
     return hip_status(launch_append(a, static_cast<hipStream_t>(stream)));
 }
 
+uint64_t kvq_card_bytes(int32_t n_heads, int32_t head_dim, int32_t rope_dim, int32_t has_v,
+                        int32_t n_blocks, const uint8_t *bits_host, int32_t n_window)
+{
+    if (n_heads < 1 || head_dim < 64 || head_dim % 64 || head_dim > 512) return 0;
+    if (rope_dim != 0 && rope_dim != 64) return 0;
+    if (n_blocks < 0 || n_window < 0 || (n_blocks > 0 && !bits_host)) return 0;
+    const int n_kv = has_v ? 2 : 1;
+    uint64_t blocks = 0;
+    for (int j = 0; j < n_blocks; j++) {
+        const uint64_t b = kvq_block_bytes(bits_host[j], n_heads, head_dim);
+        if (!b) return 0;
+        blocks += b;
+    }
+    const uint64_t row = (uint64_t)n_heads * head_dim * 2;
+    return n_kv * blocks + n_kv * (uint64_t)n_window * row +
+           (uint64_t)(64 * (uint64_t)n_blocks + n_window) * n_heads * rope_dim * 2 + (uint64_t)n_blocks;
+}
+
+namespace {
+int card_call(const kvq_layout *L, const kvq_store *K, const kvq_store *V, uint16_t *rope, int32_t rope_dim,
+              int32_t seq, uint8_t *image, uint64_t image_bytes, int to_image, void *stream)
+{
+    int st = check_layout(L);
+    if (st) return st;
+    if ((st = check_store(L, K))) return st;
+    if (V && (st = check_store(L, V))) return st;
+    if (seq < 0 || seq >= L->n_seqs) return KVQ_EINVAL;
+    if (rope_dim != 0 && rope_dim != 64) return KVQ_EUNSUPPORTED;
+    if (rope_dim && (!rope || !aligned(rope, 16))) return KVQ_EINVAL;
+    if (!image || !aligned(image, 16)) return KVQ_EINVAL;
+    return hip_status(launch_card(tables(L), K->offset, V ? V->offset : nullptr, K->pool, V ? V->pool : nullptr,
+                                  L->window_cap > 0 ? K->window : nullptr,
+                                  (V && L->window_cap > 0) ? V->window : nullptr, rope_dim ? rope : nullptr,
+                                  rope_dim, seq, image, image_bytes, to_image, static_cast<hipStream_t>(stream)));
+}
+}  // namespace
+
+int kvq_card_gather(const kvq_layout *L, const kvq_store *K, const kvq_store *V, const uint16_t *rope,
+                    int32_t rope_dim, int32_t seq, void *image, uint64_t image_bytes, void *stream)
+{
+    return card_call(L, K, V, const_cast<uint16_t *>(rope), rope_dim, seq, static_cast<uint8_t *>(image),
+                     image_bytes, 1, stream);
+}
+
+int kvq_card_scatter(const kvq_layout *L, const kvq_store *K, const kvq_store *V, uint16_t *rope,
+                     int32_t rope_dim, int32_t seq, const void *image, uint64_t image_bytes, void *stream)
+{
+    return card_call(L, K, V, rope, rope_dim, seq, const_cast<uint8_t *>(static_cast<const uint8_t *>(image)),
+                     image_bytes, 0, stream);
+}
+
 int kvq_dequantize(const kvq_layout *L, const kvq_store *src, int32_t out_dtype, void *dst,
                    int64_t dst_seq_tokens, void *stream)
 {

@@ -107,6 +107,11 @@ struct AppendArgs {
     int32_t *n_blocks_out, *n_window_out;
 };
 
+// CacheCard image of one sequence: to_image 1 gathers, 0 scatters.
+hipError_t launch_card(const Tables &t, const uint64_t *k_offset, const uint64_t *v_offset, uint8_t *k_pool,
+                       uint8_t *v_pool, uint16_t *k_window, uint16_t *v_window, uint16_t *rope, int rope_dim,
+                       int seq, uint8_t *image, uint64_t image_bytes, int to_image, hipStream_t s);
+
 // Launchers (return hipError_t of the launch).
 hipError_t launch_quantize(const QuantArgs &a, hipStream_t s);
 hipError_t launch_append(const AppendArgs &a, hipStream_t s);          // blocks, window, counts
