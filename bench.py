@@ -45,6 +45,9 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--copy-calibration", action="store_true",
                    help="only run a plain 1 GiB device copy (the reference for the HBM byte counters)")
+    p.add_argument("--topk", type=int, default=0, metavar="K",
+                   help="time top-K sparse decode (K of 64 blocks per agent) on the Llama 10-agent "
+                        "caches, beside the full decode, instead of the workload step")
     p.add_argument("--card", action="store_true",
                    help="time CacheCard gather and scatter of the Llama 10-agent caches "
                         "(device image <-> cache) instead of the workload step")
@@ -305,6 +308,68 @@ def append_bench(args):
     print(json.dumps(res), flush=True)
 
 
+def topk_bench(args):
+    """Top-K sparse decode on the Llama-3.1-8B layer shape, 10 agents x 4096
+    Q4 tokens (64 blocks each): block scores over every K block, selection,
+    then decode over the K kept blocks; timed beside the full decode of the
+    same caches.  Algorithmic bytes: all K blocks (scores), the kept blocks'
+    K and V again, q and out.  Cache copies rotate past the 256 MB cache."""
+    import torch
+    import kvq_synth as syn
+    import quantized_kv_cache_group_amd as kvq
+
+    kvq.lib()
+    torch.cuda.set_device(0)
+    w = syn.workload(1)
+    A, H, D, Hq, K = w.n_agents, w.n_kv_heads, w.head_dim, w.n_q_heads, args.topk
+    blk = kvq.block_bytes(4, H, D)
+    one = 2 * A * w.n_blocks[0] * blk
+    R = min(12, max(2, int(np.ceil(2 * MALL_BYTES / one)) + 1))
+    caches = [kvq.LayerCache(H, D, w.n_blocks, w.n_window, None) for _ in range(R)]
+    g = torch.Generator(device="cuda")
+    g.manual_seed(5)
+    src = [torch.randn((A, 4096, H, D), generator=g, device="cuda").to(torch.bfloat16) for _ in range(2)]
+    for i, c in enumerate(caches):
+        c.quantize("k", src[i % 2])
+        c.quantize("v", src[(i + 1) % 2])
+    q = torch.randn((A, Hq, D), generator=g, device="cuda").to(torch.bfloat16)
+    out = torch.empty((A, Hq, D), dtype=torch.float32, device="cuda")
+    ws = torch.empty(max(caches[0].topk_workspace_bytes(Hq, K), caches[0].decode_workspace_bytes(Hq)),
+                     dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def run(sparse, steps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for i in range(steps):
+            c = caches[i % R]
+            if sparse:
+                c.attend_decode_topk(q, w.scale, K, out=out, workspace=ws)
+            else:
+                c.attend_decode(q, w.scale, out=out, workspace=ws)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / steps
+    run(True, args.warmup)
+    sp_us = run(True, args.steps)
+    run(False, args.warmup)
+    full_us = run(False, args.steps)
+    kb = min(K, w.n_blocks[0])
+    algo = A * (w.n_blocks[0] * blk + 2 * kb * blk) + A * Hq * D * 2 + A * Hq * D * 4
+    gbs = algo / (sp_us * 1e-6) / 1e9
+    res = {"metric": "top-K sparse decode GB/s", "value": round(gbs, 2), "unit": "GB/s", "n_gpus": 1,
+           "steps": args.steps, "warmup": args.warmup, "higher_is_better": True, "dtype": "f32",
+           "data": "synthetic",
+           "config": {"workload": f"llama8b-10agent-q4-top{K}", "agents": A, "q_heads": Hq, "kv_heads": H,
+                      "head_dim": D, "blocks": w.n_blocks[0], "top_k": K, "bits": 4, "rotated_copies": R},
+           "sparse_us": round(sp_us, 3), "full_decode_us": round(full_us, 3),
+           "speedup_vs_full": round(full_us / sp_us, 3), "bytes_per_call": algo,
+           "roofline": {"kernel": "kvq attend_decode_topk", "bound": "hbm", "achieved": round(gbs, 2),
+                        "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
+                        "traffic": None}}
+    print(json.dumps(res), flush=True)
+
+
 def card_bench(args):
     """CacheCard gather (cache -> contiguous device image) and scatter (image
     -> cache) for each of the 10 agents of the Llama-3.1-8B layer shape (4096
@@ -380,6 +445,9 @@ def main():
     args = parse()
     if args.card:
         card_bench(args)
+        return
+    if args.topk:
+        topk_bench(args)
         return
     if args.copy_calibration:
         copy_calibration()

@@ -217,6 +217,34 @@ int kvq_attend_decode(const kvq_layout *L, const kvq_store *K, const kvq_store *
                       int32_t n_q_heads, float softmax_scale, float *out,
                       void *workspace, size_t workspace_bytes, void *stream);
 
+/* Workspace bytes kvq_attend_decode_topk needs (written to *bytes).
+ * Errors: KVQ_EINVAL, KVQ_EUNSUPPORTED. */
+int kvq_topk_workspace(const kvq_layout *L, int32_t n_q_heads, int32_t rope_dim, int32_t top_k,
+                       size_t *bytes);
+
+/* Sparse decode over the top-K blocks (Reasoning-Aware Error-Bounded
+ * KV-Cache Compression and Sparse Attention for Long-Context LLMs, section 2C:
+ * the active set is the top-K entries by a query-aware score built on the
+ * query-key compatibility; section 2B: the output then differs from full
+ * attention by at most 2 * max_t |v_t| * (attention mass left out)).
+ * For each sequence a, block j < n_blocks[a] scores
+ *     max over its 64 tokens t and the sequence's query heads h of
+ *     softmax_scale * <q[a][h], k_t of KV head h / G>
+ * (restored keys, plus the rope dims when rope_dim is 64, in fp32).  The
+ * min(top_k, n_blocks[a]) highest-scoring blocks (equal scores: lower index
+ * first) and the whole bf16 window form the active set; the result is
+ * kvq_attend_decode restricted to it (the same kernels run over a compacted
+ * copy of the tables in the workspace).
+ *   selected  NULL or device int32 [A][top_k]: the kept block indices in
+ *             ascending order, -1 past min(top_k, n_blocks[a]).
+ *   top_k >= 1; max_blocks <= 16384; (n_q_heads/H) * (head_dim + rope_dim)
+ *   <= 9216.  Other arguments as for kvq_attend_decode.
+ * Errors: KVQ_EINVAL, KVQ_ENOSPC, KVQ_EUNSUPPORTED, KVQ_EHIP. */
+int kvq_attend_decode_topk(const kvq_layout *L, const kvq_store *K, const kvq_store *V,
+                           const uint16_t *rope, int32_t rope_dim, const uint16_t *q,
+                           int32_t n_q_heads, float softmax_scale, int32_t top_k, float *out,
+                           int32_t *selected, void *workspace, size_t workspace_bytes, void *stream);
+
 /* Workspace bytes kvq_attend_chunk needs (written to *bytes). */
 int kvq_chunk_workspace(const kvq_layout *L, int32_t n_q_heads, int32_t n_new, size_t *bytes);
 

@@ -81,6 +81,8 @@ def lib() -> ctypes.CDLL:
         L.kvq_ref_append_seq.argtypes = [P, P, P, P, P, i32, i32, P, P, i32, i32, i32, i32, P, P, i32,
                                          i32, P, P, i32, P, P]
         L.kvq_ref_append_seq.restype = i32
+        L.kvq_ref_block_scores_seq.argtypes = [P, P, P, i32, P, i32, i32, i32, P, i32, ctypes.c_double, P]
+        L.kvq_ref_block_scores_seq.restype = i32
         L.kvq_ref_max_threads.argtypes = []
         L.kvq_ref_max_threads.restype = i32
         _lib = L
@@ -315,6 +317,32 @@ def card_image(pool, bits, k_offset, v_offset, k_window, v_window, rope, n_heads
         parts.append(np.ascontiguousarray(rope, np.uint16).view(np.uint8).ravel())
     parts.append(bits)
     return np.concatenate([np.asarray(p, np.uint8).ravel() for p in parts])
+
+
+def block_scores_seq(pool, bits, k_offset, rope, n_kv_heads, head_dim, q_bf16, scale) -> np.ndarray:
+    """fp64 score of each block: max over its tokens and the query heads of
+    scale * <q, k> (restored keys, plus rope dims)."""
+    bits = _c(bits, np.uint8)
+    k_offset = _c(k_offset, np.uint64)
+    nb = bits.size
+    rope = _c(rope, np.uint16)
+    rope_dim = 0 if rope is None else rope.size // max(1, 64 * nb * n_kv_heads)
+    q = _c(q_bf16, np.uint16)
+    Hq = q.size // (head_dim + rope_dim)
+    out = np.zeros(nb, np.float64)
+    rc = lib().kvq_ref_block_scores_seq(_p(pool), _p(bits), _p(k_offset), nb, _p(rope), rope_dim,
+                                        n_kv_heads, head_dim, _p(q), Hq, float(scale), _p(out))
+    if rc:
+        raise ValueError("kvq_ref_block_scores_seq failed")
+    return out
+
+
+def topk_blocks(scores, k: int) -> np.ndarray:
+    """Indices (ascending) of the min(k, n) highest scores; equal scores
+    rank the lower index first."""
+    s = np.asarray(scores, np.float64)
+    order = sorted(range(s.size), key=lambda i: (-s[i], i))
+    return np.array(sorted(order[:min(k, s.size)]), np.int64)
 
 
 def max_threads() -> int:

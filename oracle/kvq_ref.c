@@ -503,3 +503,37 @@ int kvq_ref_attend_chunk_seq(const uint8_t *pool, const uint8_t *bits,
     free(V);
     return 0;
 }
+
+int kvq_ref_block_scores_seq(const uint8_t *pool, const uint8_t *bits, const uint64_t *k_offset,
+                             int n_blocks, const uint16_t *rope, int rope_dim, int n_kv_heads,
+                             int head_dim, const uint16_t *q, int n_q_heads, double scale,
+                             double *scores)
+{
+    if (!dims_ok(n_kv_heads, head_dim) || n_blocks < 0 || n_q_heads < 1 || n_q_heads % n_kv_heads) return -1;
+    const int G = n_q_heads / n_kv_heads, dk = head_dim + rope_dim;
+    const size_t T = (size_t)64 * n_blocks;
+    float *K = malloc((T + 1) * n_kv_heads * head_dim * sizeof(float));
+    if (!K) return -1;
+    int rc = kvq_ref_restore_seq(pool, bits, k_offset, n_blocks, NULL, 0, n_kv_heads, head_dim, K);
+    if (rc) { free(K); return rc; }
+    for (int j = 0; j < n_blocks; j++) {
+        double best = -INFINITY;
+        for (int t = 64 * j; t < 64 * j + 64; t++) {
+            for (int h = 0; h < n_q_heads; h++) {
+                const int g = h / G;
+                const float *k = K + ((size_t)t * n_kv_heads + g) * head_dim;
+                const uint16_t *qh = q + (size_t)h * dk;
+                double dot = 0.0;
+                for (int d = 0; d < head_dim; d++) dot += (double)kvq_ref_bf16_to_f32(qh[d]) * (double)k[d];
+                for (int d = 0; d < rope_dim; d++)
+                    dot += (double)kvq_ref_bf16_to_f32(qh[head_dim + d]) *
+                           (double)kvq_ref_bf16_to_f32(rope[((size_t)t * n_kv_heads + g) * rope_dim + d]);
+                const double sc = scale * dot;
+                if (sc > best) best = sc;
+            }
+        }
+        scores[j] = best;
+    }
+    free(K);
+    return 0;
+}

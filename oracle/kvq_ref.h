@@ -154,6 +154,20 @@ int kvq_ref_attend_chunk_seq(const uint8_t *pool, const uint8_t *bits,
                              int n_new, int n_q_heads, float scale,
                              int row_begin, int row_end, float *out);
 
+/* Block scores for top-K sparse decode (Reasoning-Aware Error-Bounded
+ * KV-Cache Compression and Sparse Attention for Long-Context LLMs, section
+ * 2C: the active set is the top-K entries by a score built on the
+ * instantaneous query-key compatibility).  The entry is a 64-token block; its
+ * score is the largest scale * <q_h, k_t> over the block's tokens t and all
+ * query heads h (query head h reads KV head h / (n_q_heads / n_kv_heads)),
+ * with the restored keys of kvq_ref_restore_seq and, if rope_dim > 0, the
+ * rope dims (rope [64*n_blocks][H][rope_dim], q rows of head_dim + rope_dim).
+ * fp64.  scores[n_blocks]. */
+int kvq_ref_block_scores_seq(const uint8_t *pool, const uint8_t *bits, const uint64_t *k_offset,
+                             int n_blocks, const uint16_t *rope, int rope_dim, int n_kv_heads,
+                             int head_dim, const uint16_t *q, int n_q_heads, double scale,
+                             double *scores);
+
 /* Threads the OpenMP runtime uses for the parallel loops (1 without OpenMP). */
 int kvq_ref_max_threads(void);
 

@@ -26,7 +26,8 @@ WIDTHS = (2, 3, 4, 8)
 
 SYMBOLS = ("kvq_block_bytes", "kvq_quantize", "kvq_append", "kvq_dequantize", "kvq_card_bytes",
            "kvq_card_gather", "kvq_card_scatter", "kvq_decode_workspace", "kvq_attend_decode",
-           "kvq_chunk_workspace", "kvq_attend_chunk", "kvq_strerror")
+           "kvq_topk_workspace", "kvq_attend_decode_topk", "kvq_chunk_workspace", "kvq_attend_chunk",
+           "kvq_strerror")
 
 
 class KVQError(RuntimeError):
@@ -78,6 +79,10 @@ def lib() -> ctypes.CDLL:
         L.kvq_decode_workspace.restype = ctypes.c_int
         L.kvq_attend_decode.argtypes = [P, P, P, P, i32, P, i32, f32, P, P, sz, P]
         L.kvq_attend_decode.restype = ctypes.c_int
+        L.kvq_topk_workspace.argtypes = [P, i32, i32, i32, ctypes.POINTER(sz)]
+        L.kvq_topk_workspace.restype = ctypes.c_int
+        L.kvq_attend_decode_topk.argtypes = [P, P, P, P, i32, P, i32, f32, i32, P, P, P, sz, P]
+        L.kvq_attend_decode_topk.restype = ctypes.c_int
         L.kvq_chunk_workspace.argtypes = [P, i32, i32, ctypes.POINTER(sz)]
         L.kvq_chunk_workspace.restype = ctypes.c_int
         L.kvq_attend_chunk.argtypes = [P, P, P, P, P, P, i32, i32, f32, P, P, sz, P]
@@ -313,6 +318,36 @@ class LayerCache:
                                        _ptr(self.rope), self.rope_dim, _ptr(q), Hq, float(scale),
                                        _ptr(out), _ptr(workspace), workspace.numel(),
                                        _stream(stream)), "kvq_attend_decode")
+        return out
+
+    def topk_workspace_bytes(self, n_q_heads: int, top_k: int) -> int:
+        n = ctypes.c_size_t(0)
+        _check(lib().kvq_topk_workspace(ctypes.byref(self._layout), n_q_heads, self.rope_dim, top_k,
+                                        ctypes.byref(n)), "kvq_topk_workspace")
+        return int(n.value)
+
+    def attend_decode_topk(self, q: torch.Tensor, scale: float, top_k: int, out: torch.Tensor | None = None,
+                           selected: torch.Tensor | None = None, workspace: torch.Tensor | None = None,
+                           stream=None) -> torch.Tensor:
+        """Decode over the top_k highest-scoring blocks of each sequence plus its
+        window.  q bf16 [A][Hq][D + rope_dim] -> fp32 [A][Hq][D]; ``selected``
+        (int32 [A][top_k]) receives the kept block indices."""
+        assert q.dtype == torch.bfloat16 and q.is_contiguous() and q.shape[0] == self.A
+        Hq = q.shape[1]
+        if out is None:
+            out = torch.empty((self.A, Hq, self.D), dtype=torch.float32, device=q.device)
+        if workspace is None:
+            workspace = torch.empty(max(self.topk_workspace_bytes(Hq, top_k), 256), dtype=torch.uint8,
+                                    device=q.device)
+        if selected is not None:
+            assert selected.dtype == torch.int32 and selected.is_contiguous()
+            assert selected.numel() >= self.A * top_k
+        kst, vst = self.store("k"), self.store("v")
+        _check(lib().kvq_attend_decode_topk(ctypes.byref(self._layout), ctypes.byref(kst),
+                                            None if vst is None else ctypes.byref(vst), _ptr(self.rope),
+                                            self.rope_dim, _ptr(q), Hq, float(scale), int(top_k), _ptr(out),
+                                            _ptr(selected), _ptr(workspace), workspace.numel(),
+                                            _stream(stream)), "kvq_attend_decode_topk")
         return out
 
     def attend_chunk(self, q_new: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor,

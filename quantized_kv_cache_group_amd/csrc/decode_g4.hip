@@ -301,21 +301,31 @@ __device__ __forceinline__ void dots_phase(f4 (&T)[NG], const h4 (*qs)[4], const
 // scores: sum_g s (T - 1024 Q_g) + b Q_g, with token 4b+r's (s, b) from km;
 // returns P' = fp16(p s_v) per group and adds the bias and P' sums.
 template <int NG>
-__device__ __forceinline__ void score_phase(State<NG> &st, h4 (&pg)[NG], const f4 (&T)[NG], const uint32_t *km,
-                                            const uint32_t *vm, const float (&qg)[NG], float c)
+__device__ __forceinline__ f4 scores_of(const f4 (&T)[NG], const uint32_t *km, const float (&qg)[NG])
 {
     f4 s = {0.f, 0.f, 0.f, 0.f};
-    f2 vsb[NG][4];
 #pragma unroll
     for (int gg = 0; gg < NG; gg++) {
         const float q1024 = 1024.0f * qg[gg];
 #pragma unroll
         for (int r = 0; r < 4; r++) {
             const f2 ksb = meta_of(quad_bcast(km[gg], r));
-            vsb[gg][r] = meta_of(quad_bcast(vm[gg], r));
             s[r] = __builtin_fmaf(ksb[0], T[gg][r] - q1024, __builtin_fmaf(ksb[1], qg[gg], s[r]));
         }
     }
+    return s;
+}
+
+template <int NG>
+__device__ __forceinline__ void score_phase(State<NG> &st, h4 (&pg)[NG], const f4 (&T)[NG], const uint32_t *km,
+                                            const uint32_t *vm, const float (&qg)[NG], float c)
+{
+    const f4 s = scores_of<NG>(T, km, qg);
+    f2 vsb[NG][4];
+#pragma unroll
+    for (int gg = 0; gg < NG; gg++)
+#pragma unroll
+        for (int r = 0; r < 4; r++) vsb[gg][r] = meta_of(quad_bcast(vm[gg], r));
     const h4 p = softmax_round<NG>(st, s, 64, c);
     const f4 pf = {(float)p[0], (float)p[1], (float)p[2], (float)p[3]};
 #pragma unroll
@@ -383,6 +393,40 @@ __device__ __forceinline__ void round_window(State<NG> &st, const h4 (*qs)[4], c
     pv_round<NG>(st, [&](int) { return p; }, vr, [&](int cidx) { return bf16_pairs(vrow[cidx]); });
 }
 
+// Query rows of KV head g's G heads, fp16, in the unpack order of the key
+// chunks, into qs; and Q_g of head j: the sum of its fp16 query over each
+// 64-dim group (lane (b, j) adds slice 16g + b, then the 16 lanes of head j
+// combine).
+template <int NG>
+__device__ __forceinline__ void stage_query(const DecodeArgs &p, int a, int g, h4 (*qs)[4], float (&qg)[NG])
+{
+    constexpr int D = 64 * NG, NCH = 8 * NG;
+    const int lane = threadIdx.x, b = lane >> 2, j = lane & 3;
+    for (int e = lane; e < 4 * NCH; e += 64) {
+        const int h = e / NCH, cc = e % NCH;
+        Pairs pr;
+        if (h < p.G) {
+            const uint4 v = *reinterpret_cast<const uint4 *>(p.q + ((size_t)a * p.Hq + g * p.G + h) * D + 8 * cc);
+            pr = bf16_pairs(v);
+        } else {
+            pr.p[0] = pr.p[1] = pr.p[2] = pr.p[3] = h2{(_Float16)0.0f, (_Float16)0.0f};
+        }
+        qs[2 * cc][h] = h4{pr.p[0][0], pr.p[0][1], pr.p[1][0], pr.p[1][1]};
+        qs[2 * cc + 1][h] = h4{pr.p[2][0], pr.p[2][1], pr.p[3][0], pr.p[3][1]};
+    }
+    wave_sync();
+    const h2 ones = {(_Float16)1.0f, (_Float16)1.0f};
+#pragma unroll
+    for (int gg = 0; gg < NG; gg++) {
+        const h4 v = qs[16 * gg + b][j];
+        float acc = __builtin_amdgcn_fdot2(h2{v[2], v[3]}, ones, __builtin_amdgcn_fdot2(h2{v[0], v[1]}, ones, 0.0f, false),
+                                           false);
+#pragma unroll
+        for (int o = 4; o < 64; o <<= 1) acc += __shfl_xor(acc, o);
+        qg[gg] = acc;
+    }
+}
+
 template <int NG>
 __global__ __launch_bounds__(64, (NG <= 2 ? 3 : 2)) void decode_g4_split(DecodeArgs p)
 {
@@ -402,33 +446,8 @@ __global__ __launch_bounds__(64, (NG <= 2 ? 3 : 2)) void decode_g4_split(DecodeA
     const int j0 = s * p.SB, j1 = min(j0 + p.SB, nb);
     if (!win) split_meta(sm, p, a, j0, j1);
 
-    // Query rows of the G heads, fp16, in the unpack order of the key chunks.
-    for (int e = lane; e < 4 * NCH; e += 64) {
-        const int h = e / NCH, cc = e % NCH;
-        Pairs pr;
-        if (h < p.G) {
-            const uint4 v = *reinterpret_cast<const uint4 *>(p.q + ((size_t)a * p.Hq + g * p.G + h) * D + 8 * cc);
-            pr = bf16_pairs(v);
-        } else {
-            pr.p[0] = pr.p[1] = pr.p[2] = pr.p[3] = h2{(_Float16)0.0f, (_Float16)0.0f};
-        }
-        qs[2 * cc][h] = h4{pr.p[0][0], pr.p[0][1], pr.p[1][0], pr.p[1][1]};
-        qs[2 * cc + 1][h] = h4{pr.p[2][0], pr.p[2][1], pr.p[3][0], pr.p[3][1]};
-    }
-    wave_sync();
-    // Q_g of head j: the sum of its fp16 query over each 64-dim group (lane
-    // (b, j) adds slice 16g + b, then the 16 lanes of head j combine).
     float qg[NG];
-    const h2 ones = {(_Float16)1.0f, (_Float16)1.0f};
-#pragma unroll
-    for (int gg = 0; gg < NG; gg++) {
-        const h4 v = qs[16 * gg + b][j];
-        float acc = __builtin_amdgcn_fdot2(h2{v[2], v[3]}, ones, __builtin_amdgcn_fdot2(h2{v[0], v[1]}, ones, 0.0f, false),
-                                           false);
-#pragma unroll
-        for (int o = 4; o < 64; o <<= 1) acc += __shfl_xor(acc, o);
-        qg[gg] = acc;
-    }
+    stage_query<NG>(p, a, g, qs, qg);
 
     State<NG> st;
 #pragma unroll
@@ -501,6 +520,60 @@ __global__ __launch_bounds__(64, (NG <= 2 ? 3 : 2)) void decode_g4_split(DecodeA
     }
 }
 
+// Block scores for top-K selection: the Q.K products and scale/bias
+// corrections of the decode above, then the largest score of the block over
+// its 64 tokens and the KV head's G query heads, times the softmax scale.
+// One wave per (split, KV head, sequence); scores_h [A][max_blocks][H].
+template <int B, int NG>
+__device__ __forceinline__ float block_max(const h4 (*qs)[4], const float (&qg)[NG], const uint8_t *kblk, int H,
+                                           int g, int G)
+{
+    constexpr uint32_t CODE_ROW = 8 * NG * B;
+    const uint32_t row = (uint32_t)g * 64 + threadIdx.x;
+    const uint32_t moff = (uint32_t)H * 64 * CODE_ROW + 4 * NG * row;
+    uint32_t kw[FullRow<B, NG>::NDW], km[NG];
+    FullRow<B, NG>::load(kw, kblk + row * CODE_ROW);
+#pragma unroll
+    for (int i = 0; i < NG; i++) km[i] = reinterpret_cast<const uint32_t *>(kblk + moff)[i];
+    f4 T[NG];
+    dots_phase<B, NG>(T, qs, kw);
+    const f4 s = scores_of<NG>(T, km, qg);
+    float m = ((int)(threadIdx.x & 3) < G) ? fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3])) : -INFINITY;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) m = fmaxf(m, __shfl_xor(m, o));
+    return m;
+}
+
+template <int NG>
+__global__ __launch_bounds__(64, (NG <= 2 ? 3 : 2)) void decode_g4_scores(DecodeArgs p, float scale, float *scores_h)
+{
+    constexpr int NCH = 8 * NG;
+    __shared__ __attribute__((aligned(16))) h4 qs[2 * NCH][4];
+    const int s = blockIdx.x, g = blockIdx.y, a = blockIdx.z;
+    const int nb = seq_blocks(p.t, a);
+    const int j0 = s * p.SB, j1 = min(j0 + p.SB, nb);
+    if (j0 >= j1) return;
+    SplitMeta sm;
+    split_meta(sm, p, a, j0, j1);
+    float qg[NG];
+    stage_query<NG>(p, a, g, qs, qg);
+    for (int jb = j0; jb < j1; jb++) {
+        if (jb - sm.base >= 64) split_meta(sm, p, a, jb, j1);   // blocks are visited in order
+        const int i = jb - sm.base;
+        const int bw = __builtin_amdgcn_readlane(sm.bits, i);
+        const uint8_t *kb = p.k.pool + (((uint64_t)(uint32_t)__builtin_amdgcn_readlane(sm.khi, i) << 32) |
+                                        (uint32_t)__builtin_amdgcn_readlane(sm.klo, i));
+        float m;
+        switch (bw) {
+        case 2: m = block_max<2, NG>(qs, qg, kb, p.t.H, g, p.G); break;
+        case 3: m = block_max<3, NG>(qs, qg, kb, p.t.H, g, p.G); break;
+        case 4: m = block_max<4, NG>(qs, qg, kb, p.t.H, g, p.G); break;
+        default: m = block_max<8, NG>(qs, qg, kb, p.t.H, g, p.G); break;
+        }
+        if (threadIdx.x == 0) scores_h[((size_t)a * p.t.max_blocks + jb) * p.t.H + g] = scale * m;
+    }
+}
+
 }  // namespace
 
 bool decode_g4_supported(int D, int G) { return G <= 4 && (D == 64 || D == 128 || D == 256); }
@@ -518,6 +591,20 @@ void decode_g4_plan(int A, int H, int max_blocks, int window_cap, int *SB, int *
     *SB = sb;
     *n_splits = (max_blocks + sb - 1) / sb + (window_cap > 0 ? 1 : 0);
     if (*n_splits < 1) *n_splits = 1;
+}
+
+hipError_t launch_g4_scores(const DecodeArgs &p, float scale, float *scores_h, hipStream_t s)
+{
+    const int nsb = (p.t.max_blocks + p.SB - 1) / p.SB;
+    if (nsb == 0) return hipSuccess;
+    dim3 grid(nsb, p.t.H, p.t.A);
+    switch (p.t.D) {
+    case 64: decode_g4_scores<1><<<grid, 64, 0, s>>>(p, scale, scores_h); break;
+    case 128: decode_g4_scores<2><<<grid, 64, 0, s>>>(p, scale, scores_h); break;
+    case 256: decode_g4_scores<4><<<grid, 64, 0, s>>>(p, scale, scores_h); break;
+    default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
 }
 
 hipError_t launch_decode_g4(const DecodeArgs &p, hipStream_t s)

@@ -235,7 +235,7 @@ uint64_t kvq_card_bytes(int32_t n_heads, int32_t head_dim, int32_t rope_dim, int
 }
 
 namespace {
-int card_call(const kvq_layout *L, const kvq_store *K, const kvq_store *V, uint16_t *rope, int32_t rope_dim,
+static int card_call(const kvq_layout *L, const kvq_store *K, const kvq_store *V, uint16_t *rope, int32_t rope_dim,
               int32_t seq, uint8_t *image, uint64_t image_bytes, int to_image, void *stream)
 {
     int st = check_layout(L);
@@ -376,6 +376,121 @@ int kvq_attend_decode(const kvq_layout *L, const kvq_store *K, const kvq_store *
     a.part = static_cast<float *>(workspace);
     a.out = out;
     return hip_status(launch_attend_generic(a, static_cast<hipStream_t>(stream)));
+}
+
+namespace {
+// Workspace of a top-K call: selection tables, then the decode's own.
+struct TopkWs {
+    size_t scores, n_sel, sel_idx, sel_bits, sel_koff, sel_voff, rope_sel, dec, total;
+    kvq_layout L2;                            // pointers filled in at call time
+    size_t dec_bytes;
+};
+
+static int topk_plan(const kvq_layout *L, int32_t n_q_heads, int32_t rope_dim, int32_t top_k, TopkWs *w)
+{
+    int st = check_layout(L);
+    if (st) return st;
+    if (top_k < 1 || n_q_heads < 1 || n_q_heads % L->n_heads) return KVQ_EINVAL;
+    if (rope_dim != 0 && rope_dim != 64) return KVQ_EUNSUPPORTED;
+    if (!topk_supported(L->max_blocks, n_q_heads / L->n_heads, L->head_dim, rope_dim)) return KVQ_EUNSUPPORTED;
+    const int k = top_k < L->max_blocks ? top_k : (L->max_blocks > 0 ? L->max_blocks : 1);
+    const size_t A = (size_t)L->n_seqs;
+    size_t pos = 0;
+    w->scores = pos;   pos += round256(A * (size_t)(L->max_blocks > 0 ? L->max_blocks : 1) * L->n_heads * 4);
+    w->n_sel = pos;    pos += round256(A * 4);
+    w->sel_idx = pos;  pos += round256(A * (size_t)k * 4);
+    w->sel_bits = pos; pos += round256(A * (size_t)k);
+    w->sel_koff = pos; pos += round256(A * (size_t)k * 8);
+    w->sel_voff = pos; pos += round256(A * (size_t)k * 8);
+    w->rope_sel = pos;
+    pos += round256(A * ((size_t)64 * k + L->window_cap) * L->n_heads * rope_dim * 2);
+    w->L2 = *L;
+    w->L2.max_blocks = k;
+    size_t dec = 0;
+    if ((st = kvq_decode_workspace(&w->L2, n_q_heads, rope_dim, &dec))) return st;
+    w->dec = pos;
+    w->dec_bytes = dec;
+    w->total = pos + dec;
+    return KVQ_OK;
+}
+}  // namespace
+
+int kvq_topk_workspace(const kvq_layout *L, int32_t n_q_heads, int32_t rope_dim, int32_t top_k, size_t *bytes)
+{
+    if (!bytes) return KVQ_EINVAL;
+    TopkWs w;
+    int st = topk_plan(L, n_q_heads, rope_dim, top_k, &w);
+    if (st) return st;
+    *bytes = w.total;
+    return KVQ_OK;
+}
+
+int kvq_attend_decode_topk(const kvq_layout *L, const kvq_store *K, const kvq_store *V,
+                           const uint16_t *rope, int32_t rope_dim, const uint16_t *q,
+                           int32_t n_q_heads, float softmax_scale, int32_t top_k, float *out,
+                           int32_t *selected, void *workspace, size_t workspace_bytes, void *stream)
+{
+    TopkWs w;
+    int st = topk_plan(L, n_q_heads, rope_dim, top_k, &w);
+    if (st) return st;
+    if ((st = check_store(L, K))) return st;
+    if (V && (st = check_store(L, V))) return st;
+    if ((rope_dim > 0) != (rope != nullptr)) return KVQ_EINVAL;
+    if (rope && !aligned(rope, 16)) return KVQ_EINVAL;
+    if (!q || !out || !aligned(q, 16) || !aligned(out, 16)) return KVQ_EINVAL;
+    if (selected && !aligned(selected, 4)) return KVQ_EINVAL;
+    if (!isfinite(softmax_scale)) return KVQ_EINVAL;
+    if (workspace_bytes < w.total) return KVQ_ENOSPC;
+    if (!workspace || !aligned(workspace, 256)) return KVQ_EINVAL;
+    const int k = w.L2.max_blocks;
+    uint8_t *ws = static_cast<uint8_t *>(workspace);
+    TopkArgs p{};
+    p.t = tables(L);
+    p.k = store(K);
+    if (V) p.v = store(V);
+    p.q = q;
+    p.rope = rope;
+    p.rope_dim = rope_dim;
+    p.Hq = n_q_heads;
+    p.G = n_q_heads / L->n_heads;
+    p.scale = softmax_scale;
+    p.top_k = k;
+    p.scores = reinterpret_cast<float *>(ws + w.scores);
+    p.n_sel = reinterpret_cast<int32_t *>(ws + w.n_sel);
+    p.sel_idx = reinterpret_cast<int32_t *>(ws + w.sel_idx);
+    p.sel_bits = ws + w.sel_bits;
+    p.sel_koff = reinterpret_cast<uint64_t *>(ws + w.sel_koff);
+    p.sel_voff = V ? reinterpret_cast<uint64_t *>(ws + w.sel_voff) : nullptr;
+    p.rope_sel = rope_dim ? reinterpret_cast<uint16_t *>(ws + w.rope_sel) : nullptr;
+    p.selected = selected;
+    p.sel_stride = top_k;
+    p.score_stride = 1;
+    hipStream_t hs = static_cast<hipStream_t>(stream);
+    DecodeArgs g4{};
+    const bool use_g4 = rope_dim == 0 && decode_g4_supported(L->head_dim, p.G);
+    if (use_g4) {
+        g4.t = tables(L);
+        g4.k = store(K);
+        g4.q = q;
+        g4.Hq = n_q_heads;
+        g4.G = p.G;
+        int splits = 0;
+        decode_g4_plan(L->n_seqs, L->n_heads, L->max_blocks, 0, &g4.SB, &splits);
+        p.score_stride = L->n_heads;
+    }
+    if (launch_topk_select(p, use_g4 ? &g4 : nullptr, hs) != hipSuccess) return KVQ_EHIP;
+    kvq_layout L2 = w.L2;
+    L2.n_blocks = p.n_sel;
+    L2.bits = p.sel_bits;
+    kvq_store K2 = *K;
+    K2.offset = p.sel_koff;
+    kvq_store V2{};
+    if (V) {
+        V2 = *V;
+        V2.offset = p.sel_voff;
+    }
+    return kvq_attend_decode(&L2, &K2, V ? &V2 : nullptr, p.rope_sel, rope_dim, q, n_q_heads, softmax_scale, out,
+                             ws + w.dec, workspace_bytes - w.dec, stream);
 }
 
 int kvq_chunk_workspace(const kvq_layout *L, int32_t n_q_heads, int32_t n_new, size_t *bytes)

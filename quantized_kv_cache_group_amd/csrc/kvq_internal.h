@@ -107,6 +107,29 @@ struct AppendArgs {
     int32_t *n_blocks_out, *n_window_out;
 };
 
+// Top-K block selection for sparse decode: scores, then compacted tables.
+struct TopkArgs {
+    Tables t;
+    Store k, v;                 // v.offset null for a latent cache
+    const uint16_t *q;          // [A][Hq][D + rope_dim]
+    const uint16_t *rope;       // [A][64*max_blocks + window_cap][H][rope_dim] or null
+    int rope_dim;
+    int Hq, G;
+    float scale;
+    int top_k;
+    float *scores;              // [A][max_blocks][score_stride], the block score is the max over the last axis
+    int score_stride;           // 1 (generic scores) or H (per KV head, from the decode's products)
+    int32_t *n_sel;             // [A]
+    int32_t *sel_idx;           // [A][top_k], ascending, -1 padded
+    uint8_t *sel_bits;          // [A][top_k]
+    uint64_t *sel_koff, *sel_voff;   // [A][top_k]
+    uint16_t *rope_sel;         // [A][64*top_k + window_cap][H][rope_dim]
+    int32_t *selected;          // caller's [A][sel_stride] copy of sel_idx, or null
+    int sel_stride;             // >= top_k; columns past top_k get -1
+};
+bool topk_supported(int max_blocks, int G, int head_dim, int rope_dim);
+hipError_t launch_topk_select(const TopkArgs &p, const DecodeArgs *g4, hipStream_t s);  // g4: score with the decode kernel
+
 // CacheCard image of one sequence: to_image 1 gathers, 0 scatters.
 hipError_t launch_card(const Tables &t, const uint64_t *k_offset, const uint64_t *v_offset, uint8_t *k_pool,
                        uint8_t *v_pool, uint16_t *k_window, uint16_t *v_window, uint16_t *rope, int rope_dim,
@@ -119,6 +142,7 @@ hipError_t launch_dequantize(const DequantArgs &a, hipStream_t s);
 hipError_t launch_attend_generic(const AttnArgs &a, hipStream_t s);
 hipError_t launch_decode_gqa(const DecodeArgs &a, hipStream_t s);     // split + merge
 hipError_t launch_decode_g4(const DecodeArgs &a, hipStream_t s);      // split only (G <= 4)
+hipError_t launch_g4_scores(const DecodeArgs &a, float scale, float *scores_h, hipStream_t s);
 hipError_t launch_decode_merge(const DecodeArgs &a, hipStream_t s);
 bool decode_g4_supported(int D, int G);
 void decode_g4_plan(int A, int H, int max_blocks, int window_cap, int *SB, int *n_splits);

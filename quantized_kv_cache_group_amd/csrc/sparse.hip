@@ -1,0 +1,226 @@
+// Top-K block selection for sparse decode over the quantized cache.
+//
+// What it computes (Reasoning-Aware Error-Bounded KV-Cache Compression and
+// Sparse Attention for Long-Context LLMs, section 2C: the active set is the
+// top-K entries by a query-aware score built on the instantaneous query-key
+// compatibility; section 2B: the output error is bounded by twice the
+// largest value norm times the attention mass left out).  Here an entry is a
+// 64-token quantized block of a sequence, its score the largest scaled
+// query-key product over its tokens and over all of the sequence's query
+// heads, computed from the restored keys (plus raw rope dims).  The top-K
+// blocks (ties to the lower index) are compacted, in block order, into
+// tables that the ordinary decode kernels then read; the bf16 window is
+// always active.
+#include "kvq_internal.h"
+
+namespace kvq {
+namespace {
+
+__device__ __forceinline__ float bf16f(uint16_t h) { return __uint_as_float((uint32_t)h << 16); }
+
+// Scores: one workgroup (4 waves) per (block j, sequence a); lane = token,
+// wave w takes the query heads h of each group with h % 4 == w.  The query
+// rows of one KV head's group are staged in LDS as fp32.
+constexpr int MAXQ = 16 * (512 + 64);                 // G <= 16 rows of D + rope <= 576
+
+__global__ __launch_bounds__(256) void block_scores(TopkArgs p)
+{
+    __shared__ float qs[MAXQ];
+    __shared__ float wmax[4];
+    const int j = blockIdx.x, a = blockIdx.y;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int H = p.t.H, D = p.t.D, R = p.rope_dim, Dk = D + R, G = p.G;
+    int nb = p.t.n_blocks[a];
+    nb = nb < 0 ? 0 : (nb > p.t.max_blocks ? p.t.max_blocks : nb);
+    if (j >= p.t.max_blocks) return;
+    if (j >= nb) {
+        if (threadIdx.x == 0) p.scores[(size_t)a * p.t.max_blocks + j] = -INFINITY;
+        return;
+    }
+    const size_t e = (size_t)a * p.t.max_blocks + j;
+    const int B = p.t.bits[e];
+    const uint8_t *blk = p.k.pool + p.k.offset[e];
+    const int code_row = D * B / 8, NG = D / 64;
+    const size_t rope_tokens = (size_t)64 * p.t.max_blocks + p.t.window_cap;
+    float best = -INFINITY;
+    for (int g = 0; g < H; g++) {
+        __syncthreads();                               // previous group's rows are consumed
+        for (int i = threadIdx.x; i < G * Dk; i += 256)
+            qs[i] = bf16f(p.q[((size_t)a * p.Hq + (size_t)g * G) * Dk + i]);
+        __syncthreads();
+        float acc[4] = {0.f, 0.f, 0.f, 0.f};          // heads wave, wave+4, wave+8, wave+12
+        const uint32_t *row = reinterpret_cast<const uint32_t *>(blk + ((size_t)g * 64 + lane) * code_row);
+        const uint32_t *meta = reinterpret_cast<const uint32_t *>(blk + (size_t)H * 64 * code_row) +
+                               ((size_t)g * 64 + lane) * NG;
+        for (int gg = 0; gg < NG; gg++) {
+            const uint32_t m = meta[gg];
+            const float s = (float)__builtin_bit_cast(_Float16, (uint16_t)(m & 0xffff));
+            const float b = (float)__builtin_bit_cast(_Float16, (uint16_t)(m >> 16));
+            const uint32_t *w = row + gg * 2 * B;      // the group's 2B code words
+            for (int i = 0; i < 64; i++) {
+                const int bit = B * i, wi = bit >> 5, sh = bit & 31;
+                uint32_t c = w[wi] >> sh;
+                if (sh + B > 32) c |= w[wi + 1] << (32 - sh);
+                c &= (1u << B) - 1u;
+                const float k = __builtin_fmaf((float)c, s, b);    // restored key value
+                const int d = 64 * gg + i;
+#pragma unroll
+                for (int r = 0; r < 4; r++) {
+                    const int h = wave + 4 * r;
+                    if (h < G) acc[r] = __builtin_fmaf(qs[h * Dk + d], k, acc[r]);
+                }
+            }
+        }
+        if (R) {
+            const uint16_t *rr = p.rope + (((size_t)a * rope_tokens + (size_t)64 * j + lane) * H + g) * R;
+            for (int d = 0; d < R; d++) {
+                const float k = bf16f(rr[d]);
+#pragma unroll
+                for (int r = 0; r < 4; r++) {
+                    const int h = wave + 4 * r;
+                    if (h < G) acc[r] = __builtin_fmaf(qs[h * Dk + D + d], k, acc[r]);
+                }
+            }
+        }
+#pragma unroll
+        for (int r = 0; r < 4; r++)
+            if (wave + 4 * r < G) best = fmaxf(best, p.scale * acc[r]);
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) best = fmaxf(best, __shfl_xor(best, o));
+    if (lane == 0) wmax[wave] = best;
+    __syncthreads();
+    if (threadIdx.x == 0)
+        p.scores[e] = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));
+}
+
+// Selection: one workgroup per sequence.  Block i is kept when fewer than
+// Kk = min(top_k, nb) blocks rank above it (higher score, or equal score and
+// lower index); kept blocks are compacted in block order.
+constexpr int MAXB = 16384;
+
+__global__ __launch_bounds__(256) void select_blocks(TopkArgs p)
+{
+    __shared__ uint8_t keep[MAXB];
+    __shared__ int cnt[256];
+    const int a = blockIdx.x, tid = threadIdx.x;
+    int nb = p.t.n_blocks[a];
+    nb = nb < 0 ? 0 : (nb > p.t.max_blocks ? p.t.max_blocks : nb);
+    const int Kk = nb < p.top_k ? nb : p.top_k;
+    // a block's score: the max over its score_stride entries, reduced once into LDS
+    __shared__ float sc[MAXB];
+    const int S = p.score_stride;
+    const float *s = p.scores + (size_t)a * p.t.max_blocks * S;
+    for (int i = tid; i < nb; i += 256) {
+        float m = s[(size_t)i * S];
+        for (int e = 1; e < S; e++) m = fmaxf(m, s[(size_t)i * S + e]);
+        sc[i] = m;
+    }
+    __syncthreads();
+    for (int i = tid; i < nb; i += 256) {
+        const float si = sc[i];
+        int rank = 0;
+        for (int jj = 0; jj < nb; jj++) {
+            const float sj = sc[jj];
+            rank += (sj > si) || (sj == si && jj < i);
+        }
+        keep[i] = rank < Kk;
+    }
+    __syncthreads();
+    // each thread owns a contiguous run of blocks; exclusive scan of the counts
+    const int per = (nb + 255) / 256, b0 = tid * per, b1 = min(b0 + per, nb);
+    int c = 0;
+    for (int i = b0; i < b1; i++) c += keep[i];
+    cnt[tid] = c;
+    __syncthreads();
+    for (int o = 1; o < 256; o <<= 1) {
+        const int v = tid >= o ? cnt[tid - o] : 0;
+        __syncthreads();
+        cnt[tid] += v;
+        __syncthreads();
+    }
+    int pos = cnt[tid] - c;
+    const size_t in = (size_t)a * p.t.max_blocks, out = (size_t)a * p.top_k;
+    int32_t *user = p.selected ? p.selected + (size_t)a * p.sel_stride : nullptr;
+    for (int i = b0; i < b1; i++) {
+        if (!keep[i]) continue;
+        p.sel_idx[out + pos] = i;
+        if (user) user[pos] = i;
+        p.sel_bits[out + pos] = p.t.bits[in + i];
+        p.sel_koff[out + pos] = p.k.offset[in + i];
+        if (p.sel_voff) p.sel_voff[out + pos] = p.v.offset[in + i];
+        pos++;
+    }
+    for (int q = Kk + tid; q < p.top_k; q += 256) {
+        p.sel_idx[out + q] = -1;
+        p.sel_bits[out + q] = 4;
+        p.sel_koff[out + q] = 0;
+        if (p.sel_voff) p.sel_voff[out + q] = 0;
+    }
+    if (user)
+        for (int q = Kk + tid; q < p.sel_stride; q += 256) user[q] = -1;
+    if (tid == 0) p.n_sel[a] = Kk;
+}
+
+// Rope rows of the compacted layout: block slot q takes the rows of block
+// sel_idx[q]; the window rows follow the last kept block.
+__global__ __launch_bounds__(256) void compact_rope(TopkArgs p)
+{
+    const int x = blockIdx.x, a = blockIdx.y;
+    const int H = p.t.H, R = p.rope_dim;
+    int nb = p.t.n_blocks[a];
+    nb = nb < 0 ? 0 : (nb > p.t.max_blocks ? p.t.max_blocks : nb);
+    int W = p.t.n_window ? p.t.n_window[a] : 0;
+    W = W < 0 ? 0 : (W > p.t.window_cap ? p.t.window_cap : W);
+    const int Kk = nb < p.top_k ? nb : p.top_k;
+    const size_t src_tokens = (size_t)64 * p.t.max_blocks + p.t.window_cap;
+    const size_t dst_tokens = (size_t)64 * p.top_k + p.t.window_cap;
+    const uint16_t *src = p.rope + (size_t)a * src_tokens * H * R;
+    uint16_t *dst = p.rope_sel + (size_t)a * dst_tokens * H * R;
+    int s0, d0, n;                                    // rows
+    if (x < p.top_k) {
+        if (x >= Kk) return;
+        s0 = 64 * p.sel_idx[(size_t)a * p.top_k + x];
+        d0 = 64 * x;
+        n = 64;
+    } else {
+        const int c = x - p.top_k;                    // 64-row chunks of the window
+        if (64 * c >= W) return;
+        s0 = 64 * nb + 64 * c;
+        d0 = 64 * Kk + 64 * c;
+        n = min(64, W - 64 * c);
+    }
+    const int pieces = n * H * R / 8;                 // 16-byte pieces
+    const uint4 *sp = reinterpret_cast<const uint4 *>(src + (size_t)s0 * H * R);
+    uint4 *dp = reinterpret_cast<uint4 *>(dst + (size_t)d0 * H * R);
+    for (int i = threadIdx.x; i < pieces; i += 256) dp[i] = sp[i];
+}
+
+}  // namespace
+
+bool topk_supported(int max_blocks, int G, int head_dim, int rope_dim)
+{
+    return max_blocks <= MAXB && G * (head_dim + rope_dim) <= MAXQ;
+}
+
+hipError_t launch_topk_select(const TopkArgs &p, const DecodeArgs *g4, hipStream_t s)
+{
+    if (p.t.max_blocks > 0) {
+        hipError_t e;
+        if (g4) {                                     // per KV head, from the decode's own products
+            e = launch_g4_scores(*g4, p.scale, p.scores, s);
+        } else {
+            block_scores<<<dim3(p.t.max_blocks, p.t.A), 256, 0, s>>>(p);
+            e = hipGetLastError();
+        }
+        if (e != hipSuccess) return e;
+    }
+    select_blocks<<<p.t.A, 256, 0, s>>>(p);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || !p.rope_dim) return e;
+    const int wchunks = (p.t.window_cap + 63) / 64;
+    compact_rope<<<dim3(p.top_k + wchunks, p.t.A), 256, 0, s>>>(p);
+    return hipGetLastError();
+}
+
+}  // namespace kvq

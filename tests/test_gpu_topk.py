@@ -1,0 +1,114 @@
+"""GPU top-K sparse decode against the oracle.
+
+The kept set is an integer decision taken from fp32 scores on the GPU and
+fp64 scores in the oracle, so it is checked for validity: every kept block
+scores (in the oracle) at least the K-th best minus the fp32 rounding
+allowance, every dropped block at most the K-th best plus it, and the kept
+indices are ascending and distinct.  The output must then equal the
+oracle's decode over exactly the GPU's kept set (2e-3 max-abs, 1e-3 rel-L2),
+and keeping every block must reproduce the full decode."""
+import numpy as np
+import pytest
+import torch
+
+import kvq_synth as syn
+import oracle
+from parity import build, close, ref_decode, to_dev_bf16
+
+pytestmark = pytest.mark.gpu
+
+
+def _check_selection(b, q, scale, K, sel):
+    c = b.cache
+    for a in range(c.A):
+        s = b.seq(a)
+        nb = c.n_blocks_host[a]
+        rope = None if b.rope is None else b.rope[a][:64 * nb]
+        sc = oracle.block_scores_seq(b.ref_pool, s["bits"], s["koff"], rope, c.H, c.D, q[a], scale)
+        Kk = min(K, nb)
+        got = sel[a, :Kk]
+        assert np.all(sel[a, Kk:] == -1)
+        assert np.all(np.diff(got) > 0) and (Kk == 0 or (got[0] >= 0 and got[-1] < nb))
+        if Kk == 0 or Kk == nb:
+            assert Kk == 0 or np.array_equal(got, np.arange(nb))
+            continue
+        # fp32 rounding allowance: |sum q k| error <= ~Dk * 2^-23 * sum |q||k|, times the scale
+        kr = oracle.restore_seq(b.ref_pool, s["bits"], s["koff"], None, c.H, c.D).astype(np.float64)
+        qf = np.abs(syn.bf16_to_f32(q[a]).astype(np.float64))
+        bound = np.abs(kr).max() * qf.sum(axis=1).max() * abs(scale)
+        if rope is not None:
+            bound += np.abs(syn.bf16_to_f32(rope)).max() * qf.sum(axis=1).max() * abs(scale)
+        tol = 64 * 2.0 ** -23 * bound + 1e-7
+        G = q.shape[1] // c.H
+        if rope is None and G <= 4 and c.D in (64, 128, 256):
+            # scored by the decode's own products: sum_d q (1024 + code) accumulates in fp32
+            # over 64 dims and 1024 Q_g is subtracted, an error of at most ~0.0088 sum|q| per
+            # group, times the group's scale (<= 2 max|k|/3 at 2 bits) and the softmax scale
+            qg = np.abs(syn.bf16_to_f32(q[a]).astype(np.float64)).reshape(q.shape[1], c.D // 64, 64).sum(axis=2)
+            tol = max(tol, abs(scale) * (c.D // 64) * (2 * np.abs(kr).max() / 3) * 0.0088 * qg.max())
+        kth = np.sort(sc)[::-1][Kk - 1]
+        kept = np.zeros(nb, bool)
+        kept[got] = True
+        assert np.all(sc[kept] >= kth - tol), (a, sc[kept].min(), kth)
+        assert np.all(sc[~kept] <= kth + tol), (a, sc[~kept].max(), kth)
+
+
+def _ref_sparse(b, q, scale, sel):
+    c = b.cache
+    out = np.zeros((c.A, q.shape[1], c.D), np.float32)
+    for a in range(c.A):
+        s = b.seq(a)
+        nb = c.n_blocks_host[a]
+        idx = sel[a][sel[a] >= 0]
+        rope = None
+        if b.rope is not None:
+            r = b.rope[a]
+            rope = np.concatenate([r[64 * j:64 * j + 64] for j in idx] + [r[64 * nb:64 * nb + c.n_window_host[a]]])
+        out[a] = oracle.attend_decode_seq(b.ref_pool, s["bits"][idx], s["koff"][idx],
+                                          None if s["voff"] is None else s["voff"][idx], s["kw"], s["vw"], rope,
+                                          c.H, c.D, q[a], scale)
+    return out
+
+
+def _run(b, q, scale, K):
+    c = b.cache
+    sel = torch.full((c.A, K), -7, dtype=torch.int32, device="cuda")
+    out = c.attend_decode_topk(to_dev_bf16(q), scale, K, selected=sel)
+    torch.cuda.synchronize()
+    return out.cpu().numpy(), sel.cpu().numpy()
+
+
+@pytest.mark.parametrize("D,G,K", [(128, 4, 3), (128, 4, 1), (64, 8, 5), (256, 2, 4), (128, 16, 2)])
+def test_topk_gqa(D, G, K):
+    H = 2
+    lengths = [64 * 12 + 40, 64 * 3 + 100, 64 * 20, 130]
+    rng = np.random.default_rng(D + G)
+    window = [40, 100, 0, 130]
+    nb = [(L - w) // 64 for L, w in zip(lengths, window)]
+    bits = [rng.choice(np.array([2, 3, 4, 8], np.uint8), size=n) for n in nb]
+    b = build(H, D, lengths, bits=bits, window=window, seed=D + G)
+    q = syn.random_normal_bf16((4, G * H, D), 61 + K, scale=2.0)
+    scale = D ** -0.5
+    got, sel = _run(b, q, scale, K)
+    _check_selection(b, q, scale, K, sel)
+    close(got, _ref_sparse(b, q, scale, sel), what=f"topk D={D} G={G} K={K}")
+
+
+def test_topk_all_blocks_is_full_decode():
+    H, D = 8, 128
+    b = build(H, D, [64 * 10 + 5, 64 * 7], window=[5, 0], seed=12)
+    q = syn.random_normal_bf16((2, 32, D), 62)
+    got, sel = _run(b, q, D ** -0.5, 10)
+    assert np.array_equal(sel[0], np.arange(10)) and np.array_equal(sel[1], list(range(7)) + [-1] * 3)
+    close(got, ref_decode(b, q, D ** -0.5), what="topk = all")
+
+
+def test_topk_latent_rope():
+    H, D, R, Hq = 1, 512, 64, 16
+    lengths = [64 * 30 + 20, 64 * 9]
+    b = build(H, D, lengths, latent=True, rope_dim=R, window=[20, 0], seed=13)
+    q = syn.random_normal_bf16((2, Hq, D + R), 63, scale=2.0)
+    scale = 576 ** -0.5
+    got, sel = _run(b, q, scale, 6)
+    _check_selection(b, q, scale, 6, sel)
+    close(got, _ref_sparse(b, q, scale, sel), what="topk latent+rope")
