@@ -48,6 +48,9 @@ def parse():
     p.add_argument("--topk", type=int, default=0, metavar="K",
                    help="time top-K sparse decode (K of 64 blocks per agent) on the Llama 10-agent "
                         "caches, beside the full decode, instead of the workload step")
+    p.add_argument("--alloc", action="store_true",
+                   help="time block sensitivity (GPU) and the budgeted width allocation (host) on the "
+                        "Gemma mixed-width shape instead of the workload step")
     p.add_argument("--card", action="store_true",
                    help="time CacheCard gather and scatter of the Llama 10-agent caches "
                         "(device image <-> cache) instead of the workload step")
@@ -370,6 +373,62 @@ def topk_bench(args):
     print(json.dumps(res), flush=True)
 
 
+def alloc_bench(args):
+    """Width allocation on the Gemma-3-12B mixed-width shape (8 agents, L ~
+    U{1024..16384}, Hq 16 / Hkv 8, D 256): block sensitivity of every block's
+    bf16 K and V rows for the layer's query (GPU; bytes = the rows read), then
+    the greedy widths of all blocks of the 8 sampled layers at a mean-3-bit
+    budget (host C++)."""
+    import torch
+    import kvq_synth as syn
+    import quantized_kv_cache_group_amd as kvq
+
+    kvq.lib()
+    torch.cuda.set_device(0)
+    w = syn.workload(2)
+    A, H, D, Hq = w.n_agents, w.n_kv_heads, w.head_dim, w.n_q_heads
+    S_tok = 64 * max(w.n_blocks)
+    g = torch.Generator(device="cuda")
+    g.manual_seed(3)
+    R = 2
+    ks = [torch.randn((A, S_tok, H, D), generator=g, device="cuda").to(torch.bfloat16) for _ in range(R)]
+    vs = [torch.randn((A, S_tok, H, D), generator=g, device="cuda").to(torch.bfloat16) for _ in range(R)]
+    q = torch.randn((A, Hq, D), generator=g, device="cuda").to(torch.bfloat16)
+    out = torch.empty((A, max(w.n_blocks)), dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream()
+    for i in range(args.warmup):
+        kvq.block_sensitivity(ks[i % R], vs[i % R], q, w.scale, out=out)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for i in range(args.steps):
+        kvq.block_sensitivity(ks[i % R], vs[i % R], q, w.scale, out=out)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / args.steps
+    rows = A * S_tok * H * D * 2 * 2
+    gbs = rows / (us * 1e-6) / 1e9
+    S = out.cpu().numpy()
+    allS = np.concatenate([np.tile(S[a, :w.n_blocks[a]], len(w.layers)) for a in range(A)]).astype(np.float32)
+    budget = allS.size * kvq.block_bytes(3, H, D)
+    t0 = time.perf_counter()
+    widths = kvq.allocate_widths(allS, H, D, budget)
+    t_alloc = time.perf_counter() - t0
+    res = {"metric": "block sensitivity GB/s", "value": round(gbs, 2), "unit": "GB/s", "n_gpus": 1,
+           "steps": args.steps, "warmup": args.warmup, "higher_is_better": True, "dtype": "f32",
+           "data": "synthetic",
+           "config": {"workload": "gemma12b-8agent-width-allocation", "agents": A, "q_heads": Hq, "kv_heads": H,
+                      "head_dim": D, "rows_per_agent": S_tok, "layers": len(w.layers)},
+           "sensitivity_us": round(us, 3), "blocks_allocated": int(allS.size),
+           "allocate_ms_host": round(t_alloc * 1e3, 3),
+           "mean_bits": round(float(np.mean(widths)), 4),
+           "width_counts": {str(b): int((widths == b).sum()) for b in (2, 3, 4, 8)},
+           "roofline": {"kernel": "kvq block_sensitivity", "bound": "hbm", "achieved": round(gbs, 2),
+                        "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
+                        "traffic": None}}
+    print(json.dumps(res), flush=True)
+
+
 def card_bench(args):
     """CacheCard gather (cache -> contiguous device image) and scatter (image
     -> cache) for each of the 10 agents of the Llama-3.1-8B layer shape (4096
@@ -445,6 +504,9 @@ def main():
     args = parse()
     if args.card:
         card_bench(args)
+        return
+    if args.alloc:
+        alloc_bench(args)
         return
     if args.topk:
         topk_bench(args)

@@ -189,6 +189,33 @@ int kvq_card_gather(const kvq_layout *L, const kvq_store *K, const kvq_store *V,
 int kvq_card_scatter(const kvq_layout *L, const kvq_store *K, const kvq_store *V, uint16_t *rope,
                      int32_t rope_dim, int32_t seq, const void *image, uint64_t image_bytes, void *stream);
 
+/* Width-allocation sensitivity (CoMixKV, Abstract: sensitivity from a local
+ * attention-error bound using recent queries, keys and values; this
+ * library's bound, from the per-group reconstruction bound s/2 with s =
+ * range / (2^b - 1)).  For sequence a and block i < n_blocks (rows 64i ..
+ * 64i+63 of k and v, bf16 [A][seq_tokens][H][D], 16-byte aligned):
+ *     S[a][i] = sum_h ( 2 Vmax_g scale max_t sum_grp rK[t][g][grp] sum_{d in grp} |q[a][h][d]|
+ *                       + 8 max_t sqrt(sum_grp rV[t][g][grp]^2) ),   g = h / (n_q_heads/H)
+ * rK, rV: max - min of a 64-element group; Vmax_g: the largest V row norm of
+ * KV head g in the block.  Quantizing the block at width b moves attention
+ * restricted to the block by about c(b) S_h per head, c(b) = 1/(2(2^b-1))
+ * (to first order in c).  q bf16 [A][n_q_heads][D]; S fp32 device [A][n_blocks].
+ * Errors: KVQ_EINVAL, KVQ_EUNSUPPORTED (more than 1024 query heads), KVQ_EHIP. */
+int kvq_block_sensitivity(const uint16_t *k, const uint16_t *v, int32_t n_seqs, int64_t seq_tokens,
+                          int32_t n_blocks, int32_t n_heads, int32_t head_dim, const uint16_t *q,
+                          int32_t n_q_heads, float softmax_scale, float *S, void *stream);
+
+/* Budgeted widths (host; CoMixKV: joint allocation under a shared memory
+ * budget, applied to newly quantized blocks).  Every block starts at 2 bits;
+ * repeatedly the (block, next width in 2 -> 3 -> 4 -> 8) step with the
+ * largest S[i] (c(b) - c(b')) per extra byte is taken among the steps that
+ * still fit budget_bytes (equal ratios: lower index first), until none fits.
+ * Block bytes are kvq_block_bytes(b, n_heads, head_dim).  S and widths are
+ * host arrays of n entries.
+ * Errors: KVQ_EINVAL (bad sizes, or a budget below the all-2-bit size). */
+int kvq_allocate_widths(const float *S, int64_t n, int32_t n_heads, int32_t head_dim,
+                        uint64_t budget_bytes, uint8_t *widths);
+
 /* Workspace bytes kvq_attend_decode needs for this layout and head count
  * (written to *bytes).  Errors: KVQ_EINVAL, KVQ_EUNSUPPORTED. */
 int kvq_decode_workspace(const kvq_layout *L, int32_t n_q_heads, int32_t rope_dim, size_t *bytes);

@@ -83,6 +83,10 @@ def lib() -> ctypes.CDLL:
         L.kvq_ref_append_seq.restype = i32
         L.kvq_ref_block_scores_seq.argtypes = [P, P, P, i32, P, i32, i32, i32, P, i32, ctypes.c_double, P]
         L.kvq_ref_block_scores_seq.restype = i32
+        L.kvq_ref_block_sensitivity.argtypes = [P, P, i32, i32, P, i32, ctypes.c_double, P]
+        L.kvq_ref_block_sensitivity.restype = i32
+        L.kvq_ref_block_error_bound.argtypes = [P, P, i32, i32, P, i32, i32, ctypes.c_double, i32]
+        L.kvq_ref_block_error_bound.restype = ctypes.c_double
         L.kvq_ref_max_threads.argtypes = []
         L.kvq_ref_max_threads.restype = i32
         _lib = L
@@ -343,6 +347,65 @@ def topk_blocks(scores, k: int) -> np.ndarray:
     s = np.asarray(scores, np.float64)
     order = sorted(range(s.size), key=lambda i: (-s[i], i))
     return np.array(sorted(order[:min(k, s.size)]), np.int64)
+
+
+def block_sensitivity(k_bf16, v_bf16, n_kv_heads, head_dim, q_bf16, scale) -> float:
+    """S of one block (k, v bf16 [64][H][D], q bf16 [Hq][D]): the width-free
+    factor of the block's first-order attention-error bound."""
+    k = _c(k_bf16, np.uint16)
+    v = _c(v_bf16, np.uint16)
+    q = _c(q_bf16, np.uint16)
+    out = np.zeros(1, np.float64)
+    if lib().kvq_ref_block_sensitivity(_p(k), _p(v), n_kv_heads, head_dim, _p(q), q.size // head_dim,
+                                       float(scale), _p(out)):
+        raise ValueError("kvq_ref_block_sensitivity failed")
+    return float(out[0])
+
+
+def block_error_bound(k_bf16, v_bf16, n_kv_heads, head_dim, q_bf16, h, scale, bits) -> float:
+    k = _c(k_bf16, np.uint16)
+    v = _c(v_bf16, np.uint16)
+    q = _c(q_bf16, np.uint16)
+    return float(lib().kvq_ref_block_error_bound(_p(k), _p(v), n_kv_heads, head_dim, _p(q), q.size // head_dim,
+                                                 h, float(scale), bits))
+
+
+WIDTHS = (2, 3, 4, 8)
+
+
+def width_cost(b) -> float:
+    """c(b) = 1/(2(2^b - 1)): the error factor of width b."""
+    return 1.0 / (2.0 * ((1 << int(b)) - 1))
+
+
+def allocate_widths(S, bytes_per_block_at, budget) -> np.ndarray:
+    """Greedy budgeted allocation: every block starts at 2 bits; repeatedly
+    take the (block, next width) step with the largest error reduction
+    S_i (c(b) - c(b')) per extra byte that still fits the budget (equal
+    ratios: lower block index first), until no step fits.
+    bytes_per_block_at(b) -> bytes of one block at width b."""
+    S = np.asarray(S, np.float64)
+    w = np.full(S.size, 0, np.int64)                 # index into WIDTHS
+    used = S.size * bytes_per_block_at(WIDTHS[0])
+    if used > budget:
+        raise ValueError("budget below the all-2-bit size")
+    while True:
+        best, bi = None, -1
+        for i in range(S.size):
+            if w[i] + 1 >= len(WIDTHS):
+                continue
+            b0, b1 = WIDTHS[w[i]], WIDTHS[w[i] + 1]
+            extra = bytes_per_block_at(b1) - bytes_per_block_at(b0)
+            if used + extra > budget:
+                continue
+            r = S[i] * (width_cost(b0) - width_cost(b1)) / extra
+            if best is None or r > best:
+                best, bi = r, i
+        if bi < 0:
+            break
+        used += bytes_per_block_at(WIDTHS[w[bi] + 1]) - bytes_per_block_at(WIDTHS[w[bi]])
+        w[bi] += 1
+    return np.array([WIDTHS[i] for i in w], np.uint8)
 
 
 def max_threads() -> int:

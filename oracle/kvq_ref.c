@@ -537,3 +537,65 @@ int kvq_ref_block_scores_seq(const uint8_t *pool, const uint8_t *bits, const uin
     free(K);
     return 0;
 }
+
+/* Per-token pieces of the block bound for query head h: the score term
+ * sum_grp rK * sum|q| (without the width factor), the value term
+ * sqrt(sum_grp rV^2), and the value norm. */
+static void sens_terms(const uint16_t *k, const uint16_t *v, int H, int D, const uint16_t *qh, int g, int t,
+                       double *kt, double *vt, double *vn)
+{
+    double ks = 0.0, vs = 0.0, nn = 0.0;
+    for (int grp = 0; grp < D / 64; grp++) {
+        double kmn = INFINITY, kmx = -INFINITY, vmn = INFINITY, vmx = -INFINITY, qa = 0.0;
+        for (int d = 64 * grp; d < 64 * grp + 64; d++) {
+            const double kk = kvq_ref_bf16_to_f32(k[((size_t)t * H + g) * D + d]);
+            const double vv = kvq_ref_bf16_to_f32(v[((size_t)t * H + g) * D + d]);
+            kmn = fmin(kmn, kk); kmx = fmax(kmx, kk);
+            vmn = fmin(vmn, vv); vmx = fmax(vmx, vv);
+            qa += fabs((double)kvq_ref_bf16_to_f32(qh[d]));
+            nn += vv * vv;
+        }
+        ks += (kmx - kmn) * qa;
+        vs += (vmx - vmn) * (vmx - vmn);
+    }
+    *kt = ks;
+    *vt = sqrt(vs);
+    *vn = sqrt(nn);
+}
+
+int kvq_ref_block_sensitivity(const uint16_t *k, const uint16_t *v, int n_kv_heads, int head_dim,
+                              const uint16_t *q, int n_q_heads, double scale, double *S)
+{
+    if (!dims_ok(n_kv_heads, head_dim) || n_q_heads < 1 || n_q_heads % n_kv_heads) return -1;
+    const int G = n_q_heads / n_kv_heads;
+    double total = 0.0;
+    for (int h = 0; h < n_q_heads; h++) {
+        double kmax = 0.0, vmax_t = 0.0, vnorm = 0.0;
+        for (int t = 0; t < 64; t++) {
+            double kt, vt, vn;
+            sens_terms(k, v, n_kv_heads, head_dim, q + (size_t)h * head_dim, h / G, t, &kt, &vt, &vn);
+            kmax = fmax(kmax, kt);
+            vmax_t = fmax(vmax_t, vt);
+            vnorm = fmax(vnorm, vn);
+        }
+        total += 2.0 * vnorm * fabs(scale) * kmax + 8.0 * vmax_t;
+    }
+    *S = total;
+    return 0;
+}
+
+double kvq_ref_block_error_bound(const uint16_t *k, const uint16_t *v, int n_kv_heads, int head_dim,
+                                 const uint16_t *q, int n_q_heads, int h, double scale, int bits)
+{
+    const int G = n_q_heads / n_kv_heads;
+    const double c = 1.0 / (2.0 * (double)((1 << bits) - 1));
+    double kmax = 0.0, vmax_t = 0.0, vnorm = 0.0;
+    for (int t = 0; t < 64; t++) {
+        double kt, vt, vn;
+        sens_terms(k, v, n_kv_heads, head_dim, q + (size_t)h * head_dim, h / G, t, &kt, &vt, &vn);
+        kmax = fmax(kmax, kt);
+        vmax_t = fmax(vmax_t, vt);
+        vnorm = fmax(vnorm, vn);
+    }
+    return (exp(2.0 * fabs(scale) * c * kmax) - 1.0) * vnorm + 8.0 * c * vmax_t;
+}

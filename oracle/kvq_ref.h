@@ -168,6 +168,30 @@ int kvq_ref_block_scores_seq(const uint8_t *pool, const uint8_t *bits, const uin
                              int head_dim, const uint16_t *q, int n_q_heads, double scale,
                              double *scores);
 
+/* Width-allocation sensitivity of 64-token blocks (Coordinated
+ * Mixed-Precision KV Cache Quantization, arXiv 2611.10096, Abstract: a
+ * sensitivity from a local attention-error bound using recent queries, keys
+ * and values; the formula is this library's, derived from the reconstruction
+ * bound |x_hat - x| <= s/2, s = range / (2^b - 1), of each 64-element group).
+ * For query head h (KV head g) and block tokens t, a key error within that
+ * bound moves the score by at most
+ *     eps_t(b) = scale * sum_groups (rK_t,grp / (2(2^b-1))) * sum_{d in grp} |q_h,d|
+ * and a value row by at most |dv_t|(b) = sqrt(64 * sum_grp (rV_t,grp/(2(2^b-1)))^2);
+ * attention restricted to the block then moves by at most
+ *     (exp(2 max_t eps_t) - 1) * Vmax + max_t |dv_t|        (Vmax = max_t |v_t|)
+ * which to first order is c(b) * S_h, c(b) = 1/(2(2^b-1)),
+ *     S_h = 2 Vmax scale max_t sum_grp rK_t,grp sum_{d in grp}|q_h,d| + 8 max_t sqrt(sum_grp rV_t,grp^2).
+ * The block's sensitivity is S = sum_h S_h.  rK, rV: max - min of the group
+ * (fp32 from bf16).  k, v bf16 [64][H][D] (one block), q bf16 [n_q_heads][D].
+ * Writes S; returns 0. */
+int kvq_ref_block_sensitivity(const uint16_t *k, const uint16_t *v, int n_kv_heads, int head_dim,
+                              const uint16_t *q, int n_q_heads, double scale, double *S);
+
+/* The bound itself at width bits for query head h (the exponential form
+ * above, not its first-order part). */
+double kvq_ref_block_error_bound(const uint16_t *k, const uint16_t *v, int n_kv_heads, int head_dim,
+                                 const uint16_t *q, int n_q_heads, int h, double scale, int bits);
+
 /* Threads the OpenMP runtime uses for the parallel loops (1 without OpenMP). */
 int kvq_ref_max_threads(void);
 

@@ -25,7 +25,8 @@ OUT_BF16, OUT_F32 = 0, 1
 WIDTHS = (2, 3, 4, 8)
 
 SYMBOLS = ("kvq_block_bytes", "kvq_quantize", "kvq_append", "kvq_dequantize", "kvq_card_bytes",
-           "kvq_card_gather", "kvq_card_scatter", "kvq_decode_workspace", "kvq_attend_decode",
+           "kvq_card_gather", "kvq_card_scatter", "kvq_block_sensitivity", "kvq_allocate_widths",
+           "kvq_decode_workspace", "kvq_attend_decode",
            "kvq_topk_workspace", "kvq_attend_decode_topk", "kvq_chunk_workspace", "kvq_attend_chunk",
            "kvq_strerror")
 
@@ -73,6 +74,10 @@ def lib() -> ctypes.CDLL:
         L.kvq_card_gather.restype = ctypes.c_int
         L.kvq_card_scatter.argtypes = [P, P, P, P, i32, i32, P, u64, P]
         L.kvq_card_scatter.restype = ctypes.c_int
+        L.kvq_block_sensitivity.argtypes = [P, P, i32, ctypes.c_int64, i32, i32, i32, P, i32, f32, P, P]
+        L.kvq_block_sensitivity.restype = ctypes.c_int
+        L.kvq_allocate_widths.argtypes = [P, ctypes.c_int64, i32, i32, u64, P]
+        L.kvq_allocate_widths.restype = ctypes.c_int
         L.kvq_dequantize.argtypes = [P, P, i32, P, ctypes.c_int64, P]
         L.kvq_dequantize.restype = ctypes.c_int
         L.kvq_decode_workspace.argtypes = [P, i32, i32, ctypes.POINTER(sz)]
@@ -117,6 +122,31 @@ def _stream(stream=None):
 def block_bytes(bits: int, n_heads: int, head_dim: int) -> int:
     """Bytes of one 64-token block payload (0 if unsupported)."""
     return int(lib().kvq_block_bytes(bits, n_heads, head_dim))
+
+
+def block_sensitivity(k: torch.Tensor, v: torch.Tensor, q: torch.Tensor, scale: float, n_blocks: int | None = None,
+                      out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """Sensitivity S [A][n_blocks] (fp32, device) of the 64-token blocks of
+    k, v bf16 [A][T][H][D] for the recent queries q bf16 [A][Hq][D]."""
+    A, T, H, D = k.shape
+    assert k.dtype == v.dtype == q.dtype == torch.bfloat16 and k.shape == v.shape
+    assert k.is_contiguous() and v.is_contiguous() and q.is_contiguous()
+    nb = T // 64 if n_blocks is None else n_blocks
+    if out is None:
+        out = torch.empty((A, max(nb, 1)), dtype=torch.float32, device=k.device)
+    _check(lib().kvq_block_sensitivity(_ptr(k), _ptr(v), A, T, nb, H, D, _ptr(q), q.shape[1], float(scale),
+                                       _ptr(out), _stream(stream)), "kvq_block_sensitivity")
+    return out[:, :nb]
+
+
+def allocate_widths(S, n_heads: int, head_dim: int, budget_bytes: int) -> np.ndarray:
+    """Greedy widths (uint8) of blocks with sensitivities S under a byte budget."""
+    s = np.ascontiguousarray(np.asarray(S, np.float32).ravel())
+    w = np.zeros(s.size, np.uint8)
+    _check(lib().kvq_allocate_widths(s.ctypes.data_as(ctypes.c_void_p), s.size, n_heads, head_dim,
+                                     int(budget_bytes), w.ctypes.data_as(ctypes.c_void_p)),
+           "kvq_allocate_widths")
+    return w
 
 
 def _round_up(x: int, a: int) -> int:

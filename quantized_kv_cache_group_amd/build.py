@@ -31,7 +31,7 @@ PER_FILE = {
     "quantize.hip": ["-ffp-contract=off", "-fno-honor-nans", "-mno-amdgpu-ieee"],
 }
 SOURCES = ["kvq_api.cpp", "quantize.hip", "attend_generic.hip", "decode_gqa.hip", "decode_g4.hip", "chunk.hip",
-           "mla.hip", "card.hip", "sparse.hip"]
+           "mla.hip", "card.hip", "sparse.hip", "alloc.hip"]
 
 
 def _compile(src: str) -> str:

@@ -285,6 +285,34 @@ int kvq_dequantize(const kvq_layout *L, const kvq_store *src, int32_t out_dtype,
     return hip_status(launch_dequantize(a, static_cast<hipStream_t>(stream)));
 }
 
+int kvq_block_sensitivity(const uint16_t *k, const uint16_t *v, int32_t n_seqs, int64_t seq_tokens,
+                          int32_t n_blocks, int32_t n_heads, int32_t head_dim, const uint16_t *q,
+                          int32_t n_q_heads, float softmax_scale, float *S, void *stream)
+{
+    if (n_seqs < 1 || n_blocks < 0 || n_heads < 1 || head_dim < 64 || head_dim % 64 || head_dim > 512)
+        return KVQ_EINVAL;
+    if (n_q_heads < 1 || n_q_heads % n_heads || seq_tokens < (int64_t)n_blocks * 64) return KVQ_EINVAL;
+    if (n_seqs > kMaxGrid || n_blocks > 0x7fffffff) return KVQ_EUNSUPPORTED;
+    if (!sensitivity_supported(n_heads, head_dim, n_q_heads)) return KVQ_EUNSUPPORTED;
+    if (!k || !v || !q || !S || !aligned(k, 16) || !aligned(v, 16) || !aligned(q, 2) || !aligned(S, 4))
+        return KVQ_EINVAL;
+    if (!isfinite(softmax_scale)) return KVQ_EINVAL;
+    return hip_status(launch_sensitivity(k, v, n_seqs, seq_tokens, n_blocks, n_heads, head_dim, q, n_q_heads,
+                                         softmax_scale, S, static_cast<hipStream_t>(stream)));
+}
+
+int kvq_allocate_widths(const float *S, int64_t n, int32_t n_heads, int32_t head_dim,
+                        uint64_t budget_bytes, uint8_t *widths)
+{
+    if (n < 0 || (n > 0 && (!S || !widths))) return KVQ_EINVAL;
+    const uint64_t b2 = kvq_block_bytes(2, n_heads, head_dim), b3 = kvq_block_bytes(3, n_heads, head_dim);
+    const uint64_t b4 = kvq_block_bytes(4, n_heads, head_dim), b8 = kvq_block_bytes(8, n_heads, head_dim);
+    if (!b2) return KVQ_EINVAL;
+    for (int64_t i = 0; i < n; i++)
+        if (!(S[i] >= 0.0f) || !isfinite(S[i])) return KVQ_EINVAL;
+    return allocate_widths(S, n, b2, b3, b4, b8, budget_bytes, widths) ? KVQ_EINVAL : KVQ_OK;
+}
+
 int kvq_decode_workspace(const kvq_layout *L, int32_t n_q_heads, int32_t rope_dim, size_t *bytes)
 {
     if (!bytes) return KVQ_EINVAL;

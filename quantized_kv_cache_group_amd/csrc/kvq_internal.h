@@ -130,6 +130,13 @@ struct TopkArgs {
 bool topk_supported(int max_blocks, int G, int head_dim, int rope_dim);
 hipError_t launch_topk_select(const TopkArgs &p, const DecodeArgs *g4, hipStream_t s);  // g4: score with the decode kernel
 
+// Width allocation: block sensitivity (GPU) and the budgeted greedy (host).
+bool sensitivity_supported(int H, int D, int Hq);
+hipError_t launch_sensitivity(const uint16_t *k, const uint16_t *v, int A, int64_t seq_tokens, int n_blocks, int H,
+                              int D, const uint16_t *q, int Hq, float scale, float *S, hipStream_t s);
+int allocate_widths(const float *S, int64_t n, uint64_t bytes2, uint64_t bytes3, uint64_t bytes4,
+                    uint64_t bytes8, uint64_t budget, uint8_t *widths);
+
 // CacheCard image of one sequence: to_image 1 gathers, 0 scatters.
 hipError_t launch_card(const Tables &t, const uint64_t *k_offset, const uint64_t *v_offset, uint8_t *k_pool,
                        uint8_t *v_pool, uint16_t *k_window, uint16_t *v_window, uint16_t *rope, int rope_dim,
