@@ -112,7 +112,7 @@ struct FullRow {
 #pragma unroll
             for (int i = 0; i < 4; i++) {
                 const uint32_t sel = 0x0C000C00u | ((uint32_t)(4 + i) << 16) | (uint32_t)i;
-                r.p[i] = as_h2(perm(w[2 * c + 1], w[2 * c], sel) | MAGIC);
+                r.p[i] = as_h2(perm(w[2 * c + 1], w[2 * c], sel) | mv);
             }
         } else {
             // 3 bytes at byte o of the row: code i at bits 3i of those 24

@@ -19,6 +19,18 @@ typedef float f2 __attribute__((ext_vector_type(2)));
 
 constexpr uint32_t MAGIC = 0x64006400u;   // fp16 1024.0 in both halves
 
+// MAGIC in a vector register the compiler cannot fold back into a literal:
+// (x & mask) | magic then selects to one v_and_or_b32 with the mask in a
+// scalar register (a VALU instruction here reads at most one scalar
+// operand, so with two literals it would take two instructions).  The empty
+// asm emits nothing.
+__device__ __forceinline__ uint32_t magic_v()
+{
+    uint32_t m = MAGIC;
+    asm("" : "+v"(m));
+    return m;
+}
+
 __device__ __forceinline__ h2 as_h2(uint32_t u) { return __builtin_bit_cast(h2, u); }
 __device__ __forceinline__ uint32_t u32_of(h2 h) { return __builtin_bit_cast(uint32_t, h); }
 __device__ __forceinline__ uint32_t perm(uint32_t hi, uint32_t lo, uint32_t sel)
@@ -42,11 +54,11 @@ struct Unpack<4> {
     // chunk: one dword, code i at bits 4i.
     __device__ static __forceinline__ Pairs run(uint32_t w)
     {
-        const uint32_t w8 = w >> 8;
-        const h2 x0 = as_h2((w & 0x000F000Fu) | MAGIC);
-        const h2 x1 = as_h2((w & 0x00F000F0u) | MAGIC);
-        const h2 x2 = as_h2((w8 & 0x000F000Fu) | MAGIC);
-        const h2 x3 = as_h2((w8 & 0x00F000F0u) | MAGIC);
+        const uint32_t w8 = w >> 8, mv = magic_v();
+        const h2 x0 = as_h2((w & 0x000F000Fu) | mv);
+        const h2 x1 = as_h2((w & 0x00F000F0u) | mv);
+        const h2 x2 = as_h2((w8 & 0x000F000Fu) | mv);
+        const h2 x3 = as_h2((w8 & 0x00F000F0u) | mv);
         const h2 one = {(_Float16)1.0f, (_Float16)1.0f}, m1024 = {(_Float16)-1024.0f, (_Float16)-1024.0f};
         const h2 s16 = {(_Float16)0.0625f, (_Float16)0.0625f}, m64 = {(_Float16)-64.0f, (_Float16)-64.0f};
         Pairs r;
@@ -64,10 +76,11 @@ struct Unpack<2> {
     __device__ static __forceinline__ Pairs run(uint32_t v)
     {
         const uint32_t y = v | (v << 8);          // hi half: codes 4..7 at bits 0..7
+        const uint32_t mv = magic_v();
         Pairs r;
 #pragma unroll
         for (int i = 0; i < 4; i++) {
-            const h2 x = as_h2((y & (0x00030003u << (2 * i))) | MAGIC);
+            const h2 x = as_h2((y & (0x00030003u << (2 * i))) | mv);
             const float inv = 1.0f / (float)(1 << (2 * i));
             const h2 s = {(_Float16)inv, (_Float16)inv};
             const h2 b = {(_Float16)(-1024.0f * inv), (_Float16)(-1024.0f * inv)};
@@ -83,11 +96,12 @@ struct Unpack<8> {
     __device__ static __forceinline__ Pairs run2(uint32_t w0, uint32_t w1)
     {
         const h2 one = {(_Float16)1.0f, (_Float16)1.0f}, m1024 = {(_Float16)-1024.0f, (_Float16)-1024.0f};
+        const uint32_t mv = magic_v();
         Pairs r;
 #pragma unroll
         for (int i = 0; i < 4; i++) {
             const uint32_t sel = 0x0C000C00u | ((uint32_t)(4 + i) << 16) | (uint32_t)i;
-            r.p[i] = __builtin_elementwise_fma(as_h2(perm(w1, w0, sel) | MAGIC), one, m1024);
+            r.p[i] = __builtin_elementwise_fma(as_h2(perm(w1, w0, sel) | mv), one, m1024);
         }
         return r;
     }
@@ -103,10 +117,11 @@ struct Unpack<3> {
                                             ((uint32_t)(r + 1) << 8) | (uint32_t)r);
         const uint32_t z2 = perm(hi, lo, 0x0C000000u | ((uint32_t)(r + 2) << 16) |
                                              ((uint32_t)(r + 2) << 8) | (uint32_t)(r + 1));
-        const h2 x0 = as_h2((z & 0x00700007u) | MAGIC);                 // c0 x1,  c4 x16
-        const h2 x1 = as_h2((z & 0x03800038u) | MAGIC);                 // c1 x8,  c5 x128
-        const h2 x2 = as_h2((z & 0x000001C0u) | (z2 & 0x001C0000u) | MAGIC);  // c2 x64, c6 x4
-        const h2 x3 = as_h2((z2 & 0x00E0000Eu) | MAGIC);                // c3 x2,  c7 x32
+        const uint32_t mv = magic_v();
+        const h2 x0 = as_h2((z & 0x00700007u) | mv);                    // c0 x1,  c4 x16
+        const h2 x1 = as_h2((z & 0x03800038u) | mv);                    // c1 x8,  c5 x128
+        const h2 x2 = as_h2((z & 0x000001C0u) | ((z2 & 0x001C0000u) | mv));  // c2 x64, c6 x4
+        const h2 x3 = as_h2((z2 & 0x00E0000Eu) | mv);                   // c3 x2,  c7 x32
         Pairs o;
         o.p[0] = __builtin_elementwise_fma(x0, h2{(_Float16)1.0f, (_Float16)0.0625f},
                                            h2{(_Float16)-1024.0f, (_Float16)-64.0f});
