@@ -2,7 +2,7 @@
 """Benchmark of the quantized KV-cache hot path on one MI355X.
 
 One step = the whole path over one batch of synthetic input: quantize every
-K and V cache of the workload (kvq_quantize), then attend over the packed
+K and V cache of the workload (kvq_quantize_kv: one launch per layer), then attend over the packed
 blocks (kvq_attend_decode, or kvq_attend_chunk for the restore + chunk
 workload).  Inputs are resident in HBM before timing; cache copies rotate
 so that no step reads what the 256 MB Infinity Cache still holds from the
@@ -593,9 +593,7 @@ def main():
             e0 = torch.cuda.Event(enable_timing=True) if record else None
             if record:
                 e0.record(stream)
-            cs_w[li].quantize("k", k)
-            if v is not None:
-                cs_w[li].quantize("v", v)
+            cs_w[li].quantize_kv(k, v)                # K and V in one launch
             e1 = torch.cuda.Event(enable_timing=True) if record else None
             if record:
                 e1.record(stream)
@@ -624,19 +622,18 @@ def main():
     ms_step = total_ms / args.steps
     tq = [m[0].elapsed_time(m[1]) for ms in all_marks for m in ms]   # per layer, K (+V)
     ta = [m[1].elapsed_time(m[2]) for ms in all_marks for m in ms]
-    n_launch_q = 1 if latent else 2
+    n_launch_q = 1                                    # one kvq_quantize_kv launch per layer
     # The dominant kernel's launch duration: ROOF_LAUNCHES quantize launches
     # back to back (rotating caches and sources) between one pair of events,
     # so the events' own overhead is spread over the run; each launch still
     # pays its dispatch gap.
-    ROOF_LAUNCHES = 24
+    ROOF_LAUNCHES = 16
     e_a, e_b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e_a.record(stream)
     for i in range(ROOF_LAUNCHES):
-        li = (i // 2) % len(layers)                   # every layer's widths, K then V
+        li = i % len(layers)                          # every layer's widths
         kv = srcs[i % n_src][li]
-        which = "k" if (i % 2 == 0 or kv[1] is None) else "v"
-        sets[i % R][li].quantize(which, kv[0] if which == "k" else kv[1])
+        sets[i % R][li].quantize_kv(kv[0], kv[1])
     e_b.record(stream)
     torch.cuda.synchronize()
     quant_launch_ms = e_a.elapsed_time(e_b) / ROOF_LAUNCHES

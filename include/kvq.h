@@ -109,6 +109,16 @@ uint64_t kvq_block_bytes(int32_t bits, int32_t n_heads, int32_t head_dim);
 int kvq_quantize(const kvq_layout *L, const kvq_store *dst, const uint16_t *src,
                  int64_t src_seq_tokens, void *stream);
 
+/* kvq_quantize of a layer's K and V caches in one launch (QKVShare,
+ * Metodologia: an agent's K and V groups are quantized together when its
+ * cache is packed for handoff).  The result is bit-exact to kvq_quantize(L, K,
+ * k_src, ...) followed by kvq_quantize(L, V, v_src, ...); both sources share
+ * src_seq_tokens and the layout's widths.  V == NULL quantizes K alone
+ * (v_src ignored), for a latent cache.
+ * Errors: as kvq_quantize; KVQ_EUNSUPPORTED when 2*n_seqs exceeds 65535. */
+int kvq_quantize_kv(const kvq_layout *L, const kvq_store *K, const kvq_store *V, const uint16_t *k_src,
+                    const uint16_t *v_src, int64_t src_seq_tokens, void *stream);
+
 /* Quantize on append, the window roll (CoMixKV, Abstract: a width is chosen
  * only for newly quantized blocks and the most recent states stay in native
  * precision; AgentMem, Abstract: each agent's cache keeps growing as the agent

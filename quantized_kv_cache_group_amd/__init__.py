@@ -24,7 +24,7 @@ KVQ_OK, KVQ_EINVAL, KVQ_ENOSPC, KVQ_EUNSUPPORTED, KVQ_EHIP = 0, -1, -2, -3, -4
 OUT_BF16, OUT_F32 = 0, 1
 WIDTHS = (2, 3, 4, 8)
 
-SYMBOLS = ("kvq_block_bytes", "kvq_quantize", "kvq_append", "kvq_dequantize", "kvq_card_bytes",
+SYMBOLS = ("kvq_block_bytes", "kvq_quantize", "kvq_quantize_kv", "kvq_append", "kvq_dequantize", "kvq_card_bytes",
            "kvq_card_gather", "kvq_card_scatter", "kvq_block_sensitivity", "kvq_allocate_widths",
            "kvq_decode_workspace", "kvq_attend_decode",
            "kvq_topk_workspace", "kvq_attend_decode_topk", "kvq_chunk_workspace", "kvq_attend_chunk",
@@ -65,6 +65,8 @@ def lib() -> ctypes.CDLL:
         L.kvq_block_bytes.restype = ctypes.c_uint64
         L.kvq_quantize.argtypes = [P, P, P, ctypes.c_int64, P]
         L.kvq_quantize.restype = ctypes.c_int
+        L.kvq_quantize_kv.argtypes = [P, P, P, P, P, ctypes.c_int64, P]
+        L.kvq_quantize_kv.restype = ctypes.c_int
         L.kvq_append.argtypes = [P, P, P, P, P, P, P, i32, i32, i32, P, P, P]
         L.kvq_append.restype = ctypes.c_int
         u64 = ctypes.c_uint64
@@ -244,6 +246,20 @@ class LayerCache:
         st = self.store(which)
         _check(lib().kvq_quantize(ctypes.byref(self._layout), ctypes.byref(st), _ptr(src),
                                   src.shape[1], _stream(stream)), "kvq_quantize")
+
+    def quantize_kv(self, k_src: torch.Tensor, v_src: torch.Tensor | None = None, stream=None):
+        """Quantize K and V sources bf16 [A][S][H][D] in one launch (v_src None
+        for a latent cache); bit-exact to quantize('k', ...) and quantize('v', ...)."""
+        for t in (k_src, v_src):
+            if t is not None:
+                assert t.dtype == torch.bfloat16 and t.is_contiguous() and t.dim() == 4
+                assert t.shape[0] == self.A and t.shape[2] == self.H and t.shape[3] == self.D
+        if v_src is not None:
+            assert not self.latent and v_src.shape == k_src.shape
+        kst, vst = self.store("k"), (self.store("v") if v_src is not None else None)
+        _check(lib().kvq_quantize_kv(ctypes.byref(self._layout), ctypes.byref(kst),
+                                     None if vst is None else ctypes.byref(vst), _ptr(k_src), _ptr(v_src),
+                                     k_src.shape[1], _stream(stream)), "kvq_quantize_kv")
 
     def append(self, k_new: torch.Tensor, v_new: torch.Tensor | None = None, keep_recent: int = 128,
                rope_new: torch.Tensor | None = None, stream=None):

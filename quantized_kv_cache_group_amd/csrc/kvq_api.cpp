@@ -133,6 +133,41 @@ int plan_attention(const kvq_layout *L, int n_q_heads, int rope_dim, int n_new, 
     return KVQ_OK;
 }
 
+// Shared by kvq_quantize (V == NULL) and kvq_quantize_kv: one launch over
+// every block of one or two stores.
+static int quantize_call(const kvq_layout *L, const kvq_store *K, const kvq_store *V, const uint16_t *k_src,
+                         const uint16_t *v_src, int64_t src_seq_tokens, void *stream)
+{
+    int st = check_layout(L);
+    if (st) return st;
+    const kvq_store *dst[2] = {K, V};
+    const uint16_t *src[2] = {k_src, v_src};
+    const int n = V ? 2 : 1;
+    for (int x = 0; x < n; x++) {
+        if (!dst[x] || !dst[x]->pool || !dst[x]->offset) {
+            if (L->max_blocks > 0) return KVQ_EINVAL;
+        } else if (!aligned(dst[x]->pool, 256) || !aligned(dst[x]->offset, 8)) {
+            return KVQ_EINVAL;
+        }
+        if (!src[x] || !aligned(src[x], 16)) return KVQ_EINVAL;
+    }
+    if (src_seq_tokens < (int64_t)L->max_blocks * 64 || (L->n_seqs > 1 && src_seq_tokens < 1))
+        return KVQ_EINVAL;
+    if ((int64_t)L->n_seqs * n > kMaxGrid) return KVQ_EUNSUPPORTED;
+    if (L->max_blocks == 0) return KVQ_OK;
+    QuantArgs a;
+    a.t = tables(L);
+    for (int x = 0; x < 2; x++) {
+        const int y = x < n ? x : 0;
+        a.offset[x] = dst[y]->offset;
+        a.pool[x] = dst[y]->pool;
+        a.src[x] = src[y];
+    }
+    a.src_seq_tokens = src_seq_tokens;
+    a.n_tensors = n;
+    return hip_status(launch_quantize(a, static_cast<hipStream_t>(stream)));
+}
+
 }  // namespace
 
 extern "C" {
@@ -147,24 +182,13 @@ uint64_t kvq_block_bytes(int32_t bits, int32_t n_heads, int32_t head_dim)
 int kvq_quantize(const kvq_layout *L, const kvq_store *dst, const uint16_t *src,
                  int64_t src_seq_tokens, void *stream)
 {
-    int st = check_layout(L);
-    if (st) return st;
-    if (!dst || !dst->pool || !dst->offset) {
-        if (L->max_blocks > 0) return KVQ_EINVAL;
-    } else if (!aligned(dst->pool, 256) || !aligned(dst->offset, 8)) {
-        return KVQ_EINVAL;
-    }
-    if (!src || !aligned(src, 16)) return KVQ_EINVAL;
-    if (src_seq_tokens < (int64_t)L->max_blocks * 64 || (L->n_seqs > 1 && src_seq_tokens < 1))
-        return KVQ_EINVAL;
-    if (L->max_blocks == 0) return KVQ_OK;
-    QuantArgs a;
-    a.t = tables(L);
-    a.offset = dst->offset;
-    a.pool = dst->pool;
-    a.src = src;
-    a.src_seq_tokens = src_seq_tokens;
-    return hip_status(launch_quantize(a, static_cast<hipStream_t>(stream)));
+    return quantize_call(L, dst, nullptr, src, nullptr, src_seq_tokens, stream);
+}
+
+int kvq_quantize_kv(const kvq_layout *L, const kvq_store *K, const kvq_store *V, const uint16_t *k_src,
+                    const uint16_t *v_src, int64_t src_seq_tokens, void *stream)
+{
+    return quantize_call(L, K, V, k_src, v_src, src_seq_tokens, stream);
 }
 
 int kvq_append(const kvq_layout *L, const kvq_store *K, const kvq_store *V,

@@ -23,12 +23,14 @@ struct Store {
     const uint16_t *window;
 };
 
+// One launch quantizes n_tensors (1 or 2: K then V) caches of one layout.
 struct QuantArgs {
     Tables t;
-    const uint64_t *offset;
-    uint8_t *pool;
-    const uint16_t *src;
+    const uint64_t *offset[2];
+    uint8_t *pool[2];
+    const uint16_t *src[2];
     int64_t src_seq_tokens;
+    int n_tensors;
 };
 
 struct DequantArgs {

@@ -207,11 +207,13 @@ __device__ __forceinline__ void quant_block(const uint16_t *__restrict__ src_blk
 template <int NG>
 __global__ __launch_bounds__(256) void quantize_kernel(QuantArgs a)
 {
-    const int h = blockIdx.x, j = blockIdx.y, s = blockIdx.z;
+    const int h = blockIdx.x, j = blockIdx.y;
+    const int x = blockIdx.z >= a.t.A ? 1 : 0;          // tensor: K, then V
+    const int s = blockIdx.z - x * a.t.A;
     if (j >= seq_blocks(a.t, s)) return;
     const int b = a.t.bits[(size_t)s * a.t.max_blocks + j];
-    uint8_t *blk = a.pool + a.offset[(size_t)s * a.t.max_blocks + j];
-    const uint16_t *src_blk = a.src + ((size_t)s * a.src_seq_tokens + (size_t)j * 64) * a.t.H * (NG * 64);
+    uint8_t *blk = a.pool[x] + a.offset[x][(size_t)s * a.t.max_blocks + j];
+    const uint16_t *src_blk = a.src[x] + ((size_t)s * a.src_seq_tokens + (size_t)j * 64) * a.t.H * (NG * 64);
     switch (b) {
     case 2: quant_block<2, NG>(src_blk, a.t.H, blk, h); break;
     case 3: quant_block<3, NG>(src_blk, a.t.H, blk, h); break;
@@ -492,7 +494,8 @@ __global__ __launch_bounds__(256) void dequantize_kernel(DequantArgs a)
 hipError_t launch_quantize(const QuantArgs &a, hipStream_t s)
 {
     if (a.t.max_blocks == 0) return hipSuccess;
-    dim3 grid(a.t.H, a.t.max_blocks, a.t.A);
+    if (a.n_tensors < 1 || a.n_tensors > 2 || (int64_t)a.t.A * a.n_tensors > 65535) return hipErrorInvalidValue;
+    dim3 grid(a.t.H, a.t.max_blocks, a.t.A * a.n_tensors);
     switch (a.t.D / 64) {
     case 1: quantize_kernel<1><<<grid, 256, 0, s>>>(a); break;
     case 2: quantize_kernel<2><<<grid, 256, 0, s>>>(a); break;

@@ -60,7 +60,7 @@ class Built:
 
 
 def build(H, D, lengths, bits=None, window=None, latent=False, rope_dim=0, k_src=None,
-          v_src=None, rope=None, seed=0, keep_recent=0, quantize_on_gpu=True) -> Built:
+          v_src=None, rope=None, seed=0, keep_recent=0, quantize_on_gpu=True, fused=False) -> Built:
     """lengths: tokens per sequence.  Full blocks are quantized, keeping at
     least ``keep_recent`` newest tokens (or ``window[a]`` tokens) in bf16."""
     A = len(lengths)
@@ -99,6 +99,7 @@ def build(H, D, lengths, bits=None, window=None, latent=False, rope_dim=0, k_src
     # GPU copy: quantize the same sources, copy windows and rope as storage.
     S = max(64 * maxb, 64)
     if quantize_on_gpu:
+        dev = {}
         for which, src in (("k", k_src), ("v", v_src)):
             if src is None:
                 continue
@@ -106,7 +107,12 @@ def build(H, D, lengths, bits=None, window=None, latent=False, rope_dim=0, k_src
             for a in range(A):
                 nq = 64 * n_blocks[a]
                 buf[a, :nq] = src[a][:nq]
-            cache.quantize(which, to_dev_bf16(buf))
+            dev[which] = to_dev_bf16(buf)
+        if fused:
+            cache.quantize_kv(dev["k"], dev.get("v"))
+        else:
+            for which, t in dev.items():
+                cache.quantize(which, t)
     for which, src in (("k", k_src), ("v", v_src)):
         if src is None:
             continue

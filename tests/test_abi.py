@@ -97,6 +97,24 @@ def test_quantize_rejects_bad_buffers():
     assert q(None, ctypes.byref(_store()), ctypes.c_void_p(FAKE), 256, None) == kvq.KVQ_EINVAL
 
 
+def test_quantize_kv_rejects():
+    L = _layout()
+    q = kvq.lib().kvq_quantize_kv
+    K, V = _store(), _store()
+    src = ctypes.c_void_p(FAKE)
+    assert q(ctypes.byref(L), ctypes.byref(K), ctypes.byref(V), src, None, 256, None) == kvq.KVQ_EINVAL
+    assert q(ctypes.byref(L), ctypes.byref(K), ctypes.byref(_store(pool=FAKE + 16)), src, src, 256,
+             None) == kvq.KVQ_EINVAL
+    assert q(ctypes.byref(L), ctypes.byref(K), ctypes.byref(V), src, ctypes.c_void_p(FAKE + 2), 256,
+             None) == kvq.KVQ_EINVAL
+    assert q(ctypes.byref(L), None, ctypes.byref(V), src, src, 256, None) == kvq.KVQ_EINVAL
+    assert q(ctypes.byref(L), ctypes.byref(K), ctypes.byref(V), src, src, 255, None) == kvq.KVQ_EINVAL
+    big = _layout(n_seqs=40000)
+    assert q(ctypes.byref(big), ctypes.byref(K), ctypes.byref(V), src, src, 256, None) == kvq.KVQ_EUNSUPPORTED
+    assert q(ctypes.byref(_layout(max_blocks=0)), ctypes.byref(K), ctypes.byref(V), src, src, 0,
+             None) == kvq.KVQ_OK
+
+
 def test_quantize_empty_layout_is_noop():
     L = _layout(max_blocks=0)
     assert kvq.lib().kvq_quantize(ctypes.byref(L), ctypes.byref(_store()), ctypes.c_void_p(FAKE), 0,

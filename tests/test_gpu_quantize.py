@@ -52,6 +52,21 @@ def test_quantize_bit_exact_mixed_widths(D, H):
     gpu_pool_matches(b)
 
 
+@pytest.mark.parametrize("D,H,latent", [(128, 8, False), (64, 2, False), (192, 3, False), (512, 1, True)])
+def test_quantize_kv_one_launch_bit_exact(D, H, latent):
+    """kvq_quantize_kv (K and V in one launch) against the oracle, with mixed
+    widths, ragged and empty sequences."""
+    rng = np.random.default_rng(7 * D + H)
+    lengths = [64 * 7, 64 * 2 + 5, 0, 64 * 4, 64]
+    window = [0, 5, 0, 0, 0]
+    nb = [(L - w) // 64 for L, w in zip(lengths, window)]
+    bits = [rng.choice(np.array([2, 3, 4, 8], np.uint8), size=n) for n in nb]
+    k_src = [_hard_values(L, H, D, 31 * a + D) for a, L in enumerate(lengths)]
+    v_src = None if latent else [syn.random_normal_bf16((L, H, D), 7 + a) for a, L in enumerate(lengths)]
+    b = build(H, D, lengths, bits=bits, window=window, latent=latent, k_src=k_src, v_src=v_src, fused=True)
+    gpu_pool_matches(b)
+
+
 @pytest.mark.parametrize("bits", [2, 3, 4, 8])
 def test_quantize_single_width_tiny(bits):
     w = syn.workload(0)
