@@ -71,7 +71,7 @@ COPY_BYTES = 1 << 30
 COUNTER_FACTOR = {"FETCH_SIZE": 2.0, "WRITE_SIZE": 1.0}
 TRAFFIC = {
     # (workload, kernel): (source file, sha256 prefix, FETCH_SIZE KiB, WRITE_SIZE KiB)
-    (1, "kvq quantize"): ("quantize.hip", "1f6432f8a756493d", 41040.6, 23041.2),
+    (1, "kvq quantize"): ("quantize.hip", "222ee04dd840777d", 82021.9, 46081.0),
 }
 
 
