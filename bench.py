@@ -610,16 +610,19 @@ def main():
     for i in range(args.warmup):
         step(i, False)
     torch.cuda.synchronize()
+    # The timed steps carry no events inside; the per-phase split below is a
+    # second pass with events between the phases.
     t_start = torch.cuda.Event(enable_timing=True)
     t_end = torch.cuda.Event(enable_timing=True)
-    all_marks = []
     t_start.record(stream)
     for i in range(args.steps):
-        all_marks.append(step(args.warmup + i, True))
+        step(args.warmup + i, False)
     t_end.record(stream)
     torch.cuda.synchronize()
     total_ms = t_start.elapsed_time(t_end)
     ms_step = total_ms / args.steps
+    all_marks = [step(args.warmup + args.steps + i, True) for i in range(args.steps)]
+    torch.cuda.synchronize()
     tq = [m[0].elapsed_time(m[1]) for ms in all_marks for m in ms]   # per layer, K (+V)
     ta = [m[1].elapsed_time(m[2]) for ms in all_marks for m in ms]
     n_launch_q = 1                                    # one kvq_quantize_kv launch per layer
