@@ -70,8 +70,13 @@ COPY_BYTES = 1 << 30
 # time; a changed source reports null until measured again.
 COUNTER_FACTOR = {"FETCH_SIZE": 2.0, "WRITE_SIZE": 1.0}
 TRAFFIC = {
-    # (workload, kernel): (source file, sha256 prefix, FETCH_SIZE KiB, WRITE_SIZE KiB)
-    (1, "kvq quantize"): ("quantize.hip", "222ee04dd840777d", 82021.9, 46081.0),
+    # (workload, call): (source files, sha256 prefix of their contents in that
+    # order, FETCH_SIZE KiB, WRITE_SIZE KiB), summed over the call's kernels
+    (1, "kvq quantize"): (("quantize.hip",), "222ee04dd840777d", 82021.9, 46081.0),
+    (2, "kvq quantize"): (("quantize.hip",), "222ee04dd840777d", 268213.8, 117415.0),
+    (3, "kvq attend_chunk"): (("chunk.hip",), "7e9bc99935b2e36f", 47185.6 + 16672.5, 35004.3 + 8192.0),
+    (4, "kvq attend_decode"): (("mla.hip", "decode_gqa.hip"), "dfc24c56db94b551",
+                               27112.9 + 4169.1, 8320.0 + 128.0),
 }
 
 
@@ -80,11 +85,13 @@ def traffic_bytes(workload: int, kernel: str):
     e = TRAFFIC.get((workload, kernel))
     if e is None:
         return None
-    src, sha, fetch_kib, write_kib = e
-    path = os.path.join(ROOT, "quantized_kv_cache_group_amd", "csrc", src)
-    with open(path, "rb") as f:
-        if hashlib.sha256(f.read()).hexdigest()[:16] != sha:
-            return None
+    srcs, sha, fetch_kib, write_kib = e
+    m = hashlib.sha256()
+    for src in srcs:
+        with open(os.path.join(ROOT, "quantized_kv_cache_group_amd", "csrc", src), "rb") as f:
+            m.update(f.read())
+    if m.hexdigest()[:16] != sha:
+        return None
     return (fetch_kib * COUNTER_FACTOR["FETCH_SIZE"] + write_kib * COUNTER_FACTOR["WRITE_SIZE"]) * 1024
 
 
@@ -581,66 +588,59 @@ def main():
     torch.cuda.synchronize()
 
     stream = torch.cuda.current_stream()
-    ev = []
 
-    def step(i, record):
+    def attend(c, li):
+        if w.n_new:
+            c.attend_chunk(qn, kn, vn, w.scale, out=out, workspace=ws)
+        else:
+            c.attend_decode(qs[li], w.scale, out=out, workspace=ws)
+
+    def step(i):
         cs_w = sets[i % R]
         cs_r = sets[(i + R // 2) % R]
         src = srcs[i % n_src]
-        marks = []
         for li in range(len(layers)):
             k, v = src[li]
-            e0 = torch.cuda.Event(enable_timing=True) if record else None
-            if record:
-                e0.record(stream)
             cs_w[li].quantize_kv(k, v)                # K and V in one launch
-            e1 = torch.cuda.Event(enable_timing=True) if record else None
-            if record:
-                e1.record(stream)
-            if w.n_new:
-                cs_r[li].attend_chunk(qn, kn, vn, w.scale, out=out, workspace=ws)
-            else:
-                cs_r[li].attend_decode(qs[li], w.scale, out=out, workspace=ws)
-            e2 = torch.cuda.Event(enable_timing=True) if record else None
-            if record:
-                e2.record(stream)
-                marks.append((e0, e1, e2))
-        return marks
+            attend(cs_r[li], li)
 
     for i in range(args.warmup):
-        step(i, False)
+        step(i)
     torch.cuda.synchronize()
-    # The timed steps carry no events inside; the per-phase split below is a
-    # second pass with events between the phases.
+    # The timed steps carry no events inside.
     t_start = torch.cuda.Event(enable_timing=True)
     t_end = torch.cuda.Event(enable_timing=True)
     t_start.record(stream)
     for i in range(args.steps):
-        step(args.warmup + i, False)
+        step(args.warmup + i)
     t_end.record(stream)
     torch.cuda.synchronize()
     total_ms = t_start.elapsed_time(t_end)
     ms_step = total_ms / args.steps
-    all_marks = [step(args.warmup + args.steps + i, True) for i in range(args.steps)]
-    torch.cuda.synchronize()
-    tq = [m[0].elapsed_time(m[1]) for ms in all_marks for m in ms]   # per layer, K (+V)
-    ta = [m[1].elapsed_time(m[2]) for ms in all_marks for m in ms]
     n_launch_q = 1                                    # one kvq_quantize_kv launch per layer
-    # The dominant kernel's launch duration: ROOF_LAUNCHES quantize launches
-    # back to back (rotating caches and sources) between one pair of events,
-    # so the events' own overhead is spread over the run; each launch still
-    # pays its dispatch gap.
+    # Per-call durations of the two phases: ROOF_LAUNCHES quantize launches,
+    # then ROOF_LAUNCHES attention calls, each back to back (rotating caches
+    # and sources) between one pair of events on the launch stream, so the
+    # events' own overhead is spread over the run; each launch still pays
+    # its dispatch gap.
     ROOF_LAUNCHES = 16
-    e_a, e_b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e_a.record(stream)
-    for i in range(ROOF_LAUNCHES):
+
+    def timed(fn):
+        e_a, e_b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e_a.record(stream)
+        for i in range(ROOF_LAUNCHES):
+            fn(i)
+        e_b.record(stream)
+        torch.cuda.synchronize()
+        return e_a.elapsed_time(e_b) / ROOF_LAUNCHES
+
+    def quant_one(i):
         li = i % len(layers)                          # every layer's widths
         kv = srcs[i % n_src][li]
         sets[i % R][li].quantize_kv(kv[0], kv[1])
-    e_b.record(stream)
-    torch.cuda.synchronize()
-    quant_launch_ms = e_a.elapsed_time(e_b) / ROOF_LAUNCHES
-    attn_ms = float(np.mean(ta))
+
+    quant_launch_ms = timed(quant_one)
+    attn_ms = timed(lambda i: attend(sets[(i + R // 2) % R][i % len(layers)], i % len(layers)))
     step_bytes = q_bytes + a_bytes
     value = step_bytes / (ms_step * 1e-3) / 1e9
     quant_gbs = (q_bytes / len(layers) / n_launch_q) / (quant_launch_ms * 1e-3) / 1e9
