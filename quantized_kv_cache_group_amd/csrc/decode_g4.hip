@@ -51,7 +51,15 @@ using namespace dev;
 typedef _Float16 h4 __attribute__((ext_vector_type(4)));
 typedef short s4 __attribute__((ext_vector_type(4)));
 
-constexpr int VS = 64 + 8;                    // LDS row stride of one 64-dim V set (halves)
+constexpr int VS = 64;                        // LDS row stride of one 64-dim V set (halves)
+
+// 16-byte chunk c of V row r sits at chunk c ^ vswz(r).  gfx950's LDS serves
+// a 16-byte write for 8 lanes per cycle over 32 banks and an 8-byte read for
+// 32 lanes over 64 banks; with this swap the row stores (8 consecutive rows,
+// one chunk) and the transposed reads (4 consecutive rows x 8 chunks per 32
+// lanes) both spread over distinct banks.  A 72-half pitch without the swap
+// left every transposed read two-way conflicted.
+__device__ __forceinline__ int vswz(int r) { return ((r & 1) ^ ((r & 2) << 1) ^ ((r >> 1) & 2)) << 3; }
 
 // (x & mask) | magic.  Written in plain C so the compiler sees every VALU
 // write that feeds a matrix instruction (it inserts the wait states such a
@@ -231,13 +239,17 @@ __device__ __forceinline__ void pv_round(State<NG> &st, PF pa, _Float16 *vr, VF 
     const int lane = threadIdx.x;
     // lane i of each 16-lane group addresses token 4S + i/4, positions
     // 16(l/16) + 4(i%4)..+3 of the set
-    const _Float16 *vb = vr + ((lane & 15) >> 2) * VS + 16 * (lane >> 4) + 4 * (lane & 3);
+    // Rows 4S + (lane&15)/4: bit 2 of the row is S&1, so even and odd S use
+    // two bases.
+    const int r0 = (lane & 15) >> 2, col = 16 * (lane >> 4) + 4 * (lane & 3);
+    const _Float16 *vb0 = vr + r0 * VS + (col ^ vswz(r0));
+    const _Float16 *vb1 = vr + r0 * VS + (col ^ vswz(r0 + 4));
 #pragma unroll
     for (int hh = 0; hh < NG; hh++) {
 #pragma unroll
         for (int cc = 0; cc < 8; cc++) {
             const Pairs pr = vx(8 * hh + cc);
-            *reinterpret_cast<h8 *>(vr + lane * VS + 8 * cc) =
+            *reinterpret_cast<h8 *>(vr + lane * VS + ((8 * cc) ^ vswz(lane))) =
                 h8{pr.p[0][0], pr.p[0][1], pr.p[1][0], pr.p[1][1], pr.p[2][0], pr.p[2][1], pr.p[3][0], pr.p[3][1]};
         }
         wave_sync();
@@ -247,7 +259,7 @@ __device__ __forceinline__ void pv_round(State<NG> &st, PF pa, _Float16 *vr, VF 
     ACC = __builtin_amdgcn_mfma_f32_4x4x4f16(                                                         \
         a,                                                                                            \
         __builtin_bit_cast(h4, __builtin_amdgcn_ds_read_tr16_b64_v4i16(                               \
-                                   (__attribute__((address_space(3))) s4 *)(vb + 4 * (S) * VS))),   \
+                                   (__attribute__((address_space(3))) s4 *)(((S) & 1 ? vb1 : vb0) + 4 * (S) * VS))), \
         ACC, 4, S, 0)
         KVQ_PV(acc0, 0); KVQ_PV(acc1, 1); KVQ_PV(acc0, 2); KVQ_PV(acc1, 3);
         KVQ_PV(acc0, 4); KVQ_PV(acc1, 5); KVQ_PV(acc0, 6); KVQ_PV(acc1, 7);
