@@ -46,8 +46,10 @@ def parse():
     p.add_argument("--copy-calibration", action="store_true",
                    help="only run a plain 1 GiB device copy (the reference for the HBM byte counters)")
     p.add_argument("--topk", type=int, default=0, metavar="K",
-                   help="time top-K sparse decode (K of 64 blocks per agent) on the Llama 10-agent "
-                        "caches, beside the full decode, instead of the workload step")
+                   help="time top-K sparse decode (K of the T/64 blocks per agent, T = --topk-tokens) "
+                        "on Llama 10-agent caches, beside the full decode, instead of the workload step")
+    p.add_argument("--topk-tokens", type=int, default=4096, metavar="T",
+                   help="cached tokens per agent for --topk (a multiple of 64)")
     p.add_argument("--alloc", action="store_true",
                    help="time block sensitivity (GPU) and the budgeted width allocation (host) on the "
                         "Gemma mixed-width shape instead of the workload step")
@@ -319,11 +321,12 @@ def append_bench(args):
 
 
 def topk_bench(args):
-    """Top-K sparse decode on the Llama-3.1-8B layer shape, 10 agents x 4096
-    Q4 tokens (64 blocks each): block scores over every K block, selection,
-    then decode over the K kept blocks; timed beside the full decode of the
-    same caches.  Algorithmic bytes: all K blocks (scores), the kept blocks'
-    K and V again, q and out.  Cache copies rotate past the 256 MB cache."""
+    """Top-K sparse decode on the Llama-3.1-8B layer shape, 10 agents x T
+    Q4 tokens (T/64 blocks each, T = --topk-tokens, 4096 by default): block
+    scores over every K block, selection, then decode over the K kept blocks;
+    timed beside the full decode of the same caches.  Algorithmic bytes: all
+    K blocks (scores), the kept blocks' K and V again, q and out.  Cache
+    copies rotate past the 256 MB cache."""
     import torch
     import kvq_synth as syn
     import quantized_kv_cache_group_amd as kvq
@@ -332,13 +335,18 @@ def topk_bench(args):
     torch.cuda.set_device(0)
     w = syn.workload(1)
     A, H, D, Hq, K = w.n_agents, w.n_kv_heads, w.head_dim, w.n_q_heads, args.topk
+    T = args.topk_tokens
+    if T < 64 or T % 64:
+        print("--topk-tokens must be a positive multiple of 64", file=sys.stderr)
+        sys.exit(2)
+    nblk = T // 64
     blk = kvq.block_bytes(4, H, D)
-    one = 2 * A * w.n_blocks[0] * blk
+    one = 2 * A * nblk * blk
     R = min(12, max(2, int(np.ceil(2 * MALL_BYTES / one)) + 1))
-    caches = [kvq.LayerCache(H, D, w.n_blocks, w.n_window, None) for _ in range(R)]
+    caches = [kvq.LayerCache(H, D, [nblk] * A, [0] * A, None) for _ in range(R)]
     g = torch.Generator(device="cuda")
     g.manual_seed(5)
-    src = [torch.randn((A, 4096, H, D), generator=g, device="cuda").to(torch.bfloat16) for _ in range(2)]
+    src = [torch.randn((A, T, H, D), generator=g, device="cuda").to(torch.bfloat16) for _ in range(2)]
     for i, c in enumerate(caches):
         c.quantize("k", src[i % 2])
         c.quantize("v", src[(i + 1) % 2])
@@ -364,14 +372,14 @@ def topk_bench(args):
     sp_us = run(True, args.steps)
     run(False, args.warmup)
     full_us = run(False, args.steps)
-    kb = min(K, w.n_blocks[0])
-    algo = A * (w.n_blocks[0] * blk + 2 * kb * blk) + A * Hq * D * 2 + A * Hq * D * 4
+    kb = min(K, nblk)
+    algo = A * (nblk * blk + 2 * kb * blk) + A * Hq * D * 2 + A * Hq * D * 4
     gbs = algo / (sp_us * 1e-6) / 1e9
     res = {"metric": "top-K sparse decode GB/s", "value": round(gbs, 2), "unit": "GB/s", "n_gpus": 1,
            "steps": args.steps, "warmup": args.warmup, "higher_is_better": True, "dtype": "f32",
            "data": "synthetic",
-           "config": {"workload": f"llama8b-10agent-q4-top{K}", "agents": A, "q_heads": Hq, "kv_heads": H,
-                      "head_dim": D, "blocks": w.n_blocks[0], "top_k": K, "bits": 4, "rotated_copies": R},
+           "config": {"workload": f"llama8b-10agent-{T}tok-q4-top{K}", "agents": A, "q_heads": Hq,
+                      "kv_heads": H, "head_dim": D, "blocks": nblk, "top_k": K, "bits": 4, "rotated_copies": R},
            "sparse_us": round(sp_us, 3), "full_decode_us": round(full_us, 3),
            "speedup_vs_full": round(full_us / sp_us, 3), "bytes_per_call": algo,
            "roofline": {"kernel": "kvq attend_decode_topk", "bound": "hbm", "achieved": round(gbs, 2),

@@ -96,59 +96,174 @@ __global__ __launch_bounds__(256) void block_scores(TopkArgs p)
 
 // Selection: one workgroup per sequence.  Block i is kept when fewer than
 // Kk = min(top_k, nb) blocks rank above it (higher score, or equal score and
-// lower index); kept blocks are compacted in block order.
+// lower index); kept blocks are compacted in block order.  The Kk-th largest
+// score comes from a radix select over order-preserving 32-bit keys (four
+// 8-bit digits, an LDS histogram per digit), so the cost is linear in nb;
+// blocks with exactly that score are taken in index order.
 constexpr int MAXB = 16384;
+
+// Key of a finite score: unsigned order equals float order (-0 is made +0
+// first, so equal scores give equal keys).
+__device__ __forceinline__ uint32_t score_key(float f)
+{
+    const uint32_t u = __float_as_uint(f + 0.0f);
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// Inclusive prefix sum across the 64 lanes of a wave.
+__device__ __forceinline__ int wave_incl_scan(int v)
+{
+    const int lane = threadIdx.x & 63;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const int t = __shfl_up(v, o);
+        if (lane >= o) v += t;
+    }
+    return v;
+}
+
+// Exclusive prefix sum of one value per thread over the 256 threads, in
+// thread order; *total gets the sum.  wsum: 4 ints of LDS.
+__device__ __forceinline__ int block_exclusive_scan(int v, int *wsum, int *total)
+{
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int incl = wave_incl_scan(v);
+    if (lane == 63) wsum[wave] = incl;
+    __syncthreads();
+    int off = 0, tot = 0;
+#pragma unroll
+    for (int w = 0; w < 4; w++) {
+        const int x = wsum[w];
+        off += w < wave ? x : 0;
+        tot += x;
+    }
+    *total = tot;
+    __syncthreads();
+    return off + incl - v;
+}
 
 __global__ __launch_bounds__(256) void select_blocks(TopkArgs p)
 {
-    __shared__ uint8_t keep[MAXB];
-    __shared__ int cnt[256];
-    const int a = blockIdx.x, tid = threadIdx.x;
+    __shared__ uint32_t key[MAXB];
+    __shared__ int hist[256];
+    __shared__ int wsum[4];
+    __shared__ int sel[2];                              // digit, candidates above it
+    const int a = blockIdx.x, tid = threadIdx.x, lane = tid & 63;
     int nb = p.t.n_blocks[a];
     nb = nb < 0 ? 0 : (nb > p.t.max_blocks ? p.t.max_blocks : nb);
     const int Kk = nb < p.top_k ? nb : p.top_k;
-    // a block's score: the max over its score_stride entries, reduced once into LDS
-    __shared__ float sc[MAXB];
-    const int S = p.score_stride;
-    const float *s = p.scores + (size_t)a * p.t.max_blocks * S;
-    for (int i = tid; i < nb; i += 256) {
-        float m = s[(size_t)i * S];
-        for (int e = 1; e < S; e++) m = fmaxf(m, s[(size_t)i * S + e]);
-        sc[i] = m;
-    }
-    __syncthreads();
-    for (int i = tid; i < nb; i += 256) {
-        const float si = sc[i];
-        int rank = 0;
-        for (int jj = 0; jj < nb; jj++) {
-            const float sj = sc[jj];
-            rank += (sj > si) || (sj == si && jj < i);
-        }
-        keep[i] = rank < Kk;
-    }
-    __syncthreads();
-    // each thread owns a contiguous run of blocks; exclusive scan of the counts
-    const int per = (nb + 255) / 256, b0 = tid * per, b1 = min(b0 + per, nb);
-    int c = 0;
-    for (int i = b0; i < b1; i++) c += keep[i];
-    cnt[tid] = c;
-    __syncthreads();
-    for (int o = 1; o < 256; o <<= 1) {
-        const int v = tid >= o ? cnt[tid - o] : 0;
-        __syncthreads();
-        cnt[tid] += v;
-        __syncthreads();
-    }
-    int pos = cnt[tid] - c;
+    // Each thread owns a contiguous run of blocks [b0, b1); the table
+    // entries of its first PF blocks are loaded now, beside the scores, so
+    // the compaction at the end waits on no load.
+    constexpr int PF = 4;
+    const int per = (nb + 255) / 256, b0 = min(tid * per, nb), b1 = min(b0 + per, nb);
     const size_t in = (size_t)a * p.t.max_blocks, out = (size_t)a * p.top_k;
+    uint8_t pbits[PF];
+    uint64_t pko[PF], pvo[PF];
+#pragma unroll
+    for (int k = 0; k < PF; k++) {
+        const int i = min(b0 + k, max(nb - 1, 0));
+        pbits[k] = p.t.bits[in + i];
+        pko[k] = p.k.offset[in + i];
+        pvo[k] = p.sel_voff ? p.v.offset[in + i] : 0;
+    }
+    // a block's score: the max over its score_stride entries (the first 16
+    // loads are independent of each other)
+    const int S = p.score_stride;
+    const float *sp = p.scores + (size_t)a * p.t.max_blocks * S;
+    for (int i = tid; i < nb; i += 256) {
+        const float *r = sp + (size_t)i * S;
+        float m = r[0];
+#pragma unroll
+        for (int e = 1; e < 16; e++)
+            if (e < S) m = fmaxf(m, r[e]);
+        for (int e = 16; e < S; e++) m = fmaxf(m, r[e]);
+        key[i] = score_key(m);
+    }
+    // Radix select, most significant digit first: T = the Kk-th largest key;
+    // `need` ends as the number of keys equal to T that are kept.
+    uint32_t prefix = 0, mask = 0;
+    int need = Kk;
+    if (Kk > 0) {
+        for (int shift = 24; shift >= 0; shift -= 8) {
+            hist[tid] = 0;
+            __syncthreads();
+            for (int i = tid; i < nb; i += 256) {
+                const uint32_t u = key[i];
+                if ((u & mask) == prefix) atomicAdd(&hist[(u >> shift) & 255u], 1);
+            }
+            __syncthreads();
+            if (tid < 64) {
+                // lane l holds digits 255-4l .. 252-4l, largest first
+                int c[4], sum = 0;
+#pragma unroll
+                for (int k = 0; k < 4; k++) {
+                    c[k] = hist[255 - 4 * lane - k];
+                    sum += c[k];
+                }
+                int above = wave_incl_scan(sum) - sum;      // candidates with a larger digit
+#pragma unroll
+                for (int k = 0; k < 4; k++) {
+                    if (above < need && above + c[k] >= need) {
+                        sel[0] = 255 - 4 * lane - k;
+                        sel[1] = above;
+                    }
+                    above += c[k];
+                }
+            }
+            __syncthreads();
+            need -= sel[1];
+            prefix |= (uint32_t)sel[0] << shift;
+            mask |= 255u << shift;
+        }
+    }
+    __syncthreads();
+    const uint32_t T = prefix;
+    // ties (key == T) ranked in index order, then the kept flags, then their
+    // compaction, over each thread's run
+    int ties = 0;
+    for (int i = b0; i < b1; i++) ties += (Kk > 0 && key[i] == T);
+    int tot;
+    int tie_rank = block_exclusive_scan(ties, wsum, &tot);
+    int kept = 0;
+    for (int i = b0; i < b1; i++) {
+        const uint32_t u = key[i];
+        bool k = false;
+        if (Kk > 0) {
+            if (u > T) k = true;
+            else if (u == T) k = tie_rank++ < need;
+        }
+        kept += k;
+    }
+    // second walk with the kept positions
+    int pos = block_exclusive_scan(kept, wsum, &tot);
+    tie_rank -= ties;                                   // back to this run's first tie rank
     int32_t *user = p.selected ? p.selected + (size_t)a * p.sel_stride : nullptr;
     for (int i = b0; i < b1; i++) {
-        if (!keep[i]) continue;
+        const uint32_t u = key[i];
+        bool k = false;
+        if (Kk > 0) {
+            if (u > T) k = true;
+            else if (u == T) k = tie_rank++ < need;
+        }
+        if (!k) continue;
+        const int r = i - b0;
+        uint8_t bw;
+        uint64_t ko, vo;
+        if (r < PF) {
+            bw = r == 0 ? pbits[0] : r == 1 ? pbits[1] : r == 2 ? pbits[2] : pbits[3];
+            ko = r == 0 ? pko[0] : r == 1 ? pko[1] : r == 2 ? pko[2] : pko[3];
+            vo = r == 0 ? pvo[0] : r == 1 ? pvo[1] : r == 2 ? pvo[2] : pvo[3];
+        } else {
+            bw = p.t.bits[in + i];
+            ko = p.k.offset[in + i];
+            vo = p.sel_voff ? p.v.offset[in + i] : 0;
+        }
         p.sel_idx[out + pos] = i;
         if (user) user[pos] = i;
-        p.sel_bits[out + pos] = p.t.bits[in + i];
-        p.sel_koff[out + pos] = p.k.offset[in + i];
-        if (p.sel_voff) p.sel_voff[out + pos] = p.v.offset[in + i];
+        p.sel_bits[out + pos] = bw;
+        p.sel_koff[out + pos] = ko;
+        if (p.sel_voff) p.sel_voff[out + pos] = vo;
         pos++;
     }
     for (int q = Kk + tid; q < p.top_k; q += 256) {
