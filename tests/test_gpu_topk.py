@@ -112,3 +112,36 @@ def test_topk_latent_rope():
     got, sel = _run(b, q, scale, 6)
     _check_selection(b, q, scale, 6, sel)
     close(got, _ref_sparse(b, q, scale, sel), what="topk latent+rope")
+
+
+def test_topk_many_blocks_per_thread():
+    """More blocks than the selection's 256 threads (several blocks per
+    thread in the scans), mixed widths, one short sequence."""
+    H, D, G, K = 2, 64, 4, 37
+    lengths = [64 * 600, 64 * 300 + 17, 64 * 20]
+    window = [0, 17, 0]
+    nb = [(L - w) // 64 for L, w in zip(lengths, window)]
+    rng = np.random.default_rng(71)
+    bits = [rng.choice(np.array([2, 3, 4, 8], np.uint8), size=n) for n in nb]
+    b = build(H, D, lengths, bits=bits, window=window, seed=71)
+    q = syn.random_normal_bf16((3, G * H, D), 72, scale=2.0)
+    scale = D ** -0.5
+    got, sel = _run(b, q, scale, K)
+    _check_selection(b, q, scale, K, sel)
+    close(got, _ref_sparse(b, q, scale, sel), what="topk 600 blocks")
+
+
+@pytest.mark.parametrize("n_blocks,K,G,D", [(8, 3, 4, 128), (300, 100, 4, 64), (300, 100, 8, 64), (520, 257, 2, 256)])
+def test_topk_ties_keep_lowest_indices(n_blocks, K, G, D):
+    """Every block holds the same keys, so every score ties exactly (the same
+    arithmetic on the same bytes): the kept set must be blocks 0..K-1."""
+    H = 2
+    blk = syn.random_normal_bf16((64, H, D), 73)
+    k = np.tile(blk, (n_blocks, 1, 1))
+    v = syn.random_normal_bf16((64 * n_blocks, H, D), 74)
+    b = build(H, D, [64 * n_blocks], window=[0], k_src=[k], v_src=[v], seed=73)
+    q = syn.random_normal_bf16((1, G * H, D), 75)
+    scale = D ** -0.5
+    got, sel = _run(b, q, scale, K)
+    assert np.array_equal(sel[0], np.arange(K)), sel[0][:10]
+    close(got, _ref_sparse(b, q, scale, sel), what=f"topk ties {n_blocks}/{K}")
