@@ -145,3 +145,17 @@ def test_topk_ties_keep_lowest_indices(n_blocks, K, G, D):
     got, sel = _run(b, q, scale, K)
     assert np.array_equal(sel[0], np.arange(K)), sel[0][:10]
     close(got, _ref_sparse(b, q, scale, sel), what=f"topk ties {n_blocks}/{K}")
+
+
+@pytest.mark.parametrize("nb,K,D,H,G", [(1300, 400, 64, 1, 4), (2100, 1100, 64, 2, 2)])
+def test_topk_long_runs_per_thread(nb, K, D, H, G):
+    """Over 1 024 blocks per sequence: each selection thread owns runs of more
+    than four blocks, past the table entries it loads ahead."""
+    rng = np.random.default_rng(nb)
+    bits = [rng.choice(np.array([2, 3, 4, 8], np.uint8), size=nb)]
+    b = build(H, D, [64 * nb], bits=bits, window=[0], seed=nb)
+    q = syn.random_normal_bf16((1, G * H, D), 76, scale=2.0)
+    scale = D ** -0.5
+    got, sel = _run(b, q, scale, K)
+    _check_selection(b, q, scale, K, sel)
+    close(got, _ref_sparse(b, q, scale, sel), what=f"topk {nb} blocks")
