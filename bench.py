@@ -50,6 +50,8 @@ def parse():
                         "on Llama 10-agent caches, beside the full decode, instead of the workload step")
     p.add_argument("--topk-tokens", type=int, default=4096, metavar="T",
                    help="cached tokens per agent for --topk (a multiple of 64)")
+    p.add_argument("--restore", action="store_true",
+                   help="time the restore (dequantize to bf16) of the 32 768-token Q4 cache, K then V")
     p.add_argument("--alloc", action="store_true",
                    help="time block sensitivity (GPU) and the budgeted width allocation (host) on the "
                         "Gemma mixed-width shape instead of the workload step")
@@ -444,6 +446,65 @@ def alloc_bench(args):
     print(json.dumps(res), flush=True)
 
 
+def restore_bench(args):
+    """Restore (dequantize) of the restore + chunk workload's cache: one
+    sequence of 32 768 Q4 tokens, 8 KV heads of 128 dims, K then V restored
+    to bf16 rows.  Algorithmic bytes per (K, V) pair: codes and metadata read
+    (2 x 18 MiB) + bf16 rows written (2 x 64 MiB).  Caches and outputs rotate
+    past the 256 MB last-level cache."""
+    import torch
+    import kvq_synth as syn
+    import quantized_kv_cache_group_amd as kvq
+
+    kvq.lib()
+    torch.cuda.set_device(0)
+    w = syn.workload(3)
+    A, H, D = w.n_agents, w.n_kv_heads, w.head_dim
+    S = 64 * max(w.n_blocks)
+    R = 3
+    g = torch.Generator(device="cuda")
+    g.manual_seed(9)
+    caches = []
+    for r in range(R):
+        c = kvq.LayerCache(H, D, w.n_blocks, w.n_window, None)
+        k = torch.randn((A, S, H, D), generator=g, device="cuda").to(torch.bfloat16)
+        v = torch.randn((A, S, H, D), generator=g, device="cuda").to(torch.bfloat16)
+        c.quantize_kv(k, v)
+        caches.append(c)
+        del k, v
+    outs = [[torch.empty((A, S, H, D), dtype=torch.bfloat16, device="cuda") for _ in range(2)] for _ in range(R)]
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+
+    def run(steps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for i in range(steps):
+            c, o = caches[i % R], outs[i % R]
+            c.dequantize("k", o[0])
+            c.dequantize("v", o[1])
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / steps
+    run(args.warmup)
+    us = run(args.steps)
+    blk = kvq.block_bytes(4, H, D)
+    algo = 2 * (A * w.n_blocks[0] * blk + A * S * H * D * 2)
+    gbs = algo / (us * 1e-6) / 1e9
+    res = {"metric": "kvq_dequantize (restore) GB/s", "value": round(gbs, 2), "unit": "GB/s", "n_gpus": 1,
+           "steps": args.steps, "warmup": args.warmup, "higher_is_better": True, "dtype": "f32",
+           "data": "synthetic",
+           "config": {"workload": "llama8b-32k-restore-kv-bf16", "agents": A, "kv_heads": H, "head_dim": D,
+                      "cache_tokens": S, "bits": 4, "rotated_copies": R},
+           "us_per_kv_pair": round(us, 3), "bytes_per_kv_pair": algo,
+           # one launch restores one tensor: half the pair's bytes in half its time
+           "roofline": {"kernel": "kvq dequantize", "bound": "hbm", "achieved": round(gbs, 2),
+                        "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
+                        "algo_bytes_per_launch": algo // 2,
+                        "traffic": traffic_bytes(3, "kvq dequantize")}}
+    print(json.dumps(res), flush=True)
+
+
 def card_bench(args):
     """CacheCard gather (cache -> contiguous device image) and scatter (image
     -> cache) for each of the 10 agents of the Llama-3.1-8B layer shape (4096
@@ -517,6 +578,9 @@ def card_bench(args):
 
 def main():
     args = parse()
+    if args.restore:
+        restore_bench(args)
+        return
     if args.card:
         card_bench(args)
         return

@@ -31,6 +31,7 @@ struct QuantArgs {
     const uint16_t *src[2];
     int64_t src_seq_tokens;
     int n_tensors;
+    int j0;             // first block of this launch (set by the launcher)
 };
 
 struct DequantArgs {
@@ -39,6 +40,7 @@ struct DequantArgs {
     void *dst;
     int64_t dst_seq_tokens;
     int out_f32;
+    int j0;             // first block or window tile of this launch (set by the launcher)
 };
 
 // Attention over quantized + window (+ new) keys.  Decode is the case

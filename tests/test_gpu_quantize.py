@@ -151,3 +151,24 @@ def test_quantize_scale_sweep(bits):
     k = syn.bf16_bits(g.reshape(L, H, D))
     b = build(H, D, [L], bits=[np.full(n_blocks, bits, np.uint8)], k_src=[k], v_src=[k])
     gpu_pool_matches(b)
+
+
+def test_quantize_restore_past_grid_limit():
+    """One sequence of 65 600 blocks (4.2M tokens, one 64-dim head): more
+    blocks than one grid dimension holds, so quantize and restore stride over
+    the blocks.  The whole pool is compared byte for byte; restored rows are
+    compared on the first blocks and on every block past the 65 535th."""
+    H, D, nblk = 1, 64, 65600
+    rng = np.random.default_rng(65600)
+    bits = [rng.choice(np.array([2, 3, 4, 8], np.uint8), size=nblk)]
+    b = build(H, D, [64 * nblk], bits=bits, window=[0], latent=True, seed=11)
+    gpu_pool_matches(b)
+    c = b.cache
+    out = torch.full((1, 64 * nblk, H, D), 7.0, dtype=torch.bfloat16, device="cuda")
+    c.dequantize("k", out)
+    s = b.seq(0)
+    for j0, j1 in ((0, 8), (65530, nblk)):
+        want = oracle.restore_seq(b.ref_pool, s["bits"][j0:j1], s["koff"][j0:j1], None, H, D)
+        got = out[0, 64 * j0:64 * j1].cpu().view(torch.int16).numpy().view(np.uint16)
+        wb = oracle.f32_to_bf16_bits(want.ravel()).reshape(want.shape)
+        assert np.array_equal(got, wb), (j0, j1)
