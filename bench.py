@@ -76,8 +76,9 @@ COUNTER_FACTOR = {"FETCH_SIZE": 2.0, "WRITE_SIZE": 1.0}
 TRAFFIC = {
     # (workload, call): (source files, sha256 prefix of their contents in that
     # order, FETCH_SIZE KiB, WRITE_SIZE KiB), summed over the call's kernels
-    (1, "kvq quantize"): (("quantize.hip",), "222ee04dd840777d", 82021.9, 46081.0),
-    (2, "kvq quantize"): (("quantize.hip",), "222ee04dd840777d", 268213.8, 117415.0),
+    (1, "kvq quantize"): (("quantize.hip",), "9a85b9518ea7fcfa", 82007.1, 46080.1),
+    (2, "kvq quantize"): (("quantize.hip",), "9a85b9518ea7fcfa", 268014.8, 119916.2),
+    (3, "kvq dequantize"): (("quantize.hip",), "9a85b9518ea7fcfa", 9271.8, 65554.1),
     (3, "kvq attend_chunk"): (("chunk.hip",), "7e9bc99935b2e36f", 47185.6 + 16672.5, 35004.3 + 8192.0),
     (4, "kvq attend_decode"): (("mla.hip", "decode_gqa.hip"), "dfc24c56db94b551",
                                27112.9 + 4169.1, 8320.0 + 128.0),
@@ -694,17 +695,22 @@ def main():
     # then ROOF_LAUNCHES attention calls, each back to back (rotating caches
     # and sources) between one pair of events on the launch stream, so the
     # events' own overhead is spread over the run; each launch still pays
-    # its dispatch gap.
+    # its dispatch gap.  The median of five such runs is reported.
     ROOF_LAUNCHES = 16
 
-    def timed(fn):
-        e_a, e_b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e_a.record(stream)
-        for i in range(ROOF_LAUNCHES):
-            fn(i)
-        e_b.record(stream)
-        torch.cuda.synchronize()
-        return e_a.elapsed_time(e_b) / ROOF_LAUNCHES
+    def timed(fn, reps=5):
+        # median over reps runs of ROOF_LAUNCHES calls: one run is short
+        # (well under a millisecond) and a single sample can be an outlier
+        per = []
+        for _ in range(reps):
+            e_a, e_b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e_a.record(stream)
+            for i in range(ROOF_LAUNCHES):
+                fn(i)
+            e_b.record(stream)
+            torch.cuda.synchronize()
+            per.append(e_a.elapsed_time(e_b) / ROOF_LAUNCHES)
+        return float(np.median(per))
 
     def quant_one(i):
         li = i % len(layers)                          # every layer's widths
