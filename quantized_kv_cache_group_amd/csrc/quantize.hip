@@ -282,64 +282,57 @@ __device__ __forceinline__ const uint16_t *stream_piece(const uint16_t *win_a, c
     return (t < W ? win_a + (size_t)t * ts : new_a + (size_t)(t - W) * ts) + (size_t)h * width + col;
 }
 
-// Blocks: one workgroup per (new block i, head h, sequence a), all groups of
-// the head, K and V loads issued together.  Blocks only read the stream, so
-// they run side by side; the window moves in the next launch.
+// Blocks: one workgroup per (new block i, tensor, head h, sequence a), all
+// groups of the head; x = 2i + tensor (K, V), or i for a latent cache.
+// Blocks only read the stream, so they run side by side; the window moves in
+// the next launch.
 template <int NG>
 __global__ __launch_bounds__(256) void append_blocks(AppendArgs p)
 {
     constexpr int D = NG * 64;
-    const int i = wg_x(), h = wg_y(), a = wg_z();
+    const int n_kv = p.v_pool ? 2 : 1;
+    const int kv = wg_x() % n_kv, i = wg_x() / n_kv, h = wg_y(), a = wg_z();
     const int H = p.t.H;
     int nb, W, k, W2;
     append_plan(p, a, nb, W, k, W2);
     if (i >= k) return;
     const size_t e = (size_t)a * p.t.max_blocks + nb + i;
-    const int B = p.t.bits[e];
+    const uint16_t *win_a = kv ? p.v_window : p.k_window;
+    if (win_a) win_a += (size_t)a * p.t.window_cap * H * D;
+    const uint16_t *new_a = (kv ? p.v_new : p.k_new) + (size_t)a * p.n_new * H * D;
     const int sub = tid_x() & 7;
-    const int n_kv = p.v_pool ? 2 : 1;
-    uint4 raw[2][2 * NG];
+    uint4 raw[2 * NG];
 #pragma unroll
-    for (int kv = 0; kv < 2; kv++) {
-        if (kv >= n_kv) break;
-        const uint16_t *win_a = kv ? p.v_window : p.k_window;
-        if (win_a) win_a += (size_t)a * p.t.window_cap * H * D;
-        const uint16_t *new_a = (kv ? p.v_new : p.k_new) + (size_t)a * p.n_new * H * D;
-#pragma unroll
-        for (int kk = 0; kk < 2 * NG; kk++) {
-            const int gi = piece_group(kk);
-            const int r = gi / NG, g = gi % NG;
-            raw[kv][kk] = *reinterpret_cast<const uint4 *>(
-                stream_piece(win_a, new_a, (size_t)H * D, W, 64 * i + r, h, D, 64 * g + 8 * sub));
-        }
+    for (int kk = 0; kk < 2 * NG; kk++) {
+        const int gi = piece_group(kk);
+        const int r = gi / NG, g = gi % NG;
+        raw[kk] = stream_load16(stream_piece(win_a, new_a, (size_t)H * D, W, 64 * i + r, h, D, 64 * g + 8 * sub));
     }
-#pragma unroll
-    for (int kv = 0; kv < 2; kv++) {
-        if (kv >= n_kv) break;
-        uint8_t *blk = (kv ? p.v_pool : p.k_pool) + (kv ? p.v_offset : p.k_offset)[e];
-        switch (B) {
-        case 2: quant_rows<2, NG>(raw[kv], blk, H, h); break;
-        case 3: quant_rows<3, NG>(raw[kv], blk, H, h); break;
-        case 4: quant_rows<4, NG>(raw[kv], blk, H, h); break;
-        case 8: quant_rows<8, NG>(raw[kv], blk, H, h); break;
-        default: break;                             // precondition violation: nothing written
-        }
+    const int B = p.t.bits[e];
+    uint8_t *blk = (kv ? p.v_pool : p.k_pool) + (kv ? p.v_offset : p.k_offset)[e];
+    switch (B) {
+    case 2: quant_rows<2, NG>(raw, blk, H, h); break;
+    case 3: quant_rows<3, NG>(raw, blk, H, h); break;
+    case 4: quant_rows<4, NG>(raw, blk, H, h); break;
+    case 8: quant_rows<8, NG>(raw, blk, H, h); break;
+    default: break;                                 // precondition violation: nothing written
     }
 }
 
-// Window: one workgroup per (slice, head, sequence), slice g < D/64 the
-// 64-dim group g of K and V.  window[u] = T[64k + u] for u < W2, in rounds of
-// WR tokens: a round loads all of its source pieces into registers, waits at
-// a barrier, then stores.  A round writes positions [r0, r0+WR) and reads
-// [64k + r0, 64k + r0 + WR): its own overlap is ordered by the barrier, and
-// it never writes what a later round reads (those start at 64k + r0 + WR >=
-// r0 + WR), so one barrier per round suffices (one round for windows of up to
-// WR tokens).  When k == 0 the old window rows are already in place and only
-// the new tokens are written, with no overlap.  The last slice (rope_dim 64)
-// writes the new tokens' rope rows, which are indexed by token position and
-// so never move.
+// Window: window[u] = T[64k + u] for u < W2.  Workgroups per (slice, row
+// chunk, head, sequence), slice g < D/64 the 64-dim group g of K and V, the
+// last slice (rope_dim 64) the new tokens' rope rows, which are indexed by
+// token position and so never move.  The old window rows read are
+// [64k, W) and the rows written [0, W2) (only [W, W2) when k == 0): when
+// these overlap, one workgroup per slice moves the rows in ordered rounds of
+// WR tokens (a round loads all of its source pieces into registers, waits at
+// a barrier, then stores; a round writes [r0, r0+WR) and reads
+// [64k + r0, 64k + r0 + WR), so it never writes what a later round reads);
+// otherwise every chunk of CR rows is moved by its own workgroup.
 constexpr int WR = 192;                              // window rows per round
 constexpr int WR_PER = WR * 8 / 256;                 // 16-byte pieces per lane and round
+constexpr int CR = 32;                               // rows per chunk: one 16-byte piece per lane
+__host__ __device__ __forceinline__ int window_chunks(int window_cap) { return window_cap > CR ? (window_cap + CR - 1) / CR : 1; }
 
 template <int NKV>
 __device__ __forceinline__ void window_rounds(const AppendArgs &p, int a, int h, int g, int W, int k, int W2)
@@ -378,7 +371,8 @@ __device__ __forceinline__ void window_rounds(const AppendArgs &p, int a, int h,
 
 __global__ __launch_bounds__(256) void append_window(AppendArgs p)
 {
-    const int g = wg_x(), h = wg_y(), a = wg_z();
+    const int RC = window_chunks(p.t.window_cap);
+    const int g = wg_x() / RC, c = wg_x() % RC, h = wg_y(), a = wg_z();
     const int H = p.t.H, D = p.t.D, NG = D / 64, R = p.rope_dim;
     const int tid = tid_x();
     int nb, W, k, W2;
@@ -390,15 +384,30 @@ __global__ __launch_bounds__(256) void append_window(AppendArgs p)
         const int n = (int)min((int64_t)p.n_new, room);
         uint16_t *dst = p.rope + ((size_t)a * rope_tokens + (size_t)64 * nb + W) * H * R;
         const uint16_t *src = p.rope_new + (size_t)a * p.n_new * H * R;
-        for (int idx = tid; idx < n * 8; idx += 256) {
+        for (int idx = c * 256 + tid; idx < n * 8; idx += RC * 256) {
             const int i = idx >> 3, col = 8 * (idx & 7);
             *reinterpret_cast<uint4 *>(dst + ((size_t)i * H + h) * R + col) =
                 *reinterpret_cast<const uint4 *>(src + ((size_t)i * H + h) * R + col);
         }
         return;
     }
-    if (p.v_pool) window_rounds<2>(p, a, h, g, W, k, W2);
-    else window_rounds<1>(p, a, h, g, W, k, W2);
+    const int nkv = p.v_pool ? 2 : 1;
+    if (k > 0 && 64 * k < W && 64 * k < W2) {       // reads and writes overlap
+        if (c == 0) {
+            if (nkv == 2) window_rounds<2>(p, a, h, g, W, k, W2);
+            else window_rounds<1>(p, a, h, g, W, k, W2);
+        }
+        return;
+    }
+    const int u = c * CR + (tid >> 3), col = 8 * (tid & 7);
+    if (u < (k == 0 ? W : 0) || u >= W2) return;
+    for (int kv = 0; kv < nkv; kv++) {
+        uint16_t *win_a = (kv ? p.v_window : p.k_window) + (size_t)a * p.t.window_cap * H * D;
+        const uint16_t *new_a = (kv ? p.v_new : p.k_new) + (size_t)a * p.n_new * H * D;
+        const uint4 v = *reinterpret_cast<const uint4 *>(
+            stream_piece(win_a, new_a, (size_t)H * D, W, 64 * k + u, h, D, 64 * g + col));
+        *reinterpret_cast<uint4 *>(win_a + ((size_t)u * H + h) * D + 64 * g + col) = v;
+    }
 }
 
 // New counts, after every slice has read the old ones.
@@ -562,9 +571,10 @@ hipError_t launch_append(const AppendArgs &a, hipStream_t s)
     const int64_t kmax = a.t.window_cap + (int64_t)a.n_new > a.keep
                              ? (a.t.window_cap + (int64_t)a.n_new - a.keep) / 64 : 0;
     const int64_t kgrid = kmax < a.t.max_blocks ? kmax : a.t.max_blocks;
-    if (kgrid > 0x7fffffff) return hipErrorInvalidValue;
+    const int n_kv = a.v_pool ? 2 : 1;
+    if (kgrid * n_kv > 0x7fffffff) return hipErrorInvalidValue;
     if (kgrid > 0) {
-        dim3 grid((unsigned)kgrid, a.t.H, a.t.A);
+        dim3 grid((unsigned)(kgrid * n_kv), a.t.H, a.t.A);
         switch (a.t.D / 64) {
         case 1: append_blocks<1><<<grid, 256, 0, s>>>(a); break;
         case 2: append_blocks<2><<<grid, 256, 0, s>>>(a); break;
@@ -580,7 +590,7 @@ hipError_t launch_append(const AppendArgs &a, hipStream_t s)
         if (e != hipSuccess) return e;
     }
     if (a.t.window_cap > 0 || a.rope_dim) {
-        dim3 grid(a.t.D / 64 + (a.rope_dim ? 1 : 0), a.t.H, a.t.A);
+        dim3 grid((unsigned)((a.t.D / 64 + (a.rope_dim ? 1 : 0)) * window_chunks(a.t.window_cap)), a.t.H, a.t.A);
         append_window<<<grid, 256, 0, s>>>(a);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;

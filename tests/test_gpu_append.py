@@ -167,3 +167,22 @@ def test_append_keep_zero_and_small_keep():
     for i, n in enumerate([1, 54, 1, 128]):
         t.append(n, 7, seed=4000 + 10 * i)
         t.check(f"keep=7 call {i}")
+
+
+def test_append_window_move_cases():
+    """Every way the window can move, each checked against the oracle: old
+    rows moved to the front with no overlap (64k < W, 64k >= W2: chunks in
+    parallel), overlapping moves (ordered rounds), new rows only (k == 0),
+    and a window made entirely of new rows (64k >= W)."""
+    t = Twin(2, 128, nb0=[0, 1, 0], nw0=[150, 140, 40], max_blocks=12, cap=200, seed=13)
+    t.check("initial")
+    # (keep, n_new) per call; the comments give sequence 0's (W, k, W2)
+    calls = [(0, 10),      # W=150, T=160: k=2, 64k=128 < W, W2=32 <= 128: disjoint move of old rows
+             (0, 5),       # W=32, T=37: k=0: new rows appended in place
+             (20, 150),    # W=37, T=187: k=2, 64k=128 >= W: new rows only
+             (100, 120),   # W=59, T=179: k=1, 64k=64 >= W
+             (137, 90),    # W=115, T=205: k=1, 64k=64 < W, W2=141 > 64: overlapping, ordered rounds
+             (137, 30)]    # W=141, T=171: k=0 (keep + 63 <= window_cap bounds keep)
+    for i, (keep, n) in enumerate(calls):
+        t.append(n, keep, seed=5000 + 10 * i)
+        t.check(f"move case {i} (keep={keep}, n_new={n})")
