@@ -187,7 +187,6 @@ __device__ __forceinline__ void quant_lane(const uint4 raw, int lane, uint8_t *g
         }
     }
     if (sub == 0) *meta_word = (uint32_t)sh | ((uint32_t)bh << 16);
-    (void)lane;
 }
 
 // Group index of this lane's k-th 16-byte piece inside a (block, head): a

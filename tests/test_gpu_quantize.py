@@ -172,3 +172,27 @@ def test_quantize_restore_past_grid_limit():
         got = out[0, 64 * j0:64 * j1].cpu().view(torch.int16).numpy().view(np.uint16)
         wb = oracle.f32_to_bf16_bits(want.ravel()).reshape(want.shape)
         assert np.array_equal(got, wb), (j0, j1)
+
+
+def test_restore_window_tiles_in_second_launch():
+    """65 530 blocks plus a 600-token window: the restore's work items (blocks,
+    then 64-token window tiles) number 65 540, so the last window tiles fall
+    in the second launch.  Restored rows of the last blocks and of the whole
+    window are compared with the oracle, in fp32 and bf16."""
+    H, D, nblk, nw = 1, 64, 65530, 600
+    rng = np.random.default_rng(65530)
+    bits = [rng.choice(np.array([2, 3, 4, 8], np.uint8), size=nblk)]
+    b = build(H, D, [64 * nblk + nw], bits=bits, window=[nw], latent=True, seed=12)
+    c = b.cache
+    s = b.seq(0)
+    j0 = nblk - 3
+    want = oracle.restore_seq(b.ref_pool, s["bits"][j0:], s["koff"][j0:], s["kw"], H, D)
+    for dt in (torch.float32, torch.bfloat16):
+        out = torch.full((1, 64 * nblk + c.window_cap, H, D), 7.0, dtype=dt, device="cuda")
+        c.dequantize("k", out)
+        tail = out[0, 64 * j0:64 * nblk + nw].cpu()
+        if dt == torch.float32:
+            assert np.array_equal(tail.numpy().view(np.uint32), want.view(np.uint32))
+        else:
+            wb = oracle.f32_to_bf16_bits(want.ravel()).reshape(want.shape)
+            assert np.array_equal(tail.view(torch.int16).numpy().view(np.uint16), wb)
