@@ -141,8 +141,11 @@ int kvq_quantize_kv(const kvq_layout *L, const kvq_store *K, const kvq_store *V,
  *                 t), so the roll moves none of them: new token i is written
  *                 at row 64*nb + W + i from rope_new bf16 [A][n_new][H][rope_dim].
  *   n_blocks_out, n_window_out  device int32 [A]; they may be L->n_blocks and
- *                 L->n_window (written after every read); n_window_out may
- *                 be NULL when window_cap == 0.
+ *                 L->n_window (written after every read, in a launch of their
+ *                 own); n_window_out may be NULL when window_cap == 0.  Outputs
+ *                 that overlap neither input count array are written by the
+ *                 window launch, one launch fewer per call (a caller can keep
+ *                 two count arrays and alternate them between calls).
  *   keep_recent   >= 0 with keep_recent + 63 <= window_cap, so the window
  *                 always fits; with window_cap == 0, keep_recent must be 0
  *                 and n_new a multiple of 64.

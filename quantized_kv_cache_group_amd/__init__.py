@@ -206,8 +206,11 @@ class LayerCache:
         self.slots_host = [self.max_blocks if future_bits is not None else n for n in self.n_blocks_host]
         self.pool_bytes = max(pos, 256)
         dev = torch.device(device)
-        self.n_blocks = torch.tensor(self.n_blocks_host, dtype=torch.int32, device=dev)
-        self.n_window = torch.tensor(self.n_window_host, dtype=torch.int32, device=dev)
+        # two sets of device counts: append writes the other set and then
+        # makes it current, so its kernels never overwrite counts they read
+        self._nb_buf = [torch.tensor(self.n_blocks_host, dtype=torch.int32, device=dev) for _ in range(2)]
+        self._nw_buf = [torch.tensor(self.n_window_host, dtype=torch.int32, device=dev) for _ in range(2)]
+        self._cur = 0
         self.bits = torch.from_numpy(bits_tab).to(dev)
         self.offset = torch.from_numpy(off.view(np.int64)).to(dev)
         self.k_pool = torch.zeros(self.pool_bytes, dtype=torch.uint8, device=dev)
@@ -226,6 +229,16 @@ class LayerCache:
     # ---- descriptors ------------------------------------------------------
     def layout(self) -> Layout:
         return self._layout
+
+    @property
+    def n_blocks(self) -> torch.Tensor:
+        """Device int32 [A]: current quantized block counts."""
+        return self._nb_buf[self._cur]
+
+    @property
+    def n_window(self) -> torch.Tensor:
+        """Device int32 [A]: current bf16 window token counts."""
+        return self._nw_buf[self._cur]
 
     def store(self, which: str) -> Store | None:
         if which == "v" and self.latent:
@@ -262,12 +275,15 @@ class LayerCache:
                                      k_src.shape[1], _stream(stream)), "kvq_quantize_kv")
 
     def append(self, k_new: torch.Tensor, v_new: torch.Tensor | None = None, keep_recent: int = 128,
-               rope_new: torch.Tensor | None = None, stream=None):
+               rope_new: torch.Tensor | None = None, stream=None, in_place: bool = False):
         """Append k_new/v_new bf16 [A][n][H][D] (rope_new [A][n][H][rope_dim])
         to the windows; every full 64-token block beyond the keep_recent newest
         tokens is quantized into the next block slot (its width and offset are
-        the table entries set at construction).  Updates the device counts in
-        place and the host mirrors by the same rule."""
+        the table entries set at construction).  The new device counts go to
+        the other of two count buffers, which becomes current (two launches
+        per call), or with in_place=True overwrite the current ones (a third
+        launch writes them after every read); the host mirrors follow the
+        same rule."""
         n = int(k_new.shape[1])
         for t in (k_new, v_new, rope_new):
             if t is not None:
@@ -276,12 +292,16 @@ class LayerCache:
         if not self.latent:
             assert v_new is not None
         kst, vst = self.store("k"), self.store("v")
+        nxt = self._cur if in_place else 1 - self._cur
         _check(lib().kvq_append(ctypes.byref(self._layout), ctypes.byref(kst),
                                 None if vst is None else ctypes.byref(vst), _ptr(k_new),
                                 _ptr(v_new if not self.latent else None), _ptr(self.rope),
                                 _ptr(rope_new), self.rope_dim, n, int(keep_recent),
-                                _ptr(self.n_blocks), _ptr(self.n_window), _stream(stream)),
+                                _ptr(self._nb_buf[nxt]), _ptr(self._nw_buf[nxt]), _stream(stream)),
                "kvq_append")
+        self._cur = nxt
+        self._layout.n_blocks = self.n_blocks.data_ptr()
+        self._layout.n_window = self.n_window.data_ptr()
         for a in range(self.A):
             nb, w = self.n_blocks_host[a], self.n_window_host[a]
             total = w + n

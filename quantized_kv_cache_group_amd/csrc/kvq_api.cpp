@@ -237,6 +237,22 @@ int kvq_append(const kvq_layout *L, const kvq_store *K, const kvq_store *V,
     a.keep = keep_recent;
     a.n_blocks_out = n_blocks_out;
     a.n_window_out = L->window_cap > 0 ? n_window_out : nullptr;
+    // With outputs that overlap no count the kernels read, the window launch
+    // writes the new counts and the separate counts launch is skipped.
+    {
+        const size_t nbytes = (size_t)L->n_seqs * sizeof(int32_t);
+        auto overlap = [nbytes](const void *x, const void *y) {
+            if (!x || !y) return false;
+            const char *p = static_cast<const char *>(x), *q = static_cast<const char *>(y);
+            return p < q + nbytes && q < p + nbytes;
+        };
+        const void *ins[2] = {L->n_blocks, L->window_cap > 0 ? L->n_window : nullptr};
+        const void *outs[2] = {a.n_blocks_out, a.n_window_out};
+        bool alias = overlap(outs[0], outs[1]);
+        for (const void *o : outs)
+            for (const void *i : ins) alias = alias || overlap(o, i);
+        a.counts_in_window = (!alias && (L->window_cap > 0 || rope_dim)) ? 1 : 0;
+    }
     return hip_status(launch_append(a, static_cast<hipStream_t>(stream)));
 }
 

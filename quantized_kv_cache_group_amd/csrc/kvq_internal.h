@@ -109,6 +109,7 @@ struct AppendArgs {
     int rope_dim;
     int n_new, keep;
     int32_t *n_blocks_out, *n_window_out;
+    int counts_in_window;   // outputs alias no count the kernels read: the window launch writes them
 };
 
 // Top-K block selection for sparse decode: scores, then compacted tables.

@@ -376,6 +376,10 @@ __global__ __launch_bounds__(256) void append_window(AppendArgs p)
     const int tid = tid_x();
     int nb, W, k, W2;
     append_plan(p, a, nb, W, k, W2);
+    if (p.counts_in_window && wg_x() == 0 && h == 0 && tid == 0) {
+        p.n_blocks_out[a] = nb + k;
+        if (p.n_window_out) p.n_window_out[a] = W2;
+    }
     if (g >= NG) {
         // token W + i of the stream is sequence position 64*nb + W + i
         const size_t rope_tokens = (size_t)64 * p.t.max_blocks + p.t.window_cap;
@@ -409,7 +413,8 @@ __global__ __launch_bounds__(256) void append_window(AppendArgs p)
     }
 }
 
-// New counts, after every slice has read the old ones.
+// New counts, after every slice has read the old ones (a launch of its own
+// when the outputs are the counts the kernels read).
 __global__ void append_counts(AppendArgs p)
 {
     const int a = wg_x() * 256 + tid_x();
@@ -593,6 +598,7 @@ hipError_t launch_append(const AppendArgs &a, hipStream_t s)
         append_window<<<grid, 256, 0, s>>>(a);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
+        if (a.counts_in_window) return hipSuccess;
     }
     append_counts<<<(a.t.A + 255) / 256, 256, 0, s>>>(a);
     return hipGetLastError();

@@ -70,13 +70,13 @@ class Twin:
             self.seqs.append(s)
         torch.cuda.synchronize()
 
-    def append(self, n, keep, seed):
+    def append(self, n, keep, seed, in_place=False):
         A, H, D = self.A, self.H, self.D
         kn = syn.random_normal_bf16((A, n, H, D), seed)
         vn = None if self.latent else syn.random_normal_bf16((A, n, H, D), seed + 1)
         rn = syn.random_normal_bf16((A, n, H, self.R), seed + 2) if self.R else None
         self.c.append(to_dev_bf16(kn), None if vn is None else to_dev_bf16(vn), keep,
-                      None if rn is None else to_dev_bf16(rn))
+                      None if rn is None else to_dev_bf16(rn), in_place=in_place)
         for a, s in enumerate(self.seqs):
             s["nb"], s["nw"] = oracle.append_seq(s["kp"], s["vp"], self.widths[a], s["koff"], s["voff"], s["nb"],
                                                  s["kw"] if self.cap else None,
@@ -129,13 +129,15 @@ class Twin:
         return out
 
 
-@pytest.mark.parametrize("D", [64, 128, 256])
-def test_append_rolls_match_oracle(D):
+@pytest.mark.parametrize("D,in_place", [(64, False), (128, False), (256, False), (128, True)])
+def test_append_rolls_match_oracle(D, in_place):
+    """Counts written to the other count buffer by the window launch, or
+    (in_place) over the counts the kernels read, by a launch of their own."""
     H = 2
     t = Twin(H, D, nb0=[0, 2, 1], nw0=[0, 100, 191], max_blocks=14, cap=191, seed=D)
     t.check("initial")
     for i, n in enumerate([1, 63, 64, 65, 0, 200, 1, 130]):
-        t.append(n, 128, seed=1000 + 10 * i)
+        t.append(n, 128, seed=1000 + 10 * i, in_place=in_place)
         t.check(f"D={D} call {i} (n_new={n})")
     q = syn.random_normal_bf16((3, 4 * H, D), 77)
     got = t.c.attend_decode(to_dev_bf16(q), D ** -0.5)
@@ -147,7 +149,7 @@ def test_append_latent_rope_matches_oracle():
     t = Twin(1, 512, nb0=[3, 0], nw0=[150, 20], max_blocks=12, cap=191, seed=5, latent=True, rope_dim=64)
     t.check("initial")
     for i, n in enumerate([1, 41, 64, 300]):
-        t.append(n, 128, seed=2000 + 10 * i)
+        t.append(n, 128, seed=2000 + 10 * i, in_place=(i == 2))
         t.check(f"latent call {i}")
     q = syn.random_normal_bf16((2, 16, 576), 78)
     got = t.c.attend_decode(to_dev_bf16(q), 576 ** -0.5)
@@ -158,7 +160,7 @@ def test_append_latent_rope_matches_oracle():
 def test_append_without_window():
     t = Twin(4, 128, nb0=[1, 0], nw0=[0, 0], max_blocks=6, cap=0, seed=9)
     for i, n in enumerate([64, 128, 0, 64]):
-        t.append(n, 0, seed=3000 + 10 * i)
+        t.append(n, 0, seed=3000 + 10 * i, in_place=(i % 2 == 1))
         t.check(f"no-window call {i}")
 
 
