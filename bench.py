@@ -76,9 +76,9 @@ COUNTER_FACTOR = {"FETCH_SIZE": 2.0, "WRITE_SIZE": 1.0}
 TRAFFIC = {
     # (workload, call): (source files, sha256 prefix of their contents in that
     # order, FETCH_SIZE KiB, WRITE_SIZE KiB), summed over the call's kernels
-    (1, "kvq quantize"): (("quantize.hip",), "51701546bb64618f", 82007.1, 46080.1),
-    (2, "kvq quantize"): (("quantize.hip",), "51701546bb64618f", 268014.8, 119916.2),
-    (3, "kvq dequantize"): (("quantize.hip",), "51701546bb64618f", 9271.8, 65554.1),
+    (1, "kvq quantize"): (("quantize.hip",), "80dc430f5391874b", 82007.1, 46080.1),
+    (2, "kvq quantize"): (("quantize.hip",), "80dc430f5391874b", 268014.8, 119916.2),
+    (3, "kvq dequantize"): (("quantize.hip",), "80dc430f5391874b", 9271.8, 65554.1),
     (3, "kvq attend_chunk"): (("chunk.hip",), "7e9bc99935b2e36f", 47185.6 + 16672.5, 35004.3 + 8192.0),
     (4, "kvq attend_decode"): (("mla.hip", "decode_gqa.hip"), "dfc24c56db94b551",
                                27112.9 + 4169.1, 8320.0 + 128.0),
