@@ -116,9 +116,15 @@ def _ptr(t):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
 
 
+_raw_stream = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+
+
 def _stream(stream=None):
-    s = stream if stream is not None else torch.cuda.current_stream()
-    return ctypes.c_void_p(s.cuda_stream)
+    if stream is not None:
+        return ctypes.c_void_p(stream.cuda_stream)
+    if _raw_stream is not None:          # no Stream object per call
+        return ctypes.c_void_p(_raw_stream(torch.cuda.current_device()))
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
 
 
 def block_bytes(bits: int, n_heads: int, head_dim: int) -> int:
@@ -222,6 +228,7 @@ class LayerCache:
         if rope_dim:
             self.rope = torch.zeros((A, self.max_blocks * 64 + self.window_cap, self.H, rope_dim),
                                     dtype=torch.bfloat16, device=dev)
+        self._stores = {}
         self._layout = Layout(A, self.H, self.D, self.max_blocks, self.window_cap,
                               self.n_blocks.data_ptr(), self.n_window.data_ptr(),
                               self.bits.data_ptr())
@@ -243,9 +250,12 @@ class LayerCache:
     def store(self, which: str) -> Store | None:
         if which == "v" and self.latent:
             return None
-        pool = self.k_pool if which == "k" else self.v_pool
-        win = self.k_window if which == "k" else self.v_window
-        return Store(self.offset.data_ptr(), pool.data_ptr(), win.data_ptr())
+        st = self._stores.get(which)
+        if st is None:                   # the tensors behind a store never move
+            pool = self.k_pool if which == "k" else self.v_pool
+            win = self.k_window if which == "k" else self.v_window
+            st = self._stores[which] = Store(self.offset.data_ptr(), pool.data_ptr(), win.data_ptr())
+        return st
 
     @property
     def lengths(self):
