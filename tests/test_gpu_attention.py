@@ -49,6 +49,36 @@ def test_decode_edge_lengths():
     close(got, want, what="edges")
 
 
+def test_decode_more_sequences_than_a_wave():
+    """70 sequences (the split plan scans them 64 at a time), many empty or
+    window-only, windows of 0..200 tokens, mixed widths."""
+    rng = np.random.default_rng(70)
+    H, D, G, A = 2, 64, 2, 70
+    nb = [int(v) for v in rng.integers(0, 12, size=A)]
+    window = [int(v) for v in rng.integers(0, 201, size=A)]
+    for a in range(0, A, 9):
+        nb[a], window[a] = 0, 0
+    lengths = [64 * n + w for n, w in zip(nb, window)]
+    bits = [rng.choice(np.array([2, 3, 4, 8], np.uint8), size=n) for n in nb]
+    b = build(H, D, lengths, bits=bits, window=window, seed=70)
+    q = syn.random_normal_bf16((A, G * H, D), 17)
+    got = _decode(b, q, 0.125)
+    for a in range(0, A, 9):
+        assert np.all(got[a] == 0.0)
+    close(got, ref_decode(b, q, 0.125), what="70 sequences")
+
+
+def test_decode_long_window():
+    """A 9 000-token bf16 window: more than 128 rounds of 64 tokens, so each
+    window split takes 128 tokens."""
+    H, D, G = 1, 128, 4
+    lengths = [9000 + 64 * 3, 500]
+    window = [9000, 500 - 64 * 7]
+    b = build(H, D, lengths, window=window, seed=71)
+    q = syn.random_normal_bf16((2, G * H, D), 18)
+    close(_decode(b, q, D ** -0.5), ref_decode(b, q, D ** -0.5), what="long window")
+
+
 @pytest.mark.parametrize("D", [64, 256, 512])
 def test_decode_mixed_widths_window(D):
     rng = np.random.default_rng(D)
