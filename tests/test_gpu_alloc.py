@@ -13,8 +13,11 @@ from parity import to_dev_bf16
 pytestmark = pytest.mark.gpu
 
 
-@pytest.mark.parametrize("H,D,G", [(8, 128, 4), (8, 256, 2), (2, 64, 8), (1, 512, 16)])
-def test_sensitivity_matches_oracle(H, D, G):
+@pytest.mark.parametrize("H,D,G,q_offset", [(8, 128, 4, 0), (8, 256, 2, 0), (2, 64, 8, 0), (1, 512, 16, 0),
+                                            (8, 512, 1, 0), (2, 128, 2, 1)])
+def test_sensitivity_matches_oracle(H, D, G, q_offset):
+    """(8, 512): per-block tables past 48 KB of LDS, and q_offset 1: a query
+    not 16-byte aligned; both take the thread-per-row kernel."""
     A, nb = 3, 5
     T = 64 * nb + 17                                     # rows past the last block are ignored
     rng = np.random.default_rng(H * D)
@@ -24,7 +27,8 @@ def test_sensitivity_matches_oracle(H, D, G):
     vb = syn.random_normal_bf16((A, T, H, D), 2)
     q = syn.random_normal_bf16((A, G * H, D), 3)
     scale = D ** -0.5
-    got = kvq.block_sensitivity(to_dev_bf16(kb), to_dev_bf16(vb), to_dev_bf16(q), scale, n_blocks=nb)
+    qd = to_dev_bf16(np.concatenate([np.zeros(q_offset, np.uint16), q.ravel()]))[q_offset:].view(q.shape)
+    got = kvq.block_sensitivity(to_dev_bf16(kb), to_dev_bf16(vb), qd, scale, n_blocks=nb)
     torch.cuda.synchronize()
     got = got.cpu().numpy()
     for a in range(A):
