@@ -82,10 +82,11 @@ TRAFFIC = {
     (3, "kvq attend_chunk"): (("chunk.hip",), "7e9bc99935b2e36f", 47185.6 + 16672.5, 35004.3 + 8192.0),
     (4, "kvq attend_decode"): (("mla.hip", "decode_gqa.hip"), "dfc24c56db94b551",
                                27112.9 + 4169.1, 8320.0 + 128.0),
+    ("alloc", "kvq block_sensitivity"): (("alloc.hip",), "daa276e1c505e00b", 430498.4, 62.0),
 }
 
 
-def traffic_bytes(workload: int, kernel: str):
+def traffic_bytes(workload, kernel: str):
     import hashlib
     e = TRAFFIC.get((workload, kernel))
     if e is None:
@@ -319,7 +320,7 @@ def append_bench(args):
            "bytes_per_call": round(total / args.steps),
            "roofline": {"kernel": "kvq append", "bound": "hbm", "achieved": round(gbs, 2),
                         "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
-                        "traffic": None}}
+                        "traffic": traffic_bytes("alloc", "kvq block_sensitivity")}}
     print(json.dumps(res), flush=True)
 
 
@@ -387,7 +388,7 @@ def topk_bench(args):
            "speedup_vs_full": round(full_us / sp_us, 3), "bytes_per_call": algo,
            "roofline": {"kernel": "kvq attend_decode_topk", "bound": "hbm", "achieved": round(gbs, 2),
                         "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
-                        "traffic": None}}
+                        "traffic": traffic_bytes("alloc", "kvq block_sensitivity")}}
     print(json.dumps(res), flush=True)
 
 
@@ -443,7 +444,7 @@ def alloc_bench(args):
            "width_counts": {str(b): int((widths == b).sum()) for b in (2, 3, 4, 8)},
            "roofline": {"kernel": "kvq block_sensitivity", "bound": "hbm", "achieved": round(gbs, 2),
                         "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
-                        "traffic": None}}
+                        "traffic": traffic_bytes("alloc", "kvq block_sensitivity")}}
     print(json.dumps(res), flush=True)
 
 
