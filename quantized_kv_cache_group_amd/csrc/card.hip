@@ -13,14 +13,15 @@
 //   widths             uint8 [nb]
 // Every segment but the last is a multiple of 128 bytes, so all start
 // 16-byte aligned.  The kernel is a set of contiguous copies: grid.x
-// enumerates the block slots of K and V, then 16 KiB chunks of the windows
-// and the rope rows; slots past the sequence's counts exit.
+// enumerates quarters of the block slots of K and V, then 16 KiB chunks of
+// the windows and the rope rows; slots past the sequence's counts exit.
 #include "kvq_internal.h"
 
 namespace kvq {
 namespace {
 
 constexpr int CHUNK = 16384;                   // bytes per workgroup for rows
+constexpr int PARTS = 4;                       // workgroups per block payload
 
 struct CardArgs {
     Tables t;
@@ -38,22 +39,30 @@ struct CardArgs {
 
 __device__ __forceinline__ uint64_t bb(int bits, int H, int D) { return (uint64_t)H * D * (8 * bits + 4); }
 
-// Sum of the block sizes of blocks [0, n) of the sequence (all threads get it).
-__device__ uint64_t blocks_prefix(const CardArgs &p, int n)
+// Sums of the block sizes of blocks [0, j) and [0, nb) of the sequence, in
+// one pass over the widths (every thread gets both; 256 threads).
+__device__ void blocks_prefix(const CardArgs &p, int j, int nb, uint64_t &before, uint64_t &all)
 {
-    __shared__ uint64_t part[256];
+    __shared__ unsigned long long part[2][4];
     const uint8_t *bits = p.t.bits + (size_t)p.seq * p.t.max_blocks;
-    uint64_t s = 0;
-    for (int i = threadIdx.x; i < n; i += blockDim.x) s += bb(bits[i], p.t.H, p.t.D);
-    part[threadIdx.x] = s;
-    __syncthreads();
-    for (int w = blockDim.x / 2; w > 0; w >>= 1) {
-        if ((int)threadIdx.x < w) part[threadIdx.x] += part[threadIdx.x + w];
-        __syncthreads();
+    unsigned long long sa = 0, sb = 0;
+    for (int i = threadIdx.x; i < nb; i += blockDim.x) {
+        const uint64_t b = bb(bits[i], p.t.H, p.t.D);
+        sa += b;
+        if (i < j) sb += b;
     }
-    const uint64_t r = part[0];
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+        sa += __shfl_xor(sa, o);
+        sb += __shfl_xor(sb, o);
+    }
+    if ((threadIdx.x & 63) == 0) {
+        part[0][threadIdx.x >> 6] = sa;
+        part[1][threadIdx.x >> 6] = sb;
+    }
     __syncthreads();
-    return r;
+    all = part[0][0] + part[0][1] + part[0][2] + part[0][3];
+    before = part[1][0] + part[1][1] + part[1][2] + part[1][3];
 }
 
 // Copy n bytes (a multiple of 16) between device memory and the image.
@@ -86,19 +95,24 @@ __global__ __launch_bounds__(256) void card_copy(CardArgs p)
     const int n_kv = p.v_pool ? 2 : 1;
     const int mb = p.t.max_blocks;
     int x = blockIdx.x;
-    const uint64_t kv_bytes = blocks_prefix(p, nb);
+    const bool is_block = x < n_kv * mb * PARTS;
+    const int jx = is_block ? (x % (mb * PARTS)) / PARTS : 0;
+    uint64_t before, kv_bytes;
+    blocks_prefix(p, jx, nb, before, kv_bytes);
     const uint64_t row = (uint64_t)H * D * 2;
     const uint64_t win_off = kv_bytes * n_kv;
-    if (x < n_kv * mb) {                                      // one block payload
-        const int kv = x / mb, j = x % mb;
-        if (j >= nb) return;
-        const size_t e = (size_t)a * mb + j;
-        const uint64_t img = kv * kv_bytes + blocks_prefix(p, j);
+    if (is_block) {                                           // one part of a block payload
+        const int kv = x / (mb * PARTS), part = x % PARTS;
+        if (jx >= nb) return;
+        const size_t e = (size_t)a * mb + jx;
+        const uint64_t n = bb(p.t.bits[e], H, D), pn = (n / 16 + PARTS - 1) / PARTS * 16;
+        const uint64_t beg = (uint64_t)part * pn;
+        if (beg >= n) return;
         uint8_t *blk = (kv ? p.v_pool : p.k_pool) + (kv ? p.v_offset : p.k_offset)[e];
-        copy16(p, blk, img, bb(p.t.bits[e], H, D));
+        copy16(p, blk + beg, kv * kv_bytes + before + beg, n - beg < pn ? n - beg : pn);
         return;
     }
-    x -= n_kv * mb;
+    x -= n_kv * mb * PARTS;
     if (x < n_kv * p.w_chunks) {                              // window rows
         const int kv = x / p.w_chunks, c = x % p.w_chunks;
         const uint64_t total = (uint64_t)W * row, beg = (uint64_t)c * CHUNK;
@@ -154,7 +168,7 @@ hipError_t launch_card(const Tables &t, const uint64_t *k_offset, const uint64_t
                                   CHUNK)
                           : 0;
     const int n_kv = v_pool ? 2 : 1;
-    const int64_t gx = (int64_t)n_kv * t.max_blocks + (int64_t)n_kv * p.w_chunks + p.r_chunks + 1;
+    const int64_t gx = (int64_t)n_kv * t.max_blocks * PARTS + (int64_t)n_kv * p.w_chunks + p.r_chunks + 1;
     if (gx > 0x7fffffff) return hipErrorInvalidValue;
     card_copy<<<(unsigned)gx, 256, 0, s>>>(p);
     return hipGetLastError();
