@@ -184,7 +184,28 @@ __global__ __launch_bounds__(256) void select_blocks(TopkArgs p)
     // `need` ends as the number of keys equal to T that are kept.
     uint32_t prefix = 0, mask = 0;
     int need = Kk;
-    if (Kk > 0) {
+    if (Kk > 0 && nb <= 256) {
+        // One block per thread: its rank (larger keys, then equal keys at lower
+        // indices) by counting over the LDS keys; the block of rank Kk - 1
+        // gives T and the number of keys above it.
+        __syncthreads();
+        if (tid < nb) {
+            const uint32_t u = key[tid];
+            int gt = 0, eqb = 0;
+            for (int j = 0; j < nb; j++) {
+                const uint32_t w = key[j];
+                gt += w > u;
+                eqb += (w == u) & (j < tid);
+            }
+            if (gt + eqb == Kk - 1) {
+                sel[0] = (int)u;
+                sel[1] = gt;
+            }
+        }
+        __syncthreads();
+        prefix = (uint32_t)sel[0];
+        need = Kk - sel[1];
+    } else if (Kk > 0) {
         for (int shift = 24; shift >= 0; shift -= 8) {
             hist[tid] = 0;
             __syncthreads();

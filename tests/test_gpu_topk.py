@@ -131,7 +131,7 @@ def test_topk_many_blocks_per_thread():
     close(got, _ref_sparse(b, q, scale, sel), what="topk 600 blocks")
 
 
-@pytest.mark.parametrize("n_blocks,K,G,D", [(8, 3, 4, 128), (300, 100, 4, 64), (300, 100, 8, 64), (520, 257, 2, 256)])
+@pytest.mark.parametrize("n_blocks,K,G,D", [(8, 3, 4, 128), (256, 100, 4, 64), (300, 100, 4, 64), (300, 100, 8, 64), (520, 257, 2, 256)])
 def test_topk_ties_keep_lowest_indices(n_blocks, K, G, D):
     """Every block holds the same keys, so every score ties exactly (the same
     arithmetic on the same bytes): the kept set must be blocks 0..K-1."""
