@@ -356,7 +356,7 @@ def topk_bench(args):
         c.quantize("v", src[(i + 1) % 2])
     q = torch.randn((A, Hq, D), generator=g, device="cuda").to(torch.bfloat16)
     out = torch.empty((A, Hq, D), dtype=torch.float32, device="cuda")
-    ws = torch.empty(max(caches[0].topk_workspace_bytes(Hq, K), caches[0].decode_workspace_bytes(Hq)),
+    ws = torch.zeros(max(caches[0].topk_workspace_bytes(Hq, K), caches[0].decode_workspace_bytes(Hq)),
                      dtype=torch.uint8, device="cuda")
     stream = torch.cuda.current_stream()
 
@@ -651,7 +651,7 @@ def main():
         qs = [torch.randn((A, Hq, D + w.rope_dim), generator=gq, device="cuda").to(torch.bfloat16)
               for _ in layers]
         out = torch.empty((A, Hq, D), dtype=torch.float32, device="cuda")
-        ws = torch.empty(max(sets[0][0].decode_workspace_bytes(Hq), 256), dtype=torch.uint8,
+        ws = torch.zeros(max(sets[0][0].decode_workspace_bytes(Hq), 256), dtype=torch.uint8,
                          device="cuda")
     # Windows and rope are bf16 storage: filled once per copy with N(0,1).
     for cs in sets:

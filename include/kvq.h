@@ -206,7 +206,8 @@ int kvq_card_scatter(const kvq_layout *L, const kvq_store *K, const kvq_store *V
  * attention-error bound using recent queries, keys and values; this
  * library's bound, from the per-group reconstruction bound s/2 with s =
  * range / (2^b - 1)).  For sequence a and block i < n_blocks (rows 64i ..
- * 64i+63 of k and v, bf16 [A][seq_tokens][H][D], 16-byte aligned):
+ * 64i+63 of k and v, bf16 [A][seq_tokens][H][D], 16-byte aligned), with
+ * scale = softmax_scale (finite, > 0):
  *     S[a][i] = sum_h ( 2 Vmax_g scale max_t sum_grp rK[t][g][grp] sum_{d in grp} |q[a][h][d]|
  *                       + 8 max_t sqrt(sum_grp rV[t][g][grp]^2) ),   g = h / (n_q_heads/H)
  * rK, rV: max - min of a 64-element group; Vmax_g: the largest V row norm of
@@ -230,7 +231,14 @@ int kvq_allocate_widths(const float *S, int64_t n, int32_t n_heads, int32_t head
                         uint64_t budget_bytes, uint8_t *widths);
 
 /* Workspace bytes kvq_attend_decode needs for this layout and head count
- * (written to *bytes).  Errors: KVQ_EINVAL, KVQ_EUNSUPPORTED. */
+ * (written to *bytes).  The workspace starts with round256(4*n_seqs*n_heads)
+ * bytes of merge tickets (uint32 per sequence and KV head), then split
+ * partials.  The ticket bytes must be zero before the first call on a
+ * workspace (zero-fill it once after allocating it); every call leaves them
+ * zero again, so a workspace is zeroed once, not per call.  Anything else
+ * that writes those bytes (another kind of call sharing the buffer, a call
+ * for a layout with more sequences or heads) requires zeroing them again.
+ * Errors: KVQ_EINVAL, KVQ_EUNSUPPORTED. */
 int kvq_decode_workspace(const kvq_layout *L, int32_t n_q_heads, int32_t rope_dim, size_t *bytes);
 
 /* Batched decode attention over quantized caches (AgentMem: batched
@@ -241,6 +249,9 @@ int kvq_decode_workspace(const kvq_layout *L, int32_t n_q_heads, int32_t rope_di
  * the 64*n_blocks[a] quantized tokens, then the n_window[a] window tokens.
  * The result equals softmax attention over the restored rows, within fp32
  * rounding; an empty sequence gives zeros.
+ *   softmax_scale: finite and > 0 (attention scales are positive; the
+ *        kernels take the running maximum of the scaled scores from the
+ *        maximum of the raw ones).
  *   q    bf16 [A][n_q_heads][D + rope_dim]
  *   out  fp32 [A][n_q_heads][D]
  *   V    NULL for latent attention: the values are the restored K rows (the
@@ -250,14 +261,21 @@ int kvq_decode_workspace(const kvq_layout *L, int32_t n_q_heads, int32_t rope_di
  *        per token position (token t of sequence a, blocks then window, at
  *        row t).
  *   n_q_heads: a multiple of H with n_q_heads/H <= 16.
- *   workspace: >= kvq_decode_workspace bytes, 256-byte aligned.
- * Errors: KVQ_EINVAL, KVQ_ENOSPC, KVQ_EUNSUPPORTED, KVQ_EHIP. */
+ *   workspace: >= kvq_decode_workspace bytes, 256-byte aligned, its ticket
+ *        bytes zero (see kvq_decode_workspace).  Calls that share a workspace
+ *        must not overlap in time.
+ * Errors: KVQ_EINVAL (also softmax_scale <= 0), KVQ_ENOSPC, KVQ_EUNSUPPORTED,
+ *         KVQ_EHIP. */
 int kvq_attend_decode(const kvq_layout *L, const kvq_store *K, const kvq_store *V,
                       const uint16_t *rope, int32_t rope_dim, const uint16_t *q,
                       int32_t n_q_heads, float softmax_scale, float *out,
                       void *workspace, size_t workspace_bytes, void *stream);
 
-/* Workspace bytes kvq_attend_decode_topk needs (written to *bytes).
+/* Workspace bytes kvq_attend_decode_topk needs (written to *bytes).  It
+ * begins with the workspace of the decode over the kept blocks, tickets
+ * first, so it must be zero-filled once as for kvq_attend_decode; a buffer
+ * sized for both may serve kvq_attend_decode and kvq_attend_decode_topk of
+ * the same layout alternately.
  * Errors: KVQ_EINVAL, KVQ_EUNSUPPORTED. */
 int kvq_topk_workspace(const kvq_layout *L, int32_t n_q_heads, int32_t rope_dim, int32_t top_k,
                        size_t *bytes);
@@ -277,8 +295,10 @@ int kvq_topk_workspace(const kvq_layout *L, int32_t n_q_heads, int32_t rope_dim,
  * copy of the tables in the workspace).
  *   selected  NULL or device int32 [A][top_k]: the kept block indices in
  *             ascending order, -1 past min(top_k, n_blocks[a]).
- *   top_k >= 1; max_blocks <= 16384; (n_q_heads/H) * (head_dim + rope_dim)
- *   <= 9216.  Other arguments as for kvq_attend_decode.
+ *   top_k >= 1; max_blocks <= 16384 (0 allowed: a window-only layout keeps
+ *   no block and `selected` is all -1); (n_q_heads/H) * (head_dim + rope_dim)
+ *   <= 9216.  Other arguments (softmax_scale > 0, the zeroed workspace) as
+ *   for kvq_attend_decode.
  * Errors: KVQ_EINVAL, KVQ_ENOSPC, KVQ_EUNSUPPORTED, KVQ_EHIP. */
 int kvq_attend_decode_topk(const kvq_layout *L, const kvq_store *K, const kvq_store *V,
                            const uint16_t *rope, int32_t rope_dim, const uint16_t *q,
@@ -297,7 +317,11 @@ int kvq_chunk_workspace(const kvq_layout *L, int32_t n_q_heads, int32_t n_new, s
  *   k_new, v_new bf16 [A][n_new][H][D]   (unquantized)
  *   out  fp32 [A][n_new][n_q_heads][D]
  *   n_q_heads: a multiple of H with n_q_heads/H <= 16.
- * Errors: KVQ_EINVAL, KVQ_ENOSPC, KVQ_EUNSUPPORTED, KVQ_EHIP. */
+ *   softmax_scale: finite and > 0.
+ *   workspace: >= kvq_chunk_workspace bytes, 256-byte aligned (no zeroing
+ *        needed).
+ * Errors: KVQ_EINVAL (also softmax_scale <= 0), KVQ_ENOSPC, KVQ_EUNSUPPORTED,
+ *         KVQ_EHIP. */
 int kvq_attend_chunk(const kvq_layout *L, const kvq_store *K, const kvq_store *V,
                      const uint16_t *q_new, const uint16_t *k_new, const uint16_t *v_new,
                      int32_t n_new, int32_t n_q_heads, float softmax_scale, float *out,

@@ -1,5 +1,6 @@
 // Batched split-K decode for grouped-query attention with at most 4 query
-// heads per KV head (gfx950, 4x4x4 matrix-core blocks).
+// heads per KV head (gfx950, 4x4x4 matrix-core blocks), with the split merge
+// done by the last workgroup of each (sequence, KV head) to finish.
 //
 // What it computes (Agent Memory Below the Prompt, arXiv 2603.04428,
 // Abstract: batched inference over several agents' quantized caches restored
@@ -8,38 +9,45 @@
 // attention of q[a][h] over the 64*n_blocks[a] quantized tokens and the
 // n_window[a] bf16 tokens of KV head h / G.
 //
-// Why 4x4x4 blocks: with G <= 4 query heads per KV head, a 16x16 tile would
-// leave 12 of its 16 head rows empty.  v_mfma_f32_4x4x4_16b_f16 runs 16
-// independent 4x4x4 products, so a wave of 64 lanes maps lane l to token l
-// of a 64-token block:
-//   Q.K^T  block b = tokens 4b..4b+3; A = K rows (lane = token, 4 dims per
+// Work decomposition: one workgroup per (key split, KV head, sequence) with
+// one wave per 64-dim group of head_dim (a group is the quantizer's unit, so
+// a wave needs one scale/bias per token).  A split is SB 64-token blocks or
+// the bf16 window.  For each block, wave w loads its group of every token's K
+// and V row together (lane = token), forms partial scores of the group, and
+// the waves add their partials through LDS in a fixed order, so every wave
+// holds the same full scores and runs the same online softmax; each wave then
+// accumulates the output dims of its own group.
+//
+// Matrix products on the codes themselves.  v_mfma_f32_4x4x4_16b_f16 runs 16
+// independent 4x4x4 products, so lane l of a wave is token l of a block:
+//   Q.K^T  block b = tokens 4b..4b+3; A = K values (lane = token, 4 dims per
 //          instruction), B = the G query rows (read from LDS), so lane (b, j)
 //          ends with the scores of tokens 4b..4b+3 for head j;
 //   P.V    for each 4-token slice s, A = P[heads][tokens 4s..4s+3], which is
 //          exactly what the lanes of block s hold after the softmax, broadcast
-//          to all 16 blocks by the instruction's CBSZ/ABID fields; B = V rows
+//          to all 16 blocks by the instruction's CBSZ/ABID fields; B = V values
 //          of those 4 tokens for 4 output dims per block: each lane writes its
-//          V row to LDS and ds_read_b64_tr_b16 hands lane l dim l of four
-//          consecutive tokens.  No lane shuffles move probabilities.
+//          V values to LDS and ds_read_b64_tr_b16 hands lane l dim l of four
+//          consecutive tokens.
+// A code c of width b enters the products as the exact fp16 value 1024 + m*c:
+// an and_or with the magic exponent 0x6400 places the code at the top of the
+// fp16 mantissa (m = 64, 64, 16, 1 for b = 2, 3, 4, 8), so the constant 1024
+// is at most ~10 times the code term and the fp32 sums lose almost nothing to
+// it.  Per 64-dim group of token t (scale s, bias b; restored value s*c + b):
+//   q . K_t  = (s/m) (T_t - 1024 Q) + b Q,   T_t = sum_d q_d (1024 + m c_td),
+//              Q = sum_d q_d (fp16 query, fp32 sum);
+//   sum_t p_t V_t[d] = ( sum_t p''_t (1024 + m c_td) - 1024 sum_t p''_t ) / 64
+//                      + sum_t p_t b_t,   p''_t = fp16(p_t s_t 64/m),
+// so the largest term of a sum is at most a few times its result.  The
+// factor 64/m keeps p'' in fp16 range for every width (|x| <= 65504 bounds
+// s), and the correction sums the same rounded p'' the products used.  The
+// softmax runs in fp32 (exp2) with an exact running max, so p <= 1.
 //
-// Codes are never dequantized element by element.  An and_or with a magic
-// exponent turns two codes into the exact fp16 values 1024 + code, and the
-// matrix instructions consume those.  Per 64-dim group g of token t (scale
-// s, bias b; the restored value is s*code + b):
-//   q . K_t  = sum_g s_tg (T_tg - 1024 Q_g) + b_tg Q_g,  T_tg = sum_{d in g} q_d (1024 + code)
-//   sum_t p_t V_t[d] = sum_t p'_tg (1024 + code) - 1024 sum_t p'_tg + sum_t p_t b_tg,
-//                      p'_tg = fp16(p_t s_tg),
-// with Q_g the sum of the (fp16) query over the group, all in fp32.  That
-// halves the vector work per code against dequantize-then-multiply, and the
-// restored values enter the products unrounded (a token's s and b reach the
-// lanes holding its scores through a quad broadcast).  The softmax runs in
-// fp32 (exp2); probabilities rounded to fp16 feed the running sum.
-//
-// Work decomposition: one wave per (key split, KV head, sequence); a split is
-// SB 64-token blocks or the bf16 window; many small waves per SIMD hide the
-// load latency.  The split's widths and pool offsets sit one per lane
-// (v_readlane), so no block's loads wait on a scalar load.  Partials (max,
-// sum, unnormalised output) are combined by the decode merge kernel.
+// Split merge: each workgroup writes (max, sum, unnormalised output) of its
+// rows, then takes a ticket from a per-(sequence, KV head) counter in the
+// workspace (atomicInc wraps it back to zero); the workgroup that takes the
+// last ticket merges every split of its rows.  The counters must be zero
+// before the first call on a workspace, and each call leaves them zero.
 #include "kvq_internal.h"
 #include "unpack.h"
 
@@ -51,21 +59,18 @@ using namespace dev;
 typedef _Float16 h4 __attribute__((ext_vector_type(4)));
 typedef short s4 __attribute__((ext_vector_type(4)));
 
-constexpr int VS = 64;                        // LDS row stride of one 64-dim V set (halves)
+constexpr int VS = 64;                        // LDS row stride of the V tile (halves)
+constexpr float FV = 64.0f;                   // probability factor of the V products
 
 // 16-byte chunk c of V row r sits at chunk c ^ vswz(r).  gfx950's LDS serves
 // a 16-byte write for 8 lanes per cycle over 32 banks and an 8-byte read for
 // 32 lanes over 64 banks; with this swap the row stores (8 consecutive rows,
 // one chunk) and the transposed reads (4 consecutive rows x 8 chunks per 32
-// lanes) both spread over distinct banks.  A 72-half pitch without the swap
-// left every transposed read two-way conflicted.
+// lanes) both spread over distinct banks.
 __device__ __forceinline__ int vswz(int r) { return ((r & 1) ^ ((r & 2) << 1) ^ ((r >> 1) & 2)) << 3; }
 
-// (x & mask) | magic.  Written in plain C so the compiler sees every VALU
-// write that feeds a matrix instruction (it inserts the wait states such a
-// read needs); magic_v comes from opaque_magic(), a vector register the
-// compiler cannot fold back into a literal, so the pair selects to one
-// v_and_or_b32 (a VALU instruction here reads at most one scalar register).
+// (x & mask) | magic as one v_and_or_b32 (magic in a vector register from
+// opaque_magic(), so the mask may take the one scalar operand slot).
 __device__ __forceinline__ uint32_t and_or(uint32_t x, uint32_t mask, uint32_t magic_v)
 {
     return (x & mask) | magic_v;
@@ -78,10 +83,17 @@ __device__ __forceinline__ uint32_t opaque_magic()
     return m;
 }
 
-// A lane's full token row of codes: D*B/8 bytes as dwords.
-template <int B, int NG>
-struct FullRow {
-    static constexpr int BYTES = 8 * NG * B;
+// Code multiplier m of width B: where the code sits in the fp16 mantissa.
+template <int B> struct CodeMul;
+template <> struct CodeMul<2> { static constexpr float M = 64.0f; };   // bits 6..7
+template <> struct CodeMul<3> { static constexpr float M = 64.0f; };   // bits 6..8
+template <> struct CodeMul<4> { static constexpr float M = 16.0f; };   // bits 4..7
+template <> struct CodeMul<8> { static constexpr float M = 1.0f; };    // bits 0..7
+
+// A lane's 64-dim group of one token row: 8*B bytes of codes, as dwords.
+template <int B>
+struct GroupRow {
+    static constexpr int BYTES = 8 * B;
     static constexpr int NDW = BYTES / 4;
 
     __device__ static __forceinline__ void load(uint32_t *w, const uint8_t *row)
@@ -101,21 +113,26 @@ struct FullRow {
         }
     }
 
-    // Chunk c (8 codes) as the fp16 pairs (1024+c0, 1024+c4) (1024+c1, 1024+c5)
-    // (1024+c2, 1024+c6) (1024+c3, 1024+c7), exact.  mv holds MAGIC.
+    // Chunk c (codes 8c..8c+7 of the group) as the fp16 pairs
+    // (1024 + m c0, 1024 + m c4) (.. c1, c5) (.. c2, c6) (.. c3, c7), exact.
     __device__ static __forceinline__ Pairs chunk(const uint32_t *w, int c, uint32_t mv)
     {
         Pairs r;
         if constexpr (B == 4) {
-            const uint32_t x = w[c];                          // code i at bits 4i
-#pragma unroll
-            for (int i = 0; i < 4; i++) r.p[i] = as_h2(and_or(x >> (4 * i), 0x000F000Fu, mv));
+            // code i at bits 4i: pair i sits at bits (4i, 16 + 4i); move it to bits 4..7
+            const uint32_t x = w[c];
+            r.p[0] = as_h2(and_or(x << 4, 0x00F000F0u, mv));
+            r.p[1] = as_h2(and_or(x, 0x00F000F0u, mv));
+            r.p[2] = as_h2(and_or(x >> 4, 0x00F000F0u, mv));
+            r.p[3] = as_h2(and_or(x >> 8, 0x00F000F0u, mv));
         } else if constexpr (B == 2) {
             const uint32_t d = w[c >> 1];
             const uint32_t v = (c & 1) ? (d >> 16) : (d & 0xffffu);   // code i at bits 2i
-            const uint32_t y = v | (v << 8);                  // codes 4..7 at bits 16..23
-#pragma unroll
-            for (int i = 0; i < 4; i++) r.p[i] = as_h2(and_or(y >> (2 * i), 0x00030003u, mv));
+            const uint32_t y = v | (v << 8);                  // pair i at bits (2i, 16 + 2i)
+            r.p[0] = as_h2(and_or(y << 6, 0x00C000C0u, mv));
+            r.p[1] = as_h2(and_or(y << 4, 0x00C000C0u, mv));
+            r.p[2] = as_h2(and_or(y << 2, 0x00C000C0u, mv));
+            r.p[3] = as_h2(and_or(y, 0x00C000C0u, mv));
         } else if constexpr (B == 8) {
 #pragma unroll
             for (int i = 0; i < 4; i++) {
@@ -123,27 +140,29 @@ struct FullRow {
                 r.p[i] = as_h2(perm(w[2 * c + 1], w[2 * c], sel) | mv);
             }
         } else {
-            // 3 bytes at byte o of the row: code i at bits 3i of those 24
+            // 3 bytes at byte 3c of the group: code i at bits 3i of those 24
             const int o = 3 * c, i0 = o >> 2, sh = o & 3;     // compile-time after unrolling
             const uint32_t lo = w[i0], hi = w[(i0 + 1 < NDW) ? i0 + 1 : i0];
             const uint32_t u = perm(hi, lo, 0x0C000000u | ((uint32_t)(sh + 2) << 16) |
                                                 ((uint32_t)(sh + 1) << 8) | (uint32_t)sh);
-            // codes 0..3 stay at bits 0..11, codes 4..7 move to bits 16..27
+            // codes 0..3 stay at bits 0..11, codes 4..7 move to bits 16..27:
+            // pair i at bits (3i, 16 + 3i); move it to bits 6..8
             const uint32_t z = (u & 0x00000FFFu) | ((u << 4) & 0x0FFF0000u);
-#pragma unroll
-            for (int i = 0; i < 4; i++) r.p[i] = as_h2(and_or(z >> (3 * i), 0x00070007u, mv));
+            r.p[0] = as_h2(and_or(z << 6, 0x01C001C0u, mv));
+            r.p[1] = as_h2(and_or(z << 3, 0x01C001C0u, mv));
+            r.p[2] = as_h2(and_or(z, 0x01C001C0u, mv));
+            r.p[3] = as_h2(and_or(z >> 3, 0x01C001C0u, mv));
         }
         return r;
     }
 };
 
-template <int NG>
 struct State {
-    f4 o[NG];                                 // lane (b, j): sum p'(1024+code) for head i, dim 64hh + pos 4b+j
+    f4 o;                                     // lane (b, j): sum p''(1024+m c) for head i, group pos 4b+j
     float m_run;                              // running max (log2 domain) of head j
     float l_lane;                             // this lane's share of head j's running sum
-    float ps_lane[NG];                        // this lane's share of head j's sum of p' (coded tokens), per group
-    float pb_lane[NG];                        // this lane's share of head j's sum of p*bias, per group
+    float ps_lane;                            // this lane's share of head j's sum of p'' (coded tokens)
+    float pb_lane;                            // this lane's share of head j's sum of p*bias
 };
 
 // Token 4b+r's 32-bit value broadcast to the four lanes of quad b.
@@ -157,34 +176,30 @@ __device__ __forceinline__ uint32_t quad_bcast(uint32_t v, int r)
     }
 }
 
-// Per-group sums over the lane's key row of q (fp16, from LDS) times the
-// row's chunk pairs: T[g] for tokens 4b..4b+3 of head j.
-template <int NG, typename KF>
-__device__ __forceinline__ void group_dots(f4 (&T)[NG], const h4 (*qs)[4], KF kx)
+// Sum over the lane's group row of q (fp16, from LDS) times the row's chunk
+// pairs: T for tokens 4b..4b+3 of head j.
+template <typename KF>
+__device__ __forceinline__ f4 group_dot(const h4 (*qs)[4], KF kx)
 {
     const int j = threadIdx.x & 3;
+    f4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int g = 0; g < NG; g++) {
-        f4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int c = 8 * g; c < 8 * g + 8; c++) {
-            const Pairs pr = kx(c);
-            const h4 a0 = {pr.p[0][0], pr.p[0][1], pr.p[1][0], pr.p[1][1]};
-            const h4 a1 = {pr.p[2][0], pr.p[2][1], pr.p[3][0], pr.p[3][1]};
-            s0 = __builtin_amdgcn_mfma_f32_4x4x4f16(a0, qs[2 * c][j], s0, 0, 0, 0);
-            s1 = __builtin_amdgcn_mfma_f32_4x4x4f16(a1, qs[2 * c + 1][j], s1, 0, 0, 0);
-        }
-        T[g] = s0 + s1;
+    for (int c = 0; c < 8; c++) {
+        const Pairs pr = kx(c);
+        const h4 a0 = {pr.p[0][0], pr.p[0][1], pr.p[1][0], pr.p[1][1]};
+        const h4 a1 = {pr.p[2][0], pr.p[2][1], pr.p[3][0], pr.p[3][1]};
+        s0 = __builtin_amdgcn_mfma_f32_4x4x4f16(a0, qs[2 * c][j], s0, 0, 0, 0);
+        s1 = __builtin_amdgcn_mfma_f32_4x4x4f16(a1, qs[2 * c + 1][j], s1, 0, 0, 0);
     }
+    return s0 + s1;
 }
 
 // Online softmax on the scores of one 64-token round (lane (b, j): tokens
-// 4b..4b+3 of head j).  Rescales the state and returns the probabilities
-// rounded to fp16 (the running sum adds exactly these).
-template <int NG>
-__device__ __forceinline__ h4 softmax_round(State<NG> &st, f4 s, int n_valid, float c)
+// 4b..4b+3 of head j).  Rescales the state and returns the probabilities in
+// fp32 (p <= 1).
+__device__ __forceinline__ f4 softmax_round(State &st, f4 s, int n_valid, float c)
 {
-    const int lane = threadIdx.x, b = lane >> 2;
+    const int lane = threadIdx.x & 63, b = lane >> 2;
     float sc[4];
 #pragma unroll
     for (int i = 0; i < 4; i++) sc[i] = (4 * b + i < n_valid) ? s[i] * c : -INFINITY;
@@ -194,81 +209,65 @@ __device__ __forceinline__ h4 softmax_round(State<NG> &st, f4 s, int n_valid, fl
     const float m_new = fmaxf(st.m_run, mx);
     const float alpha = __builtin_amdgcn_exp2f(st.m_run - m_new);
     st.m_run = m_new;
-    const h2 p01 = __builtin_convertvector(f2{__builtin_amdgcn_exp2f(sc[0] - m_new),
-                                              __builtin_amdgcn_exp2f(sc[1] - m_new)}, h2);
-    const h2 p23 = __builtin_convertvector(f2{__builtin_amdgcn_exp2f(sc[2] - m_new),
-                                              __builtin_amdgcn_exp2f(sc[3] - m_new)}, h2);
-    const h2 ones = {(_Float16)1.0f, (_Float16)1.0f};
-    st.l_lane = __builtin_amdgcn_fdot2(p23, ones, __builtin_amdgcn_fdot2(p01, ones, st.l_lane * alpha, false), false);
-#pragma unroll
-    for (int g = 0; g < NG; g++) {
-        st.ps_lane[g] *= alpha;
-        st.pb_lane[g] *= alpha;
-    }
+    st.l_lane *= alpha;
+    st.ps_lane *= alpha;
+    st.pb_lane *= alpha;
     // alpha of each head, for the output rows this lane holds
     if (__any(alpha != 1.0f)) {
         const int base = lane & ~3;
         const float a0 = __shfl(alpha, base), a1 = __shfl(alpha, base + 1);
         const float a2 = __shfl(alpha, base + 2), a3 = __shfl(alpha, base + 3);
-#pragma unroll
-        for (int hh = 0; hh < NG; hh++) {
-            st.o[hh][0] *= a0; st.o[hh][1] *= a1; st.o[hh][2] *= a2; st.o[hh][3] *= a3;
-        }
+        st.o[0] *= a0; st.o[1] *= a1; st.o[2] *= a2; st.o[3] *= a3;
     }
-    return h4{p01[0], p01[1], p23[0], p23[1]};
+    return f4{__builtin_amdgcn_exp2f(sc[0] - m_new), __builtin_amdgcn_exp2f(sc[1] - m_new),
+              __builtin_amdgcn_exp2f(sc[2] - m_new), __builtin_amdgcn_exp2f(sc[3] - m_new)};
 }
 
 __device__ __forceinline__ void wave_sync()
 {
-    // One wave owns the LDS buffers: its LDS instructions execute in order,
+    // One wave owns its LDS V tile: its LDS instructions execute in order,
     // so only the compiler needs a barrier between writes and reads.
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-// O += P'.X for every 64-dim set hh: each lane writes its token's row of set
-// hh to LDS (chunk order: position k of a chunk holds dim (k>>1) + 4(k&1)),
-// then 16 slices of 4 tokens whose B operand comes from
-// ds_read_b64_tr_b16 (lane l gets position l of four consecutive tokens);
-// lane l accumulates output position 64hh + l.  pa(hh) is the A operand of
-// set hh; vx(c) yields chunk c of the lane's row.
-template <int NG, typename PF, typename VF>
-__device__ __forceinline__ void pv_round(State<NG> &st, PF pa, _Float16 *vr, VF vx)
+// O += P.X for the wave's 64-dim group: each lane writes its token's values
+// to LDS (chunk order: position k of a chunk holds dim (k>>1) + 4(k&1)), then
+// 16 slices of 4 tokens whose B operand comes from ds_read_b64_tr_b16 (lane l
+// gets position l of four consecutive tokens); lane l accumulates group
+// position l.  vx(c) yields chunk c of the lane's row.
+template <typename VF>
+__device__ __forceinline__ void pv_round(State &st, h4 a, _Float16 *vr, VF vx)
 {
-    const int lane = threadIdx.x;
+    const int lane = threadIdx.x & 63;
     // lane i of each 16-lane group addresses token 4S + i/4, positions
-    // 16(l/16) + 4(i%4)..+3 of the set
-    // Rows 4S + (lane&15)/4: bit 2 of the row is S&1, so even and odd S use
+    // 16(l/16) + 4(i%4)..+3; bit 2 of the row is S&1, so even and odd S use
     // two bases.
     const int r0 = (lane & 15) >> 2, col = 16 * (lane >> 4) + 4 * (lane & 3);
     const _Float16 *vb0 = vr + r0 * VS + (col ^ vswz(r0));
     const _Float16 *vb1 = vr + r0 * VS + (col ^ vswz(r0 + 4));
 #pragma unroll
-    for (int hh = 0; hh < NG; hh++) {
-#pragma unroll
-        for (int cc = 0; cc < 8; cc++) {
-            const Pairs pr = vx(8 * hh + cc);
-            *reinterpret_cast<h8 *>(vr + lane * VS + ((8 * cc) ^ vswz(lane))) =
-                h8{pr.p[0][0], pr.p[0][1], pr.p[1][0], pr.p[1][1], pr.p[2][0], pr.p[2][1], pr.p[3][0], pr.p[3][1]};
-        }
-        wave_sync();
-        const h4 a = pa(hh);
-        f4 acc0 = st.o[hh], acc1 = {0.f, 0.f, 0.f, 0.f};
+    for (int cc = 0; cc < 8; cc++) {
+        const Pairs pr = vx(cc);
+        *reinterpret_cast<h8 *>(vr + lane * VS + ((8 * cc) ^ vswz(lane))) =
+            h8{pr.p[0][0], pr.p[0][1], pr.p[1][0], pr.p[1][1], pr.p[2][0], pr.p[2][1], pr.p[3][0], pr.p[3][1]};
+    }
+    wave_sync();
+    f4 acc0 = st.o, acc1 = {0.f, 0.f, 0.f, 0.f};
 #define KVQ_PV(ACC, S)                                                                                \
     ACC = __builtin_amdgcn_mfma_f32_4x4x4f16(                                                         \
         a,                                                                                            \
         __builtin_bit_cast(h4, __builtin_amdgcn_ds_read_tr16_b64_v4i16(                               \
                                    (__attribute__((address_space(3))) s4 *)(((S) & 1 ? vb1 : vb0) + 4 * (S) * VS))), \
         ACC, 4, S, 0)
-        KVQ_PV(acc0, 0); KVQ_PV(acc1, 1); KVQ_PV(acc0, 2); KVQ_PV(acc1, 3);
-        KVQ_PV(acc0, 4); KVQ_PV(acc1, 5); KVQ_PV(acc0, 6); KVQ_PV(acc1, 7);
-        KVQ_PV(acc0, 8); KVQ_PV(acc1, 9); KVQ_PV(acc0, 10); KVQ_PV(acc1, 11);
-        KVQ_PV(acc0, 12); KVQ_PV(acc1, 13); KVQ_PV(acc0, 14); KVQ_PV(acc1, 15);
+    KVQ_PV(acc0, 0); KVQ_PV(acc1, 1); KVQ_PV(acc0, 2); KVQ_PV(acc1, 3);
+    KVQ_PV(acc0, 4); KVQ_PV(acc1, 5); KVQ_PV(acc0, 6); KVQ_PV(acc1, 7);
+    KVQ_PV(acc0, 8); KVQ_PV(acc1, 9); KVQ_PV(acc0, 10); KVQ_PV(acc1, 11);
+    KVQ_PV(acc0, 12); KVQ_PV(acc1, 13); KVQ_PV(acc0, 14); KVQ_PV(acc1, 15);
 #undef KVQ_PV
-        st.o[hh] = acc0 + acc1;
-        wave_sync();
-    }
+    st.o = acc0 + acc1;
+    wave_sync();
 }
 
 // Widths and pool offsets of up to 64 consecutive blocks, one per lane, so
@@ -278,18 +277,21 @@ struct SplitMeta {
     uint32_t klo, khi, vlo, vhi;
 };
 
-__device__ __forceinline__ void split_meta(SplitMeta &sm, const DecodeArgs &p, int a, int j0, int j1)
+__device__ __forceinline__ void split_meta(SplitMeta &sm, const DecodeArgs &p, int a, int j0, int j1, bool with_v)
 {
-    const int jb = j0 + (int)threadIdx.x;
+    const int jb = j0 + (int)(threadIdx.x & 63);
     sm.base = j0;
     sm.bits = 0;
     sm.klo = sm.khi = sm.vlo = sm.vhi = 0;
     if (jb < j1) {
         const size_t e = (size_t)a * p.t.max_blocks + jb;
         sm.bits = p.t.bits[e];
-        const uint64_t ko = p.k.offset[e], vo = p.v.offset[e];
+        const uint64_t ko = p.k.offset[e];
         sm.klo = (uint32_t)ko; sm.khi = (uint32_t)(ko >> 32);
-        sm.vlo = (uint32_t)vo; sm.vhi = (uint32_t)(vo >> 32);
+        if (with_v) {
+            const uint64_t vo = p.v.offset[e];
+            sm.vlo = (uint32_t)vo; sm.vhi = (uint32_t)(vo >> 32);
+        }
     }
 }
 
@@ -300,180 +302,217 @@ __device__ __forceinline__ f2 meta_of(uint32_t packed)
     return f2{(float)sb[0], (float)sb[1]};
 }
 
-// A 64-token block in three phases: the Q.K products (width-specific
-// unpack of the lane's K row), the scores and the online softmax, then P.V
-// (width-specific unpack of the V row).
-template <int B, int NG>
-__device__ __forceinline__ void dots_phase(f4 (&T)[NG], const h4 (*qs)[4], const uint32_t *kw)
+// Partial scores of the wave's group for tokens 4b..4b+3 of head j:
+// (s/m)(T - 1024 Q) + b Q with token 4b+r's (s, b) from km.
+template <int B>
+__device__ __forceinline__ f4 group_scores(const h4 (*qs)[4], float qg, const uint32_t *kw, uint32_t km)
 {
     const uint32_t mv = opaque_magic();
-    group_dots<NG>(T, qs, [&](int cidx) { return FullRow<B, NG>::chunk(kw, cidx, mv); });
-}
-
-// scores: sum_g s (T - 1024 Q_g) + b Q_g, with token 4b+r's (s, b) from km;
-// returns P' = fp16(p s_v) per group and adds the bias and P' sums.
-template <int NG>
-__device__ __forceinline__ f4 scores_of(const f4 (&T)[NG], const uint32_t *km, const float (&qg)[NG])
-{
-    f4 s = {0.f, 0.f, 0.f, 0.f};
+    const f4 T = group_dot(qs, [&](int c) { return GroupRow<B>::chunk(kw, c, mv); });
+    const float q1024 = 1024.0f * qg;
+    f4 s;
 #pragma unroll
-    for (int gg = 0; gg < NG; gg++) {
-        const float q1024 = 1024.0f * qg[gg];
-#pragma unroll
-        for (int r = 0; r < 4; r++) {
-            const f2 ksb = meta_of(quad_bcast(km[gg], r));
-            s[r] = __builtin_fmaf(ksb[0], T[gg][r] - q1024, __builtin_fmaf(ksb[1], qg[gg], s[r]));
-        }
+    for (int r = 0; r < 4; r++) {
+        const f2 ksb = meta_of(quad_bcast(km, r));
+        s[r] = __builtin_fmaf(ksb[0] * (1.0f / CodeMul<B>::M), T[r] - q1024, ksb[1] * qg);
     }
     return s;
 }
 
+// Full scores from the waves' partials: each wave stores its partial in
+// LDS, the workgroup meets at a barrier, and every wave adds the NG
+// partials in the same order (so all waves hold identical scores).
 template <int NG>
-__device__ __forceinline__ void score_phase(State<NG> &st, h4 (&pg)[NG], const f4 (&T)[NG], const uint32_t *km,
-                                            const uint32_t *vm, const float (&qg)[NG], float c)
+__device__ __forceinline__ f4 exchange(f4 part, f4 (*xs)[64], int w)
 {
-    const f4 s = scores_of<NG>(T, km, qg);
-    f2 vsb[NG][4];
+    if constexpr (NG == 1) {
+        return part;
+    } else {
+        const int lane = threadIdx.x & 63;
+        xs[w][lane] = part;
+        __syncthreads();
+        f4 s = xs[0][lane];
 #pragma unroll
-    for (int gg = 0; gg < NG; gg++)
-#pragma unroll
-        for (int r = 0; r < 4; r++) vsb[gg][r] = meta_of(quad_bcast(vm[gg], r));
-    const h4 p = softmax_round<NG>(st, s, 64, c);
-    const f4 pf = {(float)p[0], (float)p[1], (float)p[2], (float)p[3]};
-#pragma unroll
-    for (int gg = 0; gg < NG; gg++) {
-        const f4 pv = {pf[0] * vsb[gg][0][0], pf[1] * vsb[gg][1][0], pf[2] * vsb[gg][2][0], pf[3] * vsb[gg][3][0]};
-        pg[gg] = __builtin_convertvector(pv, h4);
-        st.ps_lane[gg] += ((float)pg[gg][0] + (float)pg[gg][1]) + ((float)pg[gg][2] + (float)pg[gg][3]);
-        st.pb_lane[gg] += __builtin_fmaf(pf[0], vsb[gg][0][1], pf[1] * vsb[gg][1][1]) +
-                          __builtin_fmaf(pf[2], vsb[gg][2][1], pf[3] * vsb[gg][3][1]);
+        for (int u = 1; u < NG; u++) s += xs[u][lane];
+        return s;
     }
 }
 
+// One 64-token block: K and V group rows of every token issued together,
+// the Q.K products and the exchange, the softmax, then P.V.
 template <int B, int NG>
-__device__ __forceinline__ void pv_phase(State<NG> &st, const h4 (&pg)[NG], const uint32_t *vw, _Float16 *vr)
+__device__ __forceinline__ void round_block(State &st, const h4 (*qs)[4], float qg, const uint8_t *kblk,
+                                            const uint8_t *vblk, int H, int g, int w, float c, _Float16 *vr,
+                                            f4 (*xs)[64])
 {
-    const uint32_t mv = opaque_magic();
-    pv_round<NG>(st, [&](int hh) { return pg[hh]; }, vr,
-                 [&](int cidx) { return FullRow<B, NG>::chunk(vw, cidx, mv); });
-}
+    constexpr uint32_t ROW = 8 * NG * B;                  // bytes of a full token row
+    const uint32_t tok = (uint32_t)g * 64 + (threadIdx.x & 63);
+    const uint32_t roff = tok * ROW + 8 * B * w;
+    const uint32_t moff = (uint32_t)H * 64 * ROW + 4 * (NG * tok + w);
+    uint32_t kw[GroupRow<B>::NDW], vw[GroupRow<B>::NDW];
+    GroupRow<B>::load(kw, kblk + roff);
+    const uint32_t km = *reinterpret_cast<const uint32_t *>(kblk + moff);
+    GroupRow<B>::load(vw, vblk + roff);
+    const uint32_t vm = *reinterpret_cast<const uint32_t *>(vblk + moff);
 
-// The V row is fetched once the K row's registers are free (a scheduling
-// barrier keeps its loads after the K row's last use), so a row's two
-// halves are never live together.
-template <int B, int NG>
-__device__ __forceinline__ void round_block(State<NG> &st, const h4 (*qs)[4], const float (&qg)[NG],
-                                            const uint8_t *kblk, const uint8_t *vblk, int H, int g, float c,
-                                            _Float16 *vr)
-{
-    constexpr uint32_t CODE_ROW = 8 * NG * B;
-    const uint32_t row = (uint32_t)g * 64 + threadIdx.x;
-    const uint32_t moff = (uint32_t)H * 64 * CODE_ROW + 4 * NG * row;
-    uint32_t kw[FullRow<B, NG>::NDW], km[NG], vm[NG];
-    FullRow<B, NG>::load(kw, kblk + row * CODE_ROW);
+    const f4 s = exchange<NG>(group_scores<B>(qs, qg, kw, km), xs, w);
+    const f4 p = softmax_round(st, s, 64, c);
+    // p'' = fp16(p s 64/m) per token (the V scale of token 4b+r from its quad)
+    f4 pv, pbv;
 #pragma unroll
-    for (int i = 0; i < NG; i++) km[i] = reinterpret_cast<const uint32_t *>(kblk + moff)[i];
-    f4 T[NG];
-    dots_phase<B, NG>(T, qs, kw);
-    __builtin_amdgcn_sched_barrier(0);
-    uint32_t vw[FullRow<B, NG>::NDW];
-    FullRow<B, NG>::load(vw, vblk + row * CODE_ROW);
-#pragma unroll
-    for (int i = 0; i < NG; i++) vm[i] = reinterpret_cast<const uint32_t *>(vblk + moff)[i];
-    h4 pg[NG];
-    score_phase<NG>(st, pg, T, km, vm, qg, c);
-    pv_phase<B, NG>(st, pg, vw, vr);
+    for (int r = 0; r < 4; r++) {
+        const f2 vsb = meta_of(quad_bcast(vm, r));
+        pv[r] = p[r] * (vsb[0] * (FV / CodeMul<B>::M));
+        pbv[r] = p[r] * vsb[1];
+    }
+    const h4 pa = __builtin_convertvector(pv, h4);
+    st.l_lane += (p[0] + p[1]) + (p[2] + p[3]);
+    st.ps_lane += ((float)pa[0] + (float)pa[1]) + ((float)pa[2] + (float)pa[3]);
+    st.pb_lane += (pbv[0] + pbv[1]) + (pbv[2] + pbv[3]);
+    const uint32_t mv = opaque_magic();
+    pv_round(st, pa, vr, [&](int cidx) { return GroupRow<B>::chunk(vw, cidx, mv); });
 }
 
 // 64 window tokens w0 .. w0+63 (rows past nw read row nw-1 and are masked):
-// bf16 values straight into the products.
+// bf16 values straight into the products, probabilities rounded to fp16.
 template <int NG>
-__device__ __forceinline__ void round_window(State<NG> &st, const h4 (*qs)[4], const uint16_t *kw,
-                                             const uint16_t *vw, int H, int g, int w0, int nw,
-                                             float c, _Float16 *vr)
+__device__ __forceinline__ void round_window(State &st, const h4 (*qs)[4], const uint16_t *kwin,
+                                             const uint16_t *vwin, int H, int g, int w, int w0, int nw, float c,
+                                             _Float16 *vr, f4 (*xs)[64])
 {
     constexpr int D = 64 * NG;
-    const int t = min(w0 + (int)threadIdx.x, nw - 1);
-    const uint4 *kr = reinterpret_cast<const uint4 *>(kw + ((size_t)t * H + g) * D);
-    const uint4 *vrow = reinterpret_cast<const uint4 *>(vw + ((size_t)t * H + g) * D);
-    f4 T[NG];
-    group_dots<NG>(T, qs, [&](int cidx) { return bf16_pairs(kr[cidx]); });
-    f4 s = T[0];
+    const int t = min(w0 + (int)(threadIdx.x & 63), nw - 1);
+    const uint4 *kr = reinterpret_cast<const uint4 *>(kwin + ((size_t)t * H + g) * D + 64 * w);
+    const uint4 *vrow = reinterpret_cast<const uint4 *>(vwin + ((size_t)t * H + g) * D + 64 * w);
+    uint4 kx[8], vx[8];
 #pragma unroll
-    for (int gg = 1; gg < NG; gg++) s += T[gg];
-    const h4 p = softmax_round<NG>(st, s, nw - w0, c);
-    pv_round<NG>(st, [&](int) { return p; }, vr, [&](int cidx) { return bf16_pairs(vrow[cidx]); });
+    for (int i = 0; i < 8; i++) kx[i] = kr[i];
+#pragma unroll
+    for (int i = 0; i < 8; i++) vx[i] = vrow[i];
+    const f4 part = group_dot(qs, [&](int cidx) { return bf16_pairs(kx[cidx]); });
+    const f4 s = exchange<NG>(part, xs, w);
+    const f4 p = softmax_round(st, s, nw - w0, c);
+    const h4 pa = __builtin_convertvector(p, h4);
+    // the running sum adds the rounded probabilities the products use
+    st.l_lane += ((float)pa[0] + (float)pa[1]) + ((float)pa[2] + (float)pa[3]);
+    pv_round(st, pa, vr, [&](int cidx) { return bf16_pairs(vx[cidx]); });
 }
 
-// Query rows of KV head g's G heads, fp16, in the unpack order of the key
-// chunks, into qs; and Q_g of head j: the sum of its fp16 query over each
-// 64-dim group (lane (b, j) adds slice 16g + b, then the 16 lanes of head j
-// combine).
-template <int NG>
-__device__ __forceinline__ void stage_query(const DecodeArgs &p, int a, int g, h4 (*qs)[4], float (&qg)[NG])
+// Query rows of KV head g's G heads for dims [64w, 64w+64), fp16, in the
+// unpack order of the key chunks, into qs; and Q of head j: the sum of its
+// fp16 query over the group (lane (b, j) adds slice b, then the 16 lanes of
+// head j combine).
+__device__ __forceinline__ float stage_query(const DecodeArgs &p, int a, int g, int w, h4 (*qs)[4])
 {
-    constexpr int D = 64 * NG, NCH = 8 * NG;
-    const int lane = threadIdx.x, b = lane >> 2, j = lane & 3;
-    for (int e = lane; e < 4 * NCH; e += 64) {
-        const int h = e / NCH, cc = e % NCH;
-        Pairs pr;
-        if (h < p.G) {
-            const uint4 v = *reinterpret_cast<const uint4 *>(p.q + ((size_t)a * p.Hq + g * p.G + h) * D + 8 * cc);
-            pr = bf16_pairs(v);
-        } else {
-            pr.p[0] = pr.p[1] = pr.p[2] = pr.p[3] = h2{(_Float16)0.0f, (_Float16)0.0f};
+    const int lane = threadIdx.x & 63, b = lane >> 2, j = lane & 3;
+    const int D = p.t.D;
+    {
+        const int h = lane >> 3, cc = lane & 7;                 // 4 heads x 8 chunks = 32 lanes
+        if (lane < 32) {
+            Pairs pr;
+            if (h < p.G) {
+                const uint4 v = *reinterpret_cast<const uint4 *>(p.q + ((size_t)a * p.Hq + g * p.G + h) * D +
+                                                                 64 * w + 8 * cc);
+                pr = bf16_pairs(v);
+            } else {
+                pr.p[0] = pr.p[1] = pr.p[2] = pr.p[3] = h2{(_Float16)0.0f, (_Float16)0.0f};
+            }
+            qs[2 * cc][h] = h4{pr.p[0][0], pr.p[0][1], pr.p[1][0], pr.p[1][1]};
+            qs[2 * cc + 1][h] = h4{pr.p[2][0], pr.p[2][1], pr.p[3][0], pr.p[3][1]};
         }
-        qs[2 * cc][h] = h4{pr.p[0][0], pr.p[0][1], pr.p[1][0], pr.p[1][1]};
-        qs[2 * cc + 1][h] = h4{pr.p[2][0], pr.p[2][1], pr.p[3][0], pr.p[3][1]};
     }
     wave_sync();
     const h2 ones = {(_Float16)1.0f, (_Float16)1.0f};
+    const h4 v = qs[b][j];
+    float acc = __builtin_amdgcn_fdot2(h2{v[2], v[3]}, ones, __builtin_amdgcn_fdot2(h2{v[0], v[1]}, ones, 0.0f, false),
+                                       false);
 #pragma unroll
-    for (int gg = 0; gg < NG; gg++) {
-        const h4 v = qs[16 * gg + b][j];
-        float acc = __builtin_amdgcn_fdot2(h2{v[2], v[3]}, ones, __builtin_amdgcn_fdot2(h2{v[0], v[1]}, ones, 0.0f, false),
-                                           false);
+    for (int o = 4; o < 64; o <<= 1) acc += __shfl_xor(acc, o);
+    return acc;
+}
+
+// Combine the ns splits of rows (a, g*G + i), i < G, for the dims of the
+// wave's group: o = sum_s 2^(m_s - M) acc_s / sum_s 2^(m_s - M) l_s.
+__device__ void merge_splits(const DecodeArgs &p, int a, int g, int w, int ns)
+{
+    const int lane = threadIdx.x & 63;
+    const int D = p.t.D;
+    const size_t stride = (size_t)(D + 2);
+    const int d = 64 * w + lane;
+    for (int i = 0; i < p.G; i++) {
+        const size_t row = (size_t)a * p.Hq + (size_t)g * p.G + i;
+        const float *pr = p.part + row * p.n_splits * stride;
+        float M = -INFINITY;
+        for (int s0 = 0; s0 < ns; s0 += 64)
+            if (s0 + lane < ns) M = fmaxf(M, __builtin_nontemporal_load(pr + (size_t)(s0 + lane) * stride));
 #pragma unroll
-        for (int o = 4; o < 64; o <<= 1) acc += __shfl_xor(acc, o);
-        qg[gg] = acc;
+        for (int o = 32; o > 0; o >>= 1) M = fmaxf(M, __shfl_xor(M, o));
+        float L = 0.0f, acc = 0.0f;
+        for (int s0 = 0; s0 < ns; s0 += 64) {
+            const int sl = s0 + lane;
+            float wgt = 0.0f;
+            if (sl < ns) {
+                wgt = __builtin_amdgcn_exp2f(__builtin_nontemporal_load(pr + (size_t)sl * stride) - M);
+                L = __builtin_fmaf(wgt, __builtin_nontemporal_load(pr + (size_t)sl * stride + 1), L);
+            }
+            const int n = min(64, ns - s0);
+            for (int u0 = 0; u0 < n; u0 += 16) {
+                float v[16];
+#pragma unroll
+                for (int u = 0; u < 16; u++)
+                    v[u] = (u0 + u < n) ? __builtin_nontemporal_load(pr + (size_t)(s0 + u0 + u) * stride + 2 + d) : 0.0f;
+#pragma unroll
+                for (int u = 0; u < 16; u++)
+                    acc = __builtin_fmaf(__builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, wgt),
+                                                                                            u0 + u)),
+                                         v[u], acc);
+            }
+        }
+#pragma unroll
+        for (int o = 32; o > 0; o >>= 1) L += __shfl_xor(L, o);
+        p.out[row * D + d] = L > 0.0f ? acc * (1.0f / L) : 0.0f;
     }
 }
 
 template <int NG>
-__global__ __launch_bounds__(64, (NG <= 2 ? 3 : 2)) void decode_g4_split(DecodeArgs p)
+__global__ __launch_bounds__(64 * NG) void decode_g4_split(DecodeArgs p, uint32_t *tickets)
 {
-    constexpr int D = 64 * NG, NCH = 8 * NG;
-    __shared__ __attribute__((aligned(16))) h4 qs[2 * NCH][4];      // [slice][head], permuted dims
-    __shared__ __attribute__((aligned(16))) _Float16 vt[64 * VS];  // V rows, one 64-dim set
+    constexpr int D = 64 * NG;
+    __shared__ __attribute__((aligned(16))) h4 qs[NG][16][4];              // [wave][slice][head]
+    __shared__ __attribute__((aligned(16))) _Float16 vt[NG][64 * VS];      // V tile per wave
+    __shared__ __attribute__((aligned(16))) f4 xs[2][NG][64];              // partial scores
+    __shared__ int last;
     const int s = blockIdx.x, g = blockIdx.y, a = blockIdx.z;
-    const int lane = threadIdx.x, b = lane >> 2, j = lane & 3;
+    const int lane = threadIdx.x & 63, b = lane >> 2, j = lane & 3;
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int nb = seq_blocks(p.t, a), nw = seq_window(p.t, a);
     const int nsb = (nb + p.SB - 1) / p.SB;
+    const int ns = nsb + (nw > 0 ? 1 : 0);
     const bool win = (s == nsb) && nw > 0;
-    if (s > nsb || (s == nsb && !win)) return;
+    if (s >= ns) {
+        if (s == 0) {                                     // empty sequence: zeros
+            for (int i = 0; i < p.G; i++) p.out[((size_t)a * p.Hq + g * p.G + i) * D + 64 * w + lane] = 0.0f;
+        }
+        return;
+    }
 
     // The split's block table first, so its loads overlap the query loads.
     SplitMeta sm;
     sm.base = -(1 << 20);
     const int j0 = s * p.SB, j1 = min(j0 + p.SB, nb);
-    if (!win) split_meta(sm, p, a, j0, j1);
+    if (!win) split_meta(sm, p, a, j0, j1, true);
 
-    float qg[NG];
-    stage_query<NG>(p, a, g, qs, qg);
+    const float qg = stage_query(p, a, g, w, qs[w]);
 
-    State<NG> st;
-#pragma unroll
-    for (int hh = 0; hh < NG; hh++) {
-        st.o[hh] = f4{0.f, 0.f, 0.f, 0.f};
-        st.ps_lane[hh] = 0.0f;
-        st.pb_lane[hh] = 0.0f;
-    }
+    State st;
+    st.o = f4{0.f, 0.f, 0.f, 0.f};
     st.m_run = -INFINITY;
-    st.l_lane = 0.0f;
+    st.l_lane = st.ps_lane = st.pb_lane = 0.0f;
 
+    int buf = 0;
     if (!win) {
-        for (int jb = j0; jb < j1; jb++) {
-            if (jb - sm.base >= 64) split_meta(sm, p, a, jb, j1);   // blocks are visited in order
+        for (int jb = j0; jb < j1; jb++, buf ^= 1) {
+            if (jb - sm.base >= 64) split_meta(sm, p, a, jb, j1, true);   // blocks are visited in order
             const int i = jb - sm.base;
             const int bw = __builtin_amdgcn_readlane(sm.bits, i);
             const uint8_t *kb = p.k.pool + (((uint64_t)(uint32_t)__builtin_amdgcn_readlane(sm.khi, i) << 32) |
@@ -481,75 +520,82 @@ __global__ __launch_bounds__(64, (NG <= 2 ? 3 : 2)) void decode_g4_split(DecodeA
             const uint8_t *vb = p.v.pool + (((uint64_t)(uint32_t)__builtin_amdgcn_readlane(sm.vhi, i) << 32) |
                                             (uint32_t)__builtin_amdgcn_readlane(sm.vlo, i));
             switch (bw) {
-            case 2: round_block<2, NG>(st, qs, qg, kb, vb, p.t.H, g, p.c, vt); break;
-            case 3: round_block<3, NG>(st, qs, qg, kb, vb, p.t.H, g, p.c, vt); break;
-            case 4: round_block<4, NG>(st, qs, qg, kb, vb, p.t.H, g, p.c, vt); break;
-            default: round_block<8, NG>(st, qs, qg, kb, vb, p.t.H, g, p.c, vt); break;
+            case 2: round_block<2, NG>(st, qs[w], qg, kb, vb, p.t.H, g, w, p.c, vt[w], xs[buf]); break;
+            case 3: round_block<3, NG>(st, qs[w], qg, kb, vb, p.t.H, g, w, p.c, vt[w], xs[buf]); break;
+            case 4: round_block<4, NG>(st, qs[w], qg, kb, vb, p.t.H, g, w, p.c, vt[w], xs[buf]); break;
+            default: round_block<8, NG>(st, qs[w], qg, kb, vb, p.t.H, g, w, p.c, vt[w], xs[buf]); break;
             }
         }
     } else {
-        const uint16_t *kw = p.k.window + (size_t)a * p.t.window_cap * p.t.H * D;
-        const uint16_t *vw = p.v.window + (size_t)a * p.t.window_cap * p.t.H * D;
-        for (int w0 = 0; w0 < nw; w0 += 64) round_window<NG>(st, qs, kw, vw, p.t.H, g, w0, nw, p.c, vt);
+        const uint16_t *kwin = p.k.window + (size_t)a * p.t.window_cap * p.t.H * D;
+        const uint16_t *vwin = p.v.window + (size_t)a * p.t.window_cap * p.t.H * D;
+        for (int w0 = 0; w0 < nw; w0 += 64, buf ^= 1)
+            round_window<NG>(st, qs[w], kwin, vwin, p.t.H, g, w, w0, nw, p.c, vt[w], xs[buf]);
     }
 
     // Head j's sums over the 16 lanes that hold it.
-    float l = st.l_lane, ps[NG], pb[NG];
-#pragma unroll
-    for (int gg = 0; gg < NG; gg++) {
-        ps[gg] = st.ps_lane[gg];
-        pb[gg] = st.pb_lane[gg];
-    }
+    float l = st.l_lane, ps = st.ps_lane, pb = st.pb_lane;
 #pragma unroll
     for (int o = 4; o < 64; o <<= 1) {
         l += __shfl_xor(l, o);
-#pragma unroll
-        for (int gg = 0; gg < NG; gg++) {
-            ps[gg] += __shfl_xor(ps[gg], o);
-            pb[gg] += __shfl_xor(pb[gg], o);
-        }
+        ps += __shfl_xor(ps, o);
+        pb += __shfl_xor(pb, o);
     }
     const size_t stride = (size_t)(D + 2);
     const size_t rbase = (size_t)a * p.Hq + (size_t)g * p.G;
-    if (b == 0 && j < p.G) {
+    if (w == 0 && b == 0 && j < p.G) {
         float *pr = p.part + ((rbase + j) * p.n_splits + s) * stride;
         pr[0] = st.m_run;
         pr[1] = l;
     }
-    // lane l holds dim 64hh + (chunk-order position l) of head i in o[hh][i]:
-    // output = sum p'(1024+code) - 1024 sum p' + sum p b (lane i holds head i's sums)
-    const int d = ((4 * b + j) & ~7) | (((4 * b + j) & 7) >> 1) | (((4 * b + j) & 1) << 2);
+    // lane l holds group position l (dim 64w + d) of head i in o[i]:
+    // output = (sum p''(1024+m c) - 1024 sum p'')/64 + sum p b for coded
+    // tokens, sum p v for the window (lane i holds head i's sums)
+    const int d = 64 * w + ((lane & ~7) | ((lane & 7) >> 1) | ((lane & 1) << 2));
 #pragma unroll
     for (int i = 0; i < 4; i++) {
-        float corr[NG];
-#pragma unroll
-        for (int gg = 0; gg < NG; gg++) corr[gg] = __shfl(pb[gg], i) - 1024.0f * __shfl(ps[gg], i);
+        const float psi = __shfl(ps, i), pbi = __shfl(pb, i);
         if (i < p.G) {
-            float *pr = p.part + ((rbase + i) * p.n_splits + s) * stride + 2;
-#pragma unroll
-            for (int hh = 0; hh < NG; hh++) pr[64 * hh + d] = st.o[hh][i] + corr[hh];
+            const float v = win ? st.o[i] : __builtin_fmaf(st.o[i] - 1024.0f * psi, 1.0f / FV, pbi);
+            p.part[((rbase + i) * p.n_splits + s) * stride + 2 + d] = v;
         }
     }
+
+    // Last workgroup of (a, g) to finish merges every split.  The release
+    // fence makes this workgroup's partials visible device-wide before its
+    // ticket; the ticket counter wraps to zero on the last ticket.
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        __threadfence();
+        const uint32_t t = atomicInc(tickets + (size_t)a * p.t.H + g, (uint32_t)(ns - 1));
+        last = (t == (uint32_t)(ns - 1));
+    }
+    __syncthreads();
+    if (!last) return;
+    __threadfence();
+    merge_splits(p, a, g, w, ns);
 }
 
 // Block scores for top-K selection: the Q.K products and scale/bias
-// corrections of the decode above, then the largest score of the block over
-// its 64 tokens and the KV head's G query heads, times the softmax scale.
-// One wave per (split, KV head, sequence); scores_h [A][max_blocks][H].
+// corrections of the decode above, over every group of the head, then the
+// largest score of the block over its 64 tokens and the KV head's G query
+// heads, times the softmax scale.  One wave per (split, KV head, sequence);
+// scores_h [A][max_blocks][H].
 template <int B, int NG>
-__device__ __forceinline__ float block_max(const h4 (*qs)[4], const float (&qg)[NG], const uint8_t *kblk, int H,
+__device__ __forceinline__ float block_max(const h4 (*qs)[16][4], const float *qg, const uint8_t *kblk, int H,
                                            int g, int G)
 {
-    constexpr uint32_t CODE_ROW = 8 * NG * B;
-    const uint32_t row = (uint32_t)g * 64 + threadIdx.x;
-    const uint32_t moff = (uint32_t)H * 64 * CODE_ROW + 4 * NG * row;
-    uint32_t kw[FullRow<B, NG>::NDW], km[NG];
-    FullRow<B, NG>::load(kw, kblk + row * CODE_ROW);
+    constexpr uint32_t ROW = 8 * NG * B;
+    const uint32_t tok = (uint32_t)g * 64 + threadIdx.x;
+    uint32_t kw[NG][GroupRow<B>::NDW], km[NG];
 #pragma unroll
-    for (int i = 0; i < NG; i++) km[i] = reinterpret_cast<const uint32_t *>(kblk + moff)[i];
-    f4 T[NG];
-    dots_phase<B, NG>(T, qs, kw);
-    const f4 s = scores_of<NG>(T, km, qg);
+    for (int w = 0; w < NG; w++) {
+        GroupRow<B>::load(kw[w], kblk + tok * ROW + 8 * B * w);
+        km[w] = *reinterpret_cast<const uint32_t *>(kblk + (uint32_t)H * 64 * ROW + 4 * (NG * tok + w));
+    }
+    f4 s = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int w = 0; w < NG; w++) s += group_scores<B>(qs[w], qg[w], kw[w], km[w]);
     float m = ((int)(threadIdx.x & 3) < G) ? fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3])) : -INFINITY;
 #pragma unroll
     for (int o = 1; o < 64; o <<= 1) m = fmaxf(m, __shfl_xor(m, o));
@@ -557,20 +603,20 @@ __device__ __forceinline__ float block_max(const h4 (*qs)[4], const float (&qg)[
 }
 
 template <int NG>
-__global__ __launch_bounds__(64, (NG <= 2 ? 3 : 2)) void decode_g4_scores(DecodeArgs p, float scale, float *scores_h)
+__global__ __launch_bounds__(64) void decode_g4_scores(DecodeArgs p, float scale, float *scores_h)
 {
-    constexpr int NCH = 8 * NG;
-    __shared__ __attribute__((aligned(16))) h4 qs[2 * NCH][4];
+    __shared__ __attribute__((aligned(16))) h4 qs[NG][16][4];
     const int s = blockIdx.x, g = blockIdx.y, a = blockIdx.z;
     const int nb = seq_blocks(p.t, a);
     const int j0 = s * p.SB, j1 = min(j0 + p.SB, nb);
     if (j0 >= j1) return;
     SplitMeta sm;
-    split_meta(sm, p, a, j0, j1);
+    split_meta(sm, p, a, j0, j1, false);
     float qg[NG];
-    stage_query<NG>(p, a, g, qs, qg);
+#pragma unroll
+    for (int w = 0; w < NG; w++) qg[w] = stage_query(p, a, g, w, qs[w]);
     for (int jb = j0; jb < j1; jb++) {
-        if (jb - sm.base >= 64) split_meta(sm, p, a, jb, j1);   // blocks are visited in order
+        if (jb - sm.base >= 64) split_meta(sm, p, a, jb, j1, false);   // blocks are visited in order
         const int i = jb - sm.base;
         const int bw = __builtin_amdgcn_readlane(sm.bits, i);
         const uint8_t *kb = p.k.pool + (((uint64_t)(uint32_t)__builtin_amdgcn_readlane(sm.khi, i) << 32) |
@@ -590,16 +636,16 @@ __global__ __launch_bounds__(64, (NG <= 2 ? 3 : 2)) void decode_g4_scores(Decode
 
 bool decode_g4_supported(int D, int G) { return G <= 4 && (D == 64 || D == 128 || D == 256); }
 
-void decode_g4_plan(int A, int H, int max_blocks, int window_cap, int *SB, int *n_splits)
+void decode_g4_plan(int A, int H, int D, int max_blocks, int window_cap, int *SB, int *n_splits)
 {
-    // Longest splits that still give about KVQ_G4_WAVES waves (latency is
-    // hidden by waves in flight; longer splits keep the merge's partials small).
+    // Longest splits that still give about KVQ_G4_WAVES waves (one wave per
+    // 64 dims of a workgroup); longer splits keep the partials small.
 #ifndef KVQ_G4_WAVES
-#define KVQ_G4_WAVES 2048
+#define KVQ_G4_WAVES 4096
 #endif
+    const long ng = D / 64;
     int sb = 64;
-    while (sb > 1 && (long)A * H * ((max_blocks + sb - 1) / sb) < KVQ_G4_WAVES) sb >>= 1;
-    while ((max_blocks + sb - 1) / sb + 1 > 512) sb <<= 1;     // merge limit on splits
+    while (sb > 1 && (long)A * H * ng * ((max_blocks + sb - 1) / sb) < KVQ_G4_WAVES) sb >>= 1;
     *SB = sb;
     *n_splits = (max_blocks + sb - 1) / sb + (window_cap > 0 ? 1 : 0);
     if (*n_splits < 1) *n_splits = 1;
@@ -619,13 +665,13 @@ hipError_t launch_g4_scores(const DecodeArgs &p, float scale, float *scores_h, h
     return hipGetLastError();
 }
 
-hipError_t launch_decode_g4(const DecodeArgs &p, hipStream_t s)
+hipError_t launch_decode_g4(const DecodeArgs &p, uint32_t *tickets, hipStream_t s)
 {
     dim3 grid(p.n_splits, p.t.H, p.t.A);
     switch (p.t.D) {
-    case 64: decode_g4_split<1><<<grid, 64, 0, s>>>(p); break;
-    case 128: decode_g4_split<2><<<grid, 64, 0, s>>>(p); break;
-    case 256: decode_g4_split<4><<<grid, 64, 0, s>>>(p); break;
+    case 64: decode_g4_split<1><<<grid, 64, 0, s>>>(p, tickets); break;
+    case 128: decode_g4_split<2><<<grid, 128, 0, s>>>(p, tickets); break;
+    case 256: decode_g4_split<4><<<grid, 256, 0, s>>>(p, tickets); break;
     default: return hipErrorInvalidValue;
     }
     return hipGetLastError();

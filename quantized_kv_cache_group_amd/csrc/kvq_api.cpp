@@ -74,6 +74,7 @@ struct Plan {
     int mla_sb, mla_splits;     // latent decode
     int ch_row_tiles, ch_splits, ch_split_tiles;   // tuned chunk
     bool ch_ok;
+    size_t ticket_bytes;        // decode: per-(sequence, KV head) merge tickets at the start of the workspace
     size_t ws_bytes;
 };
 
@@ -94,13 +95,15 @@ int plan_attention(const kvq_layout *L, int n_q_heads, int rope_dim, int n_new, 
     if ((int64_t)pl->n_row_tiles * L->n_heads > kMaxGrid) return KVQ_EUNSUPPORTED;
     const size_t rows = (size_t)L->n_seqs * n_qtok * n_q_heads;
     if (rows > 0x7fffffffu) return KVQ_EUNSUPPORTED;
+    pl->ticket_bytes = 0;
     pl->ws_bytes = round256(rows * (size_t)pl->n_splits * (size_t)(L->head_dim + 2) * sizeof(float));
     if (n_new == 0) {
         decode_gqa_plan(L->n_seqs, L->n_heads, L->max_blocks, L->window_cap, &pl->sb, &pl->dec_splits);
         size_t t = round256(rows * (size_t)pl->dec_splits * (size_t)(L->head_dim + 2) * sizeof(float));
         if (t > pl->ws_bytes) pl->ws_bytes = t;
         if (decode_g4_supported(L->head_dim, G)) {
-            decode_g4_plan(L->n_seqs, L->n_heads, L->max_blocks, L->window_cap, &pl->g4_sb, &pl->g4_splits);
+            decode_g4_plan(L->n_seqs, L->n_heads, L->head_dim, L->max_blocks, L->window_cap, &pl->g4_sb,
+                           &pl->g4_splits);
             t = round256(rows * (size_t)pl->g4_splits * (size_t)(L->head_dim + 2) * sizeof(float));
             if (t > pl->ws_bytes) pl->ws_bytes = t;
         }
@@ -109,6 +112,10 @@ int plan_attention(const kvq_layout *L, int n_q_heads, int rope_dim, int n_new, 
             t = round256(rows * (size_t)pl->mla_splits * (size_t)(L->head_dim + 2) * sizeof(float));
             if (t > pl->ws_bytes) pl->ws_bytes = t;
         }
+        // Every decode workspace starts with the tickets (whichever kernel
+        // runs), so no decode call overwrites them with partials.
+        pl->ticket_bytes = round256((size_t)L->n_seqs * L->n_heads * sizeof(uint32_t));
+        pl->ws_bytes += pl->ticket_bytes;
     }
     pl->ch_ok = false;
     if (n_new > 0 && chunk_supported(L->head_dim)) {
@@ -336,7 +343,7 @@ int kvq_block_sensitivity(const uint16_t *k, const uint16_t *v, int32_t n_seqs, 
     if (!sensitivity_supported(n_heads, head_dim, n_q_heads)) return KVQ_EUNSUPPORTED;
     if (!k || !v || !q || !S || !aligned(k, 16) || !aligned(v, 16) || !aligned(q, 2) || !aligned(S, 4))
         return KVQ_EINVAL;
-    if (!isfinite(softmax_scale)) return KVQ_EINVAL;
+    if (!(softmax_scale > 0.0f) || !isfinite(softmax_scale)) return KVQ_EINVAL;
     return hip_status(launch_sensitivity(k, v, n_seqs, seq_tokens, n_blocks, n_heads, head_dim, q, n_q_heads,
                                          softmax_scale, S, static_cast<hipStream_t>(stream)));
 }
@@ -376,9 +383,11 @@ int kvq_attend_decode(const kvq_layout *L, const kvq_store *K, const kvq_store *
     if ((rope_dim > 0) != (rope != nullptr)) return KVQ_EINVAL;
     if (rope && !aligned(rope, 16)) return KVQ_EINVAL;
     if (!q || !out || !aligned(q, 16) || !aligned(out, 16)) return KVQ_EINVAL;
-    if (!isfinite(softmax_scale)) return KVQ_EINVAL;
+    if (!(softmax_scale > 0.0f) || !isfinite(softmax_scale)) return KVQ_EINVAL;
     if (workspace_bytes < pl.ws_bytes) return KVQ_ENOSPC;
     if (!workspace || !aligned(workspace, 256)) return KVQ_EINVAL;
+    uint32_t *tickets = static_cast<uint32_t *>(workspace);
+    float *part = reinterpret_cast<float *>(static_cast<uint8_t *>(workspace) + pl.ticket_bytes);
 
     if (V && rope_dim == 0 && decode_gqa_supported(L->head_dim)) {
         DecodeArgs d{};
@@ -387,7 +396,7 @@ int kvq_attend_decode(const kvq_layout *L, const kvq_store *K, const kvq_store *
         d.v = store(V);
         d.q = q;
         d.out = out;
-        d.part = static_cast<float *>(workspace);
+        d.part = part;
         d.Hq = n_q_heads;
         d.G = n_q_heads / L->n_heads;
         d.SB = pl.sb;
@@ -397,9 +406,7 @@ int kvq_attend_decode(const kvq_layout *L, const kvq_store *K, const kvq_store *
         if (decode_g4_supported(L->head_dim, d.G)) {
             d.SB = pl.g4_sb;
             d.n_splits = pl.g4_splits;
-            hipError_t e = launch_decode_g4(d, hs);
-            if (e != hipSuccess) return KVQ_EHIP;
-            return hip_status(launch_decode_merge(d, hs));
+            return hip_status(launch_decode_g4(d, tickets, hs));
         }
         return hip_status(launch_decode_gqa(d, hs));
     }
@@ -411,7 +418,7 @@ int kvq_attend_decode(const kvq_layout *L, const kvq_store *K, const kvq_store *
         d.v = store(K);
         d.q = q;
         d.out = out;
-        d.part = static_cast<float *>(workspace);
+        d.part = part;
         d.Hq = n_q_heads;
         d.G = n_q_heads;
         d.SB = pl.mla_sb;
@@ -441,13 +448,15 @@ int kvq_attend_decode(const kvq_layout *L, const kvq_store *K, const kvq_store *
     a.n_row_tiles = pl.n_row_tiles;
     a.split_keys = pl.split_keys;
     a.n_splits = pl.n_splits;
-    a.part = static_cast<float *>(workspace);
+    a.part = part;
     a.out = out;
     return hip_status(launch_attend_generic(a, static_cast<hipStream_t>(stream)));
 }
 
 namespace {
-// Workspace of a top-K call: selection tables, then the decode's own.
+// Workspace of a top-K call: the decode's own workspace first (so its merge
+// tickets sit at the start, as for kvq_attend_decode), then the selection
+// tables.
 struct TopkWs {
     size_t scores, n_sel, sel_idx, sel_bits, sel_koff, sel_voff, rope_sel, dec, total;
     kvq_layout L2;                            // pointers filled in at call time
@@ -461,24 +470,26 @@ static int topk_plan(const kvq_layout *L, int32_t n_q_heads, int32_t rope_dim, i
     if (top_k < 1 || n_q_heads < 1 || n_q_heads % L->n_heads) return KVQ_EINVAL;
     if (rope_dim != 0 && rope_dim != 64) return KVQ_EUNSUPPORTED;
     if (!topk_supported(L->max_blocks, n_q_heads / L->n_heads, L->head_dim, rope_dim)) return KVQ_EUNSUPPORTED;
-    const int k = top_k < L->max_blocks ? top_k : (L->max_blocks > 0 ? L->max_blocks : 1);
+    // kept blocks per sequence (0 for a window-only layout); arrays hold at least one entry
+    const int k = top_k < L->max_blocks ? top_k : L->max_blocks;
+    const size_t ka = (size_t)(k > 0 ? k : 1);
     const size_t A = (size_t)L->n_seqs;
-    size_t pos = 0;
-    w->scores = pos;   pos += round256(A * (size_t)(L->max_blocks > 0 ? L->max_blocks : 1) * L->n_heads * 4);
-    w->n_sel = pos;    pos += round256(A * 4);
-    w->sel_idx = pos;  pos += round256(A * (size_t)k * 4);
-    w->sel_bits = pos; pos += round256(A * (size_t)k);
-    w->sel_koff = pos; pos += round256(A * (size_t)k * 8);
-    w->sel_voff = pos; pos += round256(A * (size_t)k * 8);
-    w->rope_sel = pos;
-    pos += round256(A * ((size_t)64 * k + L->window_cap) * L->n_heads * rope_dim * 2);
     w->L2 = *L;
     w->L2.max_blocks = k;
     size_t dec = 0;
     if ((st = kvq_decode_workspace(&w->L2, n_q_heads, rope_dim, &dec))) return st;
-    w->dec = pos;
+    w->dec = 0;
     w->dec_bytes = dec;
-    w->total = pos + dec;
+    size_t pos = round256(dec);
+    w->scores = pos;   pos += round256(A * (size_t)(L->max_blocks > 0 ? L->max_blocks : 1) * L->n_heads * 4);
+    w->n_sel = pos;    pos += round256(A * 4);
+    w->sel_idx = pos;  pos += round256(A * ka * 4);
+    w->sel_bits = pos; pos += round256(A * ka);
+    w->sel_koff = pos; pos += round256(A * ka * 8);
+    w->sel_voff = pos; pos += round256(A * ka * 8);
+    w->rope_sel = pos;
+    pos += round256(A * ((size_t)64 * ka + L->window_cap) * L->n_heads * rope_dim * 2);
+    w->total = pos;
     return KVQ_OK;
 }
 }  // namespace
@@ -507,7 +518,7 @@ int kvq_attend_decode_topk(const kvq_layout *L, const kvq_store *K, const kvq_st
     if (rope && !aligned(rope, 16)) return KVQ_EINVAL;
     if (!q || !out || !aligned(q, 16) || !aligned(out, 16)) return KVQ_EINVAL;
     if (selected && !aligned(selected, 4)) return KVQ_EINVAL;
-    if (!isfinite(softmax_scale)) return KVQ_EINVAL;
+    if (!(softmax_scale > 0.0f) || !isfinite(softmax_scale)) return KVQ_EINVAL;
     if (workspace_bytes < w.total) return KVQ_ENOSPC;
     if (!workspace || !aligned(workspace, 256)) return KVQ_EINVAL;
     const int k = w.L2.max_blocks;
@@ -533,20 +544,7 @@ int kvq_attend_decode_topk(const kvq_layout *L, const kvq_store *K, const kvq_st
     p.selected = selected;
     p.sel_stride = top_k;
     p.score_stride = 1;
-    hipStream_t hs = static_cast<hipStream_t>(stream);
-    DecodeArgs g4{};
-    const bool use_g4 = rope_dim == 0 && decode_g4_supported(L->head_dim, p.G);
-    if (use_g4) {
-        g4.t = tables(L);
-        g4.k = store(K);
-        g4.q = q;
-        g4.Hq = n_q_heads;
-        g4.G = p.G;
-        int splits = 0;
-        decode_g4_plan(L->n_seqs, L->n_heads, L->max_blocks, 0, &g4.SB, &splits);
-        p.score_stride = L->n_heads;
-    }
-    if (launch_topk_select(p, use_g4 ? &g4 : nullptr, hs) != hipSuccess) return KVQ_EHIP;
+    // The decode over the compacted tables, validated before anything runs.
     kvq_layout L2 = w.L2;
     L2.n_blocks = p.n_sel;
     L2.bits = p.sel_bits;
@@ -557,8 +555,24 @@ int kvq_attend_decode_topk(const kvq_layout *L, const kvq_store *K, const kvq_st
         V2 = *V;
         V2.offset = p.sel_voff;
     }
+    if ((st = check_layout(&L2)) || (st = check_store(&L2, &K2)) || (V && (st = check_store(&L2, &V2))))
+        return st;
+    hipStream_t hs = static_cast<hipStream_t>(stream);
+    DecodeArgs g4{};
+    const bool use_g4 = rope_dim == 0 && decode_g4_supported(L->head_dim, p.G);
+    if (use_g4) {
+        g4.t = tables(L);
+        g4.k = store(K);
+        g4.q = q;
+        g4.Hq = n_q_heads;
+        g4.G = p.G;
+        int splits = 0;
+        decode_g4_plan(L->n_seqs, L->n_heads, L->head_dim, L->max_blocks, 0, &g4.SB, &splits);
+        p.score_stride = L->n_heads;
+    }
+    if (launch_topk_select(p, use_g4 ? &g4 : nullptr, hs) != hipSuccess) return KVQ_EHIP;
     return kvq_attend_decode(&L2, &K2, V ? &V2 : nullptr, p.rope_sel, rope_dim, q, n_q_heads, softmax_scale, out,
-                             ws + w.dec, workspace_bytes - w.dec, stream);
+                             ws + w.dec, w.dec_bytes, stream);
 }
 
 int kvq_chunk_workspace(const kvq_layout *L, int32_t n_q_heads, int32_t n_new, size_t *bytes)
@@ -587,12 +601,12 @@ int kvq_attend_chunk(const kvq_layout *L, const kvq_store *K, const kvq_store *V
     if (!q_new || !k_new || !v_new || !out) return KVQ_EINVAL;
     if (!aligned(q_new, 16) || !aligned(k_new, 16) || !aligned(v_new, 16) || !aligned(out, 16))
         return KVQ_EINVAL;
-    if (!isfinite(softmax_scale)) return KVQ_EINVAL;
+    if (!(softmax_scale > 0.0f) || !isfinite(softmax_scale)) return KVQ_EINVAL;
     if (n_new == 0) return KVQ_OK;
     if (workspace_bytes < pl.ws_bytes) return KVQ_ENOSPC;
     if (!workspace || !aligned(workspace, 256)) return KVQ_EINVAL;
 
-    if (pl.ch_ok && softmax_scale > 0.0f) {
+    if (pl.ch_ok) {
         ChunkArgs c{};
         c.t = tables(L);
         c.k = store(K);

@@ -162,10 +162,14 @@ __global__ __launch_bounds__(256) void select_blocks(TopkArgs p)
     uint64_t pko[PF], pvo[PF];
 #pragma unroll
     for (int k = 0; k < PF; k++) {
-        const int i = min(b0 + k, max(nb - 1, 0));
-        pbits[k] = p.t.bits[in + i];
-        pko[k] = p.k.offset[in + i];
-        pvo[k] = p.sel_voff ? p.v.offset[in + i] : 0;
+        pbits[k] = 0;
+        pko[k] = pvo[k] = 0;
+        if (nb > 0) {                                   // window-only tables may be empty (or null)
+            const int i = min(b0 + k, nb - 1);
+            pbits[k] = p.t.bits[in + i];
+            pko[k] = p.k.offset[in + i];
+            pvo[k] = p.sel_voff ? p.v.offset[in + i] : 0;
+        }
     }
     // a block's score: the max over its score_stride entries (the first 16
     // loads are independent of each other)

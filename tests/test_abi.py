@@ -28,12 +28,28 @@ def test_header_symbols_exported():
         assert getattr(L, n) is not None
 
 
+def _needed(path):
+    """DT_NEEDED entries of a shared library (readelf -d)."""
+    import subprocess
+    out = subprocess.run(["readelf", "-d", path], capture_output=True, text=True, check=True).stdout
+    return re.findall(r"\(NEEDED\)\s+Shared library: \[([^\]]+)\]", out)
+
+
 def test_library_links_hip_and_not_oracle():
-    maps = open(f"/proc/{os.getpid()}/maps").read()
+    """libkvq.so depends on the HIP runtime and not on the oracle: its
+    DT_NEEDED list names libamdhip64 and nothing of libkvq_ref, and loading
+    it maps the HIP runtime but not the oracle."""
+    needed = _needed(kvq.LIB_PATH)
+    assert any(n.startswith("libamdhip64") for n in needed), needed
+    assert not any("kvq_ref" in n for n in needed), needed
+    import sys
+    before = "oracle" in sys.modules
     kvq.lib()
     maps = open(f"/proc/{os.getpid()}/maps").read()
     assert "libkvq.so" in maps
     assert "libamdhip64" in maps
+    if not before:                      # nothing in this process has loaded the oracle yet
+        assert "libkvq_ref" not in maps
 
 
 def test_block_bytes():
@@ -150,6 +166,9 @@ def test_decode_rejects():
     assert _decode(L, K, out=None) == kvq.KVQ_EINVAL
     assert _decode(L, K, q=FAKE + 4) == kvq.KVQ_EINVAL
     assert _decode(L, K, scale=float("nan")) == kvq.KVQ_EINVAL
+    assert _decode(L, K, scale=0.0) == kvq.KVQ_EINVAL        # scales must be positive
+    assert _decode(L, K, scale=-0.125) == kvq.KVQ_EINVAL
+    assert _decode(L, K, scale=float("inf")) == kvq.KVQ_EINVAL
     assert _decode(L, K, rope_dim=64) == kvq.KVQ_EINVAL     # rope_dim without a rope buffer
     assert _decode(L, K, rope=FAKE, rope_dim=0) == kvq.KVQ_EINVAL
     assert _decode(L, K, rope=FAKE, rope_dim=32) == kvq.KVQ_EUNSUPPORTED
@@ -191,7 +210,60 @@ def test_chunk_rejects():
     assert call(n=-1) == kvq.KVQ_EINVAL
     assert call(Hq=3) == kvq.KVQ_EINVAL
     assert call(wsb=16) == kvq.KVQ_ENOSPC
+    assert call(scale=0.0) == kvq.KVQ_EINVAL
+    assert call(scale=-0.1) == kvq.KVQ_EINVAL
     assert call(n=0) == kvq.KVQ_OK                            # nothing to do, nothing launched
+
+
+def test_decode_workspace_starts_with_tickets():
+    """The decode workspace covers the merge tickets (4 bytes per sequence and
+    KV head, rounded to 256) on top of the partials, whatever kernel runs."""
+    n = ctypes.c_size_t(0)
+    small = _layout(n_seqs=1, n_heads=2)
+    big = _layout(n_seqs=100, n_heads=2)
+    assert kvq.lib().kvq_decode_workspace(ctypes.byref(small), 8, 0, ctypes.byref(n)) == kvq.KVQ_OK
+    a = n.value
+    assert kvq.lib().kvq_decode_workspace(ctypes.byref(big), 8, 0, ctypes.byref(n)) == kvq.KVQ_OK
+    assert n.value >= 100 * 2 * 4 + 256 and a >= 256 + 256
+
+
+def _topk(L, K, V=None, Hq=8, scale=0.125, top_k=4, selected=None, ws=FAKE, ws_bytes=1 << 40):
+    P = lambda x: None if x is None else ctypes.c_void_p(x)
+    return kvq.lib().kvq_attend_decode_topk(ctypes.byref(L), ctypes.byref(K),
+                                            None if V is None else ctypes.byref(V), None, 0,
+                                            P(FAKE), Hq, scale, top_k, P(FAKE), P(selected), P(ws),
+                                            ws_bytes, None)
+
+
+def test_topk_rejects():
+    L, K, V = _layout(), _store(), _store()
+    assert _topk(L, K, V, scale=0.0) == kvq.KVQ_EINVAL
+    assert _topk(L, K, V, scale=-1.0) == kvq.KVQ_EINVAL
+    assert _topk(L, K, V, top_k=0) == kvq.KVQ_EINVAL
+    assert _topk(L, K, V, selected=FAKE + 2) == kvq.KVQ_EINVAL
+    assert _topk(L, K, V, ws_bytes=16) == kvq.KVQ_ENOSPC
+    assert _topk(L, K, V, ws=FAKE + 64) == kvq.KVQ_EINVAL
+
+
+def test_topk_window_only_layout_with_null_tables():
+    """A window-only layout may pass null widths, offsets and pools: the
+    workspace query succeeds and argument checks reach the workspace size
+    with no table dereferenced (on the GPU the call keeps no block)."""
+    L = _layout(max_blocks=0, window_cap=64, bits=None)
+    K = _store(offset=None, pool=None)
+    V = _store(offset=None, pool=None)
+    n = ctypes.c_size_t(0)
+    assert kvq.lib().kvq_topk_workspace(ctypes.byref(L), 8, 0, 4, ctypes.byref(n)) == kvq.KVQ_OK
+    assert n.value > 0 and n.value % 256 == 0
+    assert _topk(L, K, V, ws_bytes=n.value - 1) == kvq.KVQ_ENOSPC
+    assert _topk(L, K, V, scale=0.0, ws_bytes=n.value) == kvq.KVQ_EINVAL
+
+
+def test_sensitivity_rejects_nonpositive_scale():
+    f = kvq.lib().kvq_block_sensitivity
+    P = ctypes.c_void_p
+    for sc in (0.0, -0.5, float("nan")):
+        assert f(P(FAKE), P(FAKE), 1, 64, 1, 2, 64, P(FAKE), 8, sc, P(FAKE), None) == kvq.KVQ_EINVAL
 
 
 def test_append_rejects():

@@ -194,23 +194,6 @@ def test_chunk_one_token_equals_decode():
     close(got[0], _ref_chunk(b, 0, qn[0], kn[0], vn[0], D ** -0.5), what="chunk-1")
 
 
-def test_chunk_llama_32k_restore_512_sampled_rows():
-    """Full 32768-token restore + 512-token causal chunk; the oracle checks
-    sampled query rows (first, second, middle, last), the GPU runs the whole
-    launch as the benchmark does."""
-    w = syn.workload(3)
-    k_src = [w.kv(0, 0, syn.TAG_K)]
-    v_src = [w.kv(0, 0, syn.TAG_V)]
-    b = build(w.n_kv_heads, w.head_dim, w.lengths, k_src=k_src, v_src=v_src)
-    gpu_pool_matches(b)
-    qn, kn, vn = w.chunk_new()
-    got = _chunk(b, qn[None], kn[None], vn[None], w.scale)[0]
-    assert np.all(np.isfinite(got))
-    for r0, r1 in [(0, 2), (255, 256), (510, 512)]:
-        want = _ref_chunk(b, 0, qn, kn, vn, w.scale, rows=(r0, r1))
-        close(got[r0:r1], want[r0:r1], what=f"chunk rows {r0}:{r1}")
-
-
 @pytest.mark.parametrize("D,G", [(64, 4), (256, 2), (128, 8)])
 def test_chunk_mixed_widths_window(D, G):
     """Chunk over a cache with 2/3/4/8-bit blocks and a bf16 window, causal
@@ -229,3 +212,27 @@ def test_chunk_mixed_widths_window(D, G):
     got = _chunk(b, qn, kn, vn, D ** -0.5)
     for a in range(A):
         close(got[a], _ref_chunk(b, a, qn[a], kn[a], vn[a], D ** -0.5), what=f"chunk D={D} a={a}")
+
+
+def test_decode_workspace_reuse_leaves_tickets_zero():
+    """One zero-filled workspace serves several decode and top-K calls in a
+    row: every call gives the same output as the first, and the merge
+    tickets at the start of the workspace are zero after each call."""
+    H, D, G = 8, 128, 4
+    lengths = [64 * 30 + 50, 64 * 9, 300]
+    b = build(H, D, lengths, keep_recent=60, seed=33)
+    c = b.cache
+    q = to_dev_bf16(syn.random_normal_bf16((3, G * H, D), 34))
+    nb = max(c.topk_workspace_bytes(G * H, 4), c.decode_workspace_bytes(G * H))
+    ws = torch.zeros(nb, dtype=torch.uint8, device="cuda")
+    tb = (3 * H * 4 + 255) // 256 * 256
+    first = c.attend_decode(q, D ** -0.5, workspace=ws).cpu().numpy()
+    assert int(ws[:tb].count_nonzero()) == 0
+    for i in range(3):
+        c.attend_decode_topk(q, D ** -0.5, 4, workspace=ws)
+        torch.cuda.synchronize()
+        assert int(ws[:tb].count_nonzero()) == 0
+        again = c.attend_decode(q, D ** -0.5, workspace=ws).cpu().numpy()
+        assert int(ws[:tb].count_nonzero()) == 0
+        assert np.array_equal(first, again)
+    close(first, ref_decode(b, syn.random_normal_bf16((3, G * H, D), 34), D ** -0.5), what="reuse")

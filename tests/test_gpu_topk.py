@@ -159,3 +159,46 @@ def test_topk_long_runs_per_thread(nb, K, D, H, G):
     got, sel = _run(b, q, scale, K)
     _check_selection(b, q, scale, K, sel)
     close(got, _ref_sparse(b, q, scale, sel), what=f"topk {nb} blocks")
+
+
+def test_topk_window_only_null_tables():
+    """A window-only layout through the C ABI with null widths, offsets and
+    pools: no block is kept, `selected` is all -1, and the output is the
+    decode over the windows."""
+    import ctypes
+    import quantized_kv_cache_group_amd as kvq
+    A, H, D, G, K, cap = 2, 2, 128, 4, 3, 100
+    nw = [100, 37]
+    kw = [syn.random_normal_bf16((n, H, D), 80 + a) for a, n in enumerate(nw)]
+    vw = [syn.random_normal_bf16((n, H, D), 90 + a) for a, n in enumerate(nw)]
+    kwin = torch.zeros((A, cap, H, D), dtype=torch.bfloat16, device="cuda")
+    vwin = torch.zeros_like(kwin)
+    for a in range(A):
+        kwin[a, :nw[a]] = to_dev_bf16(kw[a])
+        vwin[a, :nw[a]] = to_dev_bf16(vw[a])
+    n_blocks = torch.zeros(A, dtype=torch.int32, device="cuda")
+    n_window = torch.tensor(nw, dtype=torch.int32, device="cuda")
+    L = kvq.Layout(n_seqs=A, n_heads=H, head_dim=D, max_blocks=0, window_cap=cap,
+                   n_blocks=n_blocks.data_ptr(), n_window=n_window.data_ptr(), bits=None)
+    Ks = kvq.Store(offset=None, pool=None, window=kwin.data_ptr())
+    Vs = kvq.Store(offset=None, pool=None, window=vwin.data_ptr())
+    q = syn.random_normal_bf16((A, G * H, D), 81)
+    qd = to_dev_bf16(q)
+    out = torch.full((A, G * H, D), 7.0, dtype=torch.float32, device="cuda")
+    sel = torch.full((A, K), 5, dtype=torch.int32, device="cuda")
+    n = ctypes.c_size_t(0)
+    lib = kvq.lib()
+    assert lib.kvq_topk_workspace(ctypes.byref(L), G * H, 0, K, ctypes.byref(n)) == 0
+    ws = torch.zeros(n.value, dtype=torch.uint8, device="cuda")
+    scale = D ** -0.5
+    st = lib.kvq_attend_decode_topk(ctypes.byref(L), ctypes.byref(Ks), ctypes.byref(Vs), None, 0,
+                                    qd.data_ptr(), G * H, scale, K, out.data_ptr(), sel.data_ptr(),
+                                    ws.data_ptr(), n.value, None)
+    assert st == 0, kvq.lib().kvq_strerror(st)
+    torch.cuda.synchronize()
+    assert np.all(sel.cpu().numpy() == -1)
+    got = out.cpu().numpy()
+    for a in range(A):
+        want = oracle.attend_decode_seq(np.zeros(256, np.uint8), np.zeros(0, np.uint8), np.zeros(0, np.uint64),
+                                        np.zeros(0, np.uint64), kw[a], vw[a], None, H, D, q[a], scale)
+        close(got[a], want, what=f"window-only topk a={a}")
