@@ -41,7 +41,7 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=5)
-    p.add_argument("--workload", type=int, default=1, choices=[1, 2, 3, 4])
+    p.add_argument("--workload", type=int, default=2, choices=[1, 2, 3, 4])
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--copy-calibration", action="store_true",
                    help="only run a plain 1 GiB device copy (the reference for the HBM byte counters)")
@@ -167,80 +167,119 @@ def chunk_flops(w):
 
 # ---------------------------------------------------------------------------
 def cpu_baseline(w, layer_ids):
-    """Time the oracle on a bounded sample: quantize + attend for as many
-    agents as fit in about 20 s (for the chunk: the quantize of the cache and
-    a few query rows, the attention time scaled to all rows), as GB/s of the
-    same algorithmic traffic the GPU figure counts."""
-    import kvq_synth as syn
+    """Time the oracle on a bounded sample of the bench's own call, as GB/s of
+    the same algorithmic attention bytes the GPU figure counts: whole passes
+    of the decode over the agents of one layer (pools quantized beforehand,
+    untimed), repeated to about 10 s of host time; for the chunk workload, a
+    few query rows scaled to all rows.  Also times the oracle's decode (and
+    quantize) of the tiny and the Llama 10-agent workloads on one thread."""
     import oracle
     oracle.lib()
     H, D = w.n_kv_heads, w.head_dim
     layer = layer_ids[0]
-    t_used, bytes_done, agents_done, note = 0.0, 0.0, 0, ""
-    passes = 0
-    inputs = {}                                        # synthetic inputs, drawn once
-    # whole passes over the agents (a pass stops early once 20 s are used),
-    # repeated until about 10 s of CPU time for a stable rate
+    prep = [_cpu_prep(w, layer, a) for a in range(w.n_agents if not w.n_new else 1)]
+    t_used, bytes_done, passes, note = 0.0, 0.0, 0, ""
     while t_used < 10.0:
         passes += 1
-        t_used, bytes_done, agents_done, note = _cpu_pass(w, layer, H, D, t_used, bytes_done, inputs)
-        if note or agents_done < w.n_agents:
+        dt, b, note = _cpu_attend_pass(w, layer, H, D, prep)
+        t_used += dt
+        bytes_done += b
+        if note:
             break
-    return {"value": round(bytes_done / t_used / 1e9, 4), "unit": "GB/s",
-            "cores": oracle.max_threads(), "kind": "oracle",
-            "sample": f"{passes} pass(es) of quantize + attend over {agents_done} of {w.n_agents} agents of "
-                      f"layer {layer}: {bytes_done / 1e6:.1f} MB of algorithmic traffic in {t_used:.2f} s{note}"}
+    res = {"value": round(bytes_done / t_used / 1e9, 4), "unit": "GB/s",
+           "cores": oracle.max_threads(), "kind": "oracle",
+           "sample": f"{passes} pass(es) of the attention over {len(prep)} of {w.n_agents} agents of "
+                     f"layer {layer}: {bytes_done / 1e6:.1f} MB of algorithmic attention bytes in "
+                     f"{t_used:.2f} s{note}"}
+    res["single_thread"] = _cpu_single_thread()
+    return res
 
 
-def _cpu_pass(w, layer, H, D, t_used, bytes_done, inputs):
+def _cpu_prep(w, layer, a):
     import kvq_synth as syn
     import oracle
-    agents_done, note = 0, ""
-    for a in range(w.n_agents):
-        if a not in inputs:
-            inputs[a] = (w.kv(a, layer, syn.TAG_K), None if w.rope_dim else w.kv(a, layer, syn.TAG_V))
-        k, v = inputs[a]
-        nb, nw = w.n_blocks[a], w.n_window[a]
-        bits = w.bits(a, layer)
-        off, tot = oracle.packed_offsets(bits, H, D)
-        pool = np.zeros(2 * tot if v is not None else tot, np.uint8)
-        voff = off + np.uint64(tot) if v is not None else None
-        kw = k[64 * nb:64 * nb + nw] if nw else None
-        vw = v[64 * nb:64 * nb + nw] if (nw and v is not None) else None
-        n_t = 1 if v is None else 2
-        blk = sum(oracle.block_bytes(int(b), H, D) for b in bits)
-        t0 = time.perf_counter()
-        oracle.quantize_seq(k, H, D, bits, off, pool)
-        if v is not None:
-            oracle.quantize_seq(v, H, D, bits, voff, pool)
-        tq = time.perf_counter() - t0
-        b_q = n_t * (64 * nb * H * D * 2 + blk)
+    H, D = w.n_kv_heads, w.head_dim
+    k = w.kv(a, layer, syn.TAG_K)
+    v = None if w.rope_dim else w.kv(a, layer, syn.TAG_V)
+    nb, nw = w.n_blocks[a], w.n_window[a]
+    bits = w.bits(a, layer)
+    off, tot = oracle.packed_offsets(bits, H, D)
+    pool = np.zeros(2 * tot if v is not None else tot, np.uint8)
+    voff = off + np.uint64(tot) if v is not None else None
+    oracle.quantize_seq(k, H, D, bits, off, pool)
+    if v is not None:
+        oracle.quantize_seq(v, H, D, bits, voff, pool)
+    kw = k[64 * nb:64 * nb + nw] if nw else None
+    vw = v[64 * nb:64 * nb + nw] if (nw and v is not None) else None
+    rope = w.rope(a, layer) if w.rope_dim else None
+    return dict(a=a, bits=bits, off=off, voff=voff, pool=pool, kw=kw, vw=vw, rope=rope)
+
+
+def _cpu_attend_pass(w, layer, H, D, prep):
+    import oracle
+    dt, b, note = 0.0, 0.0, ""
+    q_all = None if w.n_new else w.q(layer)
+    for pr in prep:
+        a = pr["a"]
         if w.n_new:
             qn, kn, vn = w.chunk_new()
             rows = 4
             t1 = time.perf_counter()
-            oracle.attend_chunk_seq(pool, bits, off, voff, kw, vw, H, D, qn, kn, vn, w.scale,
-                                    w.n_new - rows, w.n_new)
-            ta = (time.perf_counter() - t1) * (w.n_new / rows)
-            _, b_a = algorithmic_bytes(w, _FakeCache(w, [bits]), w.n_q_heads)
-            t_used += tq + ta
-            bytes_done += b_q + b_a
-            agents_done = 1
-            note = (f"; attention timed on the last {rows} of {w.n_new} query rows "
-                    f"and scaled by {w.n_new // rows}")
+            oracle.attend_chunk_seq(pr["pool"], pr["bits"], pr["off"], pr["voff"], pr["kw"], pr["vw"], H, D,
+                                    qn, kn, vn, w.scale, w.n_new - rows, w.n_new)
+            dt += (time.perf_counter() - t1) * (w.n_new / rows)
+            _, b_a = algorithmic_bytes(w, _FakeCache(w, [pr["bits"]]), w.n_q_heads)
+            b += b_a
+            note = (f"; timed on the last {rows} of {w.n_new} query rows and scaled by {w.n_new // rows}")
             break
-        q = w.q(layer)[a]
-        rope = w.rope(a, layer) if w.rope_dim else None
         t1 = time.perf_counter()
-        oracle.attend_decode_seq(pool, bits, off, voff, kw, vw, rope, H, D, q, w.scale)
-        t_used += tq + (time.perf_counter() - t1)
-        b_a = (n_t * blk + n_t * nw * H * D * 2 + w.lengths[a] * H * w.rope_dim * 2 +
-               w.n_q_heads * (D + w.rope_dim) * 2 + w.n_q_heads * D * 4)
-        bytes_done += b_q + b_a
-        agents_done += 1
-        if t_used > 20.0:
-            break
-    return t_used, bytes_done, agents_done, note
+        oracle.attend_decode_seq(pr["pool"], pr["bits"], pr["off"], pr["voff"], pr["kw"], pr["vw"], pr["rope"],
+                                 H, D, q_all[a], w.scale)
+        dt += time.perf_counter() - t1
+        n_t = 1 if w.rope_dim else 2
+        blk = sum(oracle.block_bytes(int(x), H, D) for x in pr["bits"])
+        b += (n_t * blk + n_t * w.n_window[a] * H * D * 2 + w.lengths[a] * H * w.rope_dim * 2 +
+              w.n_q_heads * (D + w.rope_dim) * 2 + w.n_q_heads * D * 4)
+    return dt, b, note
+
+
+def _cpu_single_thread():
+    """The oracle on one thread: decode GB/s of the tiny and the Llama
+    10-agent workloads (one pass over their agents), and quantize GB/s of
+    the tiny one."""
+    import ctypes
+    import kvq_synth as syn
+    import oracle
+    try:
+        gomp = ctypes.CDLL("libgomp.so.1")
+    except OSError:
+        return None
+    n0 = oracle.max_threads()
+    gomp.omp_set_num_threads(1)
+    out = {"cores": 1}
+    try:
+        for wid in (0, 1):
+            w = syn.workload(wid)
+            H, D = w.n_kv_heads, w.head_dim
+            prep = [_cpu_prep(w, 0, a) for a in range(w.n_agents)]
+            dt, b, _ = _cpu_attend_pass(w, 0, H, D, prep)
+            out[f"{w.name}_decode_GBps"] = round(b / dt / 1e9, 4)
+            out[f"{w.name}_decode_s"] = round(dt, 4)
+            if wid == 0:
+                k = w.kv(0, 0, syn.TAG_K)
+                bits = w.bits(0, 0)
+                off, tot = oracle.packed_offsets(bits, H, D)
+                pool = np.zeros(tot, np.uint8)
+                reps, t0 = 0, time.perf_counter()
+                while time.perf_counter() - t0 < 1.0:
+                    oracle.quantize_seq(k, H, D, bits, off, pool)
+                    reps += 1
+                dq = (time.perf_counter() - t0) / reps
+                blk = sum(oracle.block_bytes(int(x), H, D) for x in bits)
+                out[f"{w.name}_quantize_GBps"] = round((k.size * 2 + blk) / dq / 1e9, 4)
+    finally:
+        gomp.omp_set_num_threads(n0)
+    return out
 
 
 class _FakeCache:
@@ -614,31 +653,24 @@ def main():
     w = syn.workload(args.workload)
     H, D, A, Hq = w.n_kv_heads, w.head_dim, w.n_agents, w.n_q_heads
     layers = w.layers if args.workload == 2 else [0]
+    L = len(layers)
     latent = w.rope_dim > 0
+    bits_per_layer = [[w.bits(a, layer) for a in range(A)] for layer in layers]
+    per_layer = [algorithmic_bytes(w, _FakeCache(w, bits), Hq) for bits in bits_per_layer]
+    q_bytes = sum(qb for qb, _ in per_layer)         # quantize: bf16 read + codes/meta written, all layers
+    a_bytes = sum(ab for _, ab in per_layer)         # attention: all layers
 
-    # Cache copies per layer, rotated across steps.
-    caches_per_layer = []
-    for li, layer in enumerate(layers):
-        bits = [w.bits(a, layer) for a in range(A)]
-        caches_per_layer.append(bits)
-    q_bytes, a_bytes = 0, 0
-    per_layer_bytes = []
-    for bits in caches_per_layer:
-        fake = _FakeCache(w, bits)
-        qb, ab = algorithmic_bytes(w, fake, Hq)
-        per_layer_bytes.append((qb, ab))
-        q_bytes += qb
-        a_bytes += ab
-    footprint_one = a_bytes + q_bytes                 # bytes touched per step
-    R = max(2, int(np.ceil(2 * MALL_BYTES / max(footprint_one, 1))) + 1)
-    R = min(R, 12)
-    sets = []
-    for r in range(R):
-        cs = [kvq.LayerCache(H, D, w.n_blocks, w.n_window, bits, latent=latent, rope_dim=w.rope_dim)
-              for bits in caches_per_layer]
-        sets.append(cs)
-    n_src = 3 if len(layers) == 1 else 1            # >= 2 x 256 MB between reads of one source
-    srcs = [[gpu_inputs(w, torch, 1000 * r + li) for li in range(len(layers))] for r in range(n_src)]
+    # Cache copies: one pass over all copies of all layers reads at least
+    # 2 x 256 MB of distinct attention bytes, so no call finds its cache in
+    # the Infinity Cache (the Gemma workload's 8 layers already pass 1 GB).
+    C = max(1, int(np.ceil(2 * MALL_BYTES / max(a_bytes, 1))) + (0 if a_bytes >= 2 * MALL_BYTES else 1))
+    sets = [[kvq.LayerCache(H, D, w.n_blocks, w.n_window, bits, latent=latent, rope_dim=w.rope_dim)
+             for bits in bits_per_layer] for _ in range(C)]
+    # Quantize sources: enough copies that 2 x 256 MB of other sources pass
+    # between two reads of one (the bf16 rows of all layers count).
+    src_bytes = sum(2 * (1 if latent else 2) * sum(64 * n for n in w.n_blocks) * H * D for _ in layers)
+    n_src = max(1, int(np.ceil(2 * MALL_BYTES / max(src_bytes, 1))) + (0 if src_bytes >= 2 * MALL_BYTES else 1))
+    srcs = [[gpu_inputs(w, torch, 1000 * r + li) for li in range(L)] for r in range(n_src)]
     gq = torch.Generator(device="cuda")
     gq.manual_seed(7)
     if w.n_new:
@@ -651,16 +683,17 @@ def main():
         qs = [torch.randn((A, Hq, D + w.rope_dim), generator=gq, device="cuda").to(torch.bfloat16)
               for _ in layers]
         out = torch.empty((A, Hq, D), dtype=torch.float32, device="cuda")
-        ws = torch.zeros(max(sets[0][0].decode_workspace_bytes(Hq), 256), dtype=torch.uint8,
-                         device="cuda")
-    # Windows and rope are bf16 storage: filled once per copy with N(0,1).
-    for cs in sets:
-        for c in cs:
+        ws = torch.empty(max(sets[0][0].decode_workspace_bytes(Hq), 256), dtype=torch.uint8, device="cuda")
+    # Every copy is quantized once from the sources; windows and rope are
+    # bf16 storage, filled with N(0,1).
+    for r, cs in enumerate(sets):
+        for li, c in enumerate(cs):
+            k, v = srcs[r % n_src][li]
+            c.quantize_kv(k, v)
             for t in (c.k_window, c.v_window, c.rope):
                 if t is not None:
                     t.normal_(generator=gq)
     torch.cuda.synchronize()
-
     stream = torch.cuda.current_stream()
 
     def attend(c, li):
@@ -670,18 +703,17 @@ def main():
             c.attend_decode(qs[li], w.scale, out=out, workspace=ws)
 
     def step(i):
-        cs_w = sets[i % R]
-        cs_r = sets[(i + R // 2) % R]
-        src = srcs[i % n_src]
-        for li in range(len(layers)):
-            k, v = src[li]
-            cs_w[li].quantize_kv(k, v)                # K and V in one launch
-            attend(cs_r[li], li)
+        # one batched decode step: every layer's attention call over the
+        # agents' packed caches (copy i mod C)
+        cs = sets[i % C]
+        for li in range(L):
+            attend(cs[li], li)
 
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
-    # The timed steps carry no events inside.
+    # The timed steps carry no events inside: the call duration is the
+    # timed region divided by its calls.
     t_start = torch.cuda.Event(enable_timing=True)
     t_end = torch.cuda.Event(enable_timing=True)
     t_start.record(stream)
@@ -689,81 +721,69 @@ def main():
         step(args.warmup + i)
     t_end.record(stream)
     torch.cuda.synchronize()
-    total_ms = t_start.elapsed_time(t_end)
-    ms_step = total_ms / args.steps
-    n_launch_q = 1                                    # one kvq_quantize_kv launch per layer
-    # Per-call durations of the two phases: ROOF_LAUNCHES quantize launches,
-    # then ROOF_LAUNCHES attention calls, each back to back (rotating caches
-    # and sources) between one pair of events on the launch stream, so the
-    # events' own overhead is spread over the run; each launch still pays
-    # its dispatch gap.  The median of five such runs is reported.
-    ROOF_LAUNCHES = 16
+    ms_step = t_start.elapsed_time(t_end) / args.steps
+    attn_ms = ms_step / L                             # one attention call (split + merge launches)
+    value = a_bytes / (ms_step * 1e-3) / 1e9
 
-    def timed(fn, reps=5):
-        # median over reps runs of ROOF_LAUNCHES calls: one run is short
-        # (well under a millisecond) and a single sample can be an outlier
-        per = []
-        for _ in range(reps):
-            e_a, e_b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            e_a.record(stream)
-            for i in range(ROOF_LAUNCHES):
-                fn(i)
-            e_b.record(stream)
-            torch.cuda.synchronize()
-            per.append(e_a.elapsed_time(e_b) / ROOF_LAUNCHES)
-        return float(np.median(per))
+    # Quantize (building the caches): every layer's K and V in one launch
+    # per layer, rotating sources and destination copies, timed the same way.
+    QREPS = max(2 * L, 8)
 
-    def quant_one(i):
-        li = i % len(layers)                          # every layer's widths
-        kv = srcs[i % n_src][li]
-        sets[i % R][li].quantize_kv(kv[0], kv[1])
+    def quant(i):
+        li = i % L
+        k, v = srcs[(i // L) % n_src][li]
+        sets[(i // L) % C][li].quantize_kv(k, v)
 
-    quant_launch_ms = timed(quant_one)
-    attn_ms = timed(lambda i: attend(sets[(i + R // 2) % R][i % len(layers)], i % len(layers)))
-    step_bytes = q_bytes + a_bytes
-    value = step_bytes / (ms_step * 1e-3) / 1e9
-    quant_gbs = (q_bytes / len(layers) / n_launch_q) / (quant_launch_ms * 1e-3) / 1e9
-    attn_gbs = (a_bytes / len(layers)) / (attn_ms * 1e-3) / 1e9
+    for i in range(L):
+        quant(i)
+    torch.cuda.synchronize()
+    e_a, e_b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e_a.record(stream)
+    for i in range(QREPS):
+        quant(i)
+    e_b.record(stream)
+    torch.cuda.synchronize()
+    quant_launch_ms = e_a.elapsed_time(e_b) / QREPS
+    quant_gbs = (q_bytes / L) / (quant_launch_ms * 1e-3) / 1e9
+    attn_gbs = (a_bytes / L) / (attn_ms * 1e-3) / 1e9
     res = {
         "metric": METRIC, "value": round(value, 2), "unit": "GB/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 5),
-        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "fp16 mfma, fp32 acc",
         "data": "synthetic",
-        "config": {"workload": w.name, "agents": A, "layers": len(layers), "q_heads": Hq,
+        "config": {"workload": w.name, "agents": A, "layers": L, "q_heads": Hq,
                    "kv_heads": H, "head_dim": D, "cache_tokens": w.lengths if A <= 10 else None,
                    "bits": "2/3/4/8 mixed, mean 3" if args.workload == 2 else 4, "group": 64,
                    "rope_dim": w.rope_dim, "new_tokens": w.n_new,
-                   "rotated_copies": R},
+                   "step": ("one batched decode step: the attention call of every layer"
+                            if not w.n_new else "one chunk attention call"),
+                   "rotated_cache_copies": C, "rotated_sources": n_src},
+        "attn_bytes_per_step": int(a_bytes),
+        "attn_us_per_call": round(attn_ms * 1e3, 3),
         "quantize_GBps": round(quant_gbs, 2),
         "quantize_us_per_launch": round(quant_launch_ms * 1e3, 3),
-        "attn_us": round(attn_ms * 1e3, 3),
-        "attn_effective_GBps": round(attn_gbs, 2),
+        "quantize_bytes_per_launch": int(q_bytes / L),
     }
     if w.n_new:
         fl = chunk_flops(w)
-        res["chunk_TFLOPs"] = round(fl / (attn_ms * 1e-3) / 1e12, 2)
+        tfl = fl / (attn_ms * 1e-3) / 1e12
+        res["chunk_TFLOPs"] = round(tfl, 2)
         res["prefill_tokens_per_s"] = round(w.n_new / (attn_ms * 1e-3), 1)
-    else:
-        res["decode_tokens_per_s"] = round(A / (attn_ms * len(layers) * 1e-3), 1)
-    # Roofline of the dominant kernel.
-    if n_launch_q * quant_launch_ms >= attn_ms:
-        per_launch = (q_bytes / len(layers)) / n_launch_q
-        ach = per_launch / (quant_launch_ms * 1e-3) / 1e9
-        tr = traffic_bytes(args.workload, "kvq quantize")
-        res["roofline"] = {"kernel": "kvq quantize", "bound": "hbm", "achieved": round(ach, 2),
-                           "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBS, 4),
-                           "traffic": None if tr is None else round(tr)}
-    elif w.n_new:
-        fl = chunk_flops(w) / (attn_ms * 1e-3) / 1e12
-        res["roofline"] = {"kernel": "kvq attend_chunk", "bound": "mfma", "achieved": round(fl, 2),
+        res["roofline"] = {"kernel": "kvq attend_chunk", "bound": "mfma", "achieved": round(tfl, 2),
                            "peak": MFMA_F16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                           "frac": round(fl / MFMA_F16_PEAK_TFLOPS, 4),
+                           "frac": round(tfl / MFMA_F16_PEAK_TFLOPS, 4),
                            "traffic": traffic_bytes(args.workload, "kvq attend_chunk")}
     else:
+        res["decode_tokens_per_s"] = round(A / (ms_step * 1e-3), 1)
         res["roofline"] = {"kernel": "kvq attend_decode", "bound": "hbm",
                            "achieved": round(attn_gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                            "frac": round(attn_gbs / HBM_PEAK_GBS, 4),
                            "traffic": traffic_bytes(args.workload, "kvq attend_decode")}
+    tr = traffic_bytes(args.workload, "kvq quantize")
+    res["roofline_quantize"] = {"kernel": "kvq quantize", "bound": "hbm", "achieved": round(quant_gbs, 2),
+                                "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(quant_gbs / HBM_PEAK_GBS, 4),
+                                "traffic": None if tr is None else round(tr)}
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(w, layers)
     print(json.dumps(res), flush=True)

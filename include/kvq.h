@@ -231,14 +231,7 @@ int kvq_allocate_widths(const float *S, int64_t n, int32_t n_heads, int32_t head
                         uint64_t budget_bytes, uint8_t *widths);
 
 /* Workspace bytes kvq_attend_decode needs for this layout and head count
- * (written to *bytes).  The workspace starts with round256(4*n_seqs*n_heads)
- * bytes of merge tickets (uint32 per sequence and KV head), then split
- * partials.  The ticket bytes must be zero before the first call on a
- * workspace (zero-fill it once after allocating it); every call leaves them
- * zero again, so a workspace is zeroed once, not per call.  Anything else
- * that writes those bytes (another kind of call sharing the buffer, a call
- * for a layout with more sequences or heads) requires zeroing them again.
- * Errors: KVQ_EINVAL, KVQ_EUNSUPPORTED. */
+ * (written to *bytes).  Errors: KVQ_EINVAL, KVQ_EUNSUPPORTED. */
 int kvq_decode_workspace(const kvq_layout *L, int32_t n_q_heads, int32_t rope_dim, size_t *bytes);
 
 /* Batched decode attention over quantized caches (AgentMem: batched
@@ -261,9 +254,8 @@ int kvq_decode_workspace(const kvq_layout *L, int32_t n_q_heads, int32_t rope_di
  *        per token position (token t of sequence a, blocks then window, at
  *        row t).
  *   n_q_heads: a multiple of H with n_q_heads/H <= 16.
- *   workspace: >= kvq_decode_workspace bytes, 256-byte aligned, its ticket
- *        bytes zero (see kvq_decode_workspace).  Calls that share a workspace
- *        must not overlap in time.
+ *   workspace: >= kvq_decode_workspace bytes, 256-byte aligned; calls that
+ *        share a workspace must not overlap in time.
  * Errors: KVQ_EINVAL (also softmax_scale <= 0), KVQ_ENOSPC, KVQ_EUNSUPPORTED,
  *         KVQ_EHIP. */
 int kvq_attend_decode(const kvq_layout *L, const kvq_store *K, const kvq_store *V,
@@ -271,11 +263,7 @@ int kvq_attend_decode(const kvq_layout *L, const kvq_store *K, const kvq_store *
                       int32_t n_q_heads, float softmax_scale, float *out,
                       void *workspace, size_t workspace_bytes, void *stream);
 
-/* Workspace bytes kvq_attend_decode_topk needs (written to *bytes).  It
- * begins with the workspace of the decode over the kept blocks, tickets
- * first, so it must be zero-filled once as for kvq_attend_decode; a buffer
- * sized for both may serve kvq_attend_decode and kvq_attend_decode_topk of
- * the same layout alternately.
+/* Workspace bytes kvq_attend_decode_topk needs (written to *bytes).
  * Errors: KVQ_EINVAL, KVQ_EUNSUPPORTED. */
 int kvq_topk_workspace(const kvq_layout *L, int32_t n_q_heads, int32_t rope_dim, int32_t top_k,
                        size_t *bytes);
@@ -297,8 +285,8 @@ int kvq_topk_workspace(const kvq_layout *L, int32_t n_q_heads, int32_t rope_dim,
  *             ascending order, -1 past min(top_k, n_blocks[a]).
  *   top_k >= 1; max_blocks <= 16384 (0 allowed: a window-only layout keeps
  *   no block and `selected` is all -1); (n_q_heads/H) * (head_dim + rope_dim)
- *   <= 9216.  Other arguments (softmax_scale > 0, the zeroed workspace) as
- *   for kvq_attend_decode.
+ *   <= 9216.  Other arguments (softmax_scale > 0) as for
+ *   kvq_attend_decode.
  * Errors: KVQ_EINVAL, KVQ_ENOSPC, KVQ_EUNSUPPORTED, KVQ_EHIP. */
 int kvq_attend_decode_topk(const kvq_layout *L, const kvq_store *K, const kvq_store *V,
                            const uint16_t *rope, int32_t rope_dim, const uint16_t *q,

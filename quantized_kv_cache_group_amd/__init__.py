@@ -385,8 +385,7 @@ class LayerCache:
         if out is None:
             out = torch.empty((self.A, Hq, self.D), dtype=torch.float32, device=q.device)
         if workspace is None:
-            # zero-filled: the decode's merge tickets must start at zero (calls leave them zero)
-            workspace = torch.zeros(max(self.decode_workspace_bytes(Hq), 256), dtype=torch.uint8,
+            workspace = torch.empty(max(self.decode_workspace_bytes(Hq), 256), dtype=torch.uint8,
                                     device=q.device)
         kst = self.store("k")
         vst = self.store("v")
@@ -414,7 +413,7 @@ class LayerCache:
         if out is None:
             out = torch.empty((self.A, Hq, self.D), dtype=torch.float32, device=q.device)
         if workspace is None:
-            workspace = torch.zeros(max(self.topk_workspace_bytes(Hq, top_k), 256), dtype=torch.uint8,
+            workspace = torch.empty(max(self.topk_workspace_bytes(Hq, top_k), 256), dtype=torch.uint8,
                                     device=q.device)
         if selected is not None:
             assert selected.dtype == torch.int32 and selected.is_contiguous()

@@ -1,6 +1,5 @@
 // Batched split-K decode for grouped-query attention with at most 4 query
-// heads per KV head (gfx950, 4x4x4 matrix-core blocks), with the split merge
-// done by the last workgroup of each (sequence, KV head) to finish.
+// heads per KV head (gfx950, 4x4x4 matrix-core blocks).
 //
 // What it computes (Agent Memory Below the Prompt, arXiv 2603.04428,
 // Abstract: batched inference over several agents' quantized caches restored
@@ -9,14 +8,15 @@
 // attention of q[a][h] over the 64*n_blocks[a] quantized tokens and the
 // n_window[a] bf16 tokens of KV head h / G.
 //
-// Work decomposition: one workgroup per (key split, KV head, sequence) with
-// one wave per 64-dim group of head_dim (a group is the quantizer's unit, so
-// a wave needs one scale/bias per token).  A split is SB 64-token blocks or
-// the bf16 window.  For each block, wave w loads its group of every token's K
-// and V row together (lane = token), forms partial scores of the group, and
-// the waves add their partials through LDS in a fixed order, so every wave
-// holds the same full scores and runs the same online softmax; each wave then
-// accumulates the output dims of its own group.
+// Work decomposition: one workgroup per (key split, KV head, sequence); a
+// split is SB 64-token blocks or the bf16 window.  Each wave of the workgroup
+// owns GW consecutive 64-dim groups of head_dim (a group is the quantizer's
+// unit: one scale/bias per token).  For each block a wave loads its groups of
+// every token's K and V rows together (lane = token), so a wave keeps 8*GW*b
+// bytes per lane of both tensors in flight; when a head spans several waves
+// they add their partial scores through LDS in a fixed order, so every wave
+// holds the same full scores and runs the same online softmax, and each wave
+// accumulates the output dims of its own groups.
 //
 // Matrix products on the codes themselves.  v_mfma_f32_4x4x4_16b_f16 runs 16
 // independent 4x4x4 products, so lane l of a wave is token l of a block:
@@ -43,11 +43,8 @@
 // s), and the correction sums the same rounded p'' the products used.  The
 // softmax runs in fp32 (exp2) with an exact running max, so p <= 1.
 //
-// Split merge: each workgroup writes (max, sum, unnormalised output) of its
-// rows, then takes a ticket from a per-(sequence, KV head) counter in the
-// workspace (atomicInc wraps it back to zero); the workgroup that takes the
-// last ticket merges every split of its rows.  The counters must be zero
-// before the first call on a workspace, and each call leaves them zero.
+// Each split writes (max, sum, unnormalised output) of its rows; the decode
+// merge kernel combines the splits.
 #include "kvq_internal.h"
 #include "unpack.h"
 
@@ -157,12 +154,13 @@ struct GroupRow {
     }
 };
 
+template <int GW>
 struct State {
-    f4 o;                                     // lane (b, j): sum p''(1024+m c) for head i, group pos 4b+j
+    f4 o[GW];                                 // lane (b, j): sum p''(1024+m c) for head i, position 4b+j of group u
     float m_run;                              // running max (log2 domain) of head j
     float l_lane;                             // this lane's share of head j's running sum
-    float ps_lane;                            // this lane's share of head j's sum of p'' (coded tokens)
-    float pb_lane;                            // this lane's share of head j's sum of p*bias
+    float ps_lane[GW];                        // this lane's share of head j's sum of p'' (coded tokens), per group
+    float pb_lane[GW];                        // this lane's share of head j's sum of p*bias, per group
 };
 
 // Token 4b+r's 32-bit value broadcast to the four lanes of quad b.
@@ -197,7 +195,8 @@ __device__ __forceinline__ f4 group_dot(const h4 (*qs)[4], KF kx)
 // Online softmax on the scores of one 64-token round (lane (b, j): tokens
 // 4b..4b+3 of head j).  Rescales the state and returns the probabilities in
 // fp32 (p <= 1).
-__device__ __forceinline__ f4 softmax_round(State &st, f4 s, int n_valid, float c)
+template <int GW>
+__device__ __forceinline__ f4 softmax_round(State<GW> &st, f4 s, int n_valid, float c)
 {
     const int lane = threadIdx.x & 63, b = lane >> 2;
     float sc[4];
@@ -210,14 +209,20 @@ __device__ __forceinline__ f4 softmax_round(State &st, f4 s, int n_valid, float 
     const float alpha = __builtin_amdgcn_exp2f(st.m_run - m_new);
     st.m_run = m_new;
     st.l_lane *= alpha;
-    st.ps_lane *= alpha;
-    st.pb_lane *= alpha;
+#pragma unroll
+    for (int u = 0; u < GW; u++) {
+        st.ps_lane[u] *= alpha;
+        st.pb_lane[u] *= alpha;
+    }
     // alpha of each head, for the output rows this lane holds
     if (__any(alpha != 1.0f)) {
         const int base = lane & ~3;
         const float a0 = __shfl(alpha, base), a1 = __shfl(alpha, base + 1);
         const float a2 = __shfl(alpha, base + 2), a3 = __shfl(alpha, base + 3);
-        st.o[0] *= a0; st.o[1] *= a1; st.o[2] *= a2; st.o[3] *= a3;
+#pragma unroll
+        for (int u = 0; u < GW; u++) {
+            st.o[u][0] *= a0; st.o[u][1] *= a1; st.o[u][2] *= a2; st.o[u][3] *= a3;
+        }
     }
     return f4{__builtin_amdgcn_exp2f(sc[0] - m_new), __builtin_amdgcn_exp2f(sc[1] - m_new),
               __builtin_amdgcn_exp2f(sc[2] - m_new), __builtin_amdgcn_exp2f(sc[3] - m_new)};
@@ -232,13 +237,13 @@ __device__ __forceinline__ void wave_sync()
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-// O += P.X for the wave's 64-dim group: each lane writes its token's values
-// to LDS (chunk order: position k of a chunk holds dim (k>>1) + 4(k&1)), then
-// 16 slices of 4 tokens whose B operand comes from ds_read_b64_tr_b16 (lane l
+// O += P.X for one 64-dim group: each lane writes its token's values to LDS
+// (chunk order: position k of a chunk holds dim (k>>1) + 4(k&1)), then 16
+// slices of 4 tokens whose B operand comes from ds_read_b64_tr_b16 (lane l
 // gets position l of four consecutive tokens); lane l accumulates group
 // position l.  vx(c) yields chunk c of the lane's row.
 template <typename VF>
-__device__ __forceinline__ void pv_round(State &st, h4 a, _Float16 *vr, VF vx)
+__device__ __forceinline__ f4 pv_round(f4 o, h4 a, _Float16 *vr, VF vx)
 {
     const int lane = threadIdx.x & 63;
     // lane i of each 16-lane group addresses token 4S + i/4, positions
@@ -254,7 +259,7 @@ __device__ __forceinline__ void pv_round(State &st, h4 a, _Float16 *vr, VF vx)
             h8{pr.p[0][0], pr.p[0][1], pr.p[1][0], pr.p[1][1], pr.p[2][0], pr.p[2][1], pr.p[3][0], pr.p[3][1]};
     }
     wave_sync();
-    f4 acc0 = st.o, acc1 = {0.f, 0.f, 0.f, 0.f};
+    f4 acc0 = o, acc1 = {0.f, 0.f, 0.f, 0.f};
 #define KVQ_PV(ACC, S)                                                                                \
     ACC = __builtin_amdgcn_mfma_f32_4x4x4f16(                                                         \
         a,                                                                                            \
@@ -266,8 +271,8 @@ __device__ __forceinline__ void pv_round(State &st, h4 a, _Float16 *vr, VF vx)
     KVQ_PV(acc0, 8); KVQ_PV(acc1, 9); KVQ_PV(acc0, 10); KVQ_PV(acc1, 11);
     KVQ_PV(acc0, 12); KVQ_PV(acc1, 13); KVQ_PV(acc0, 14); KVQ_PV(acc1, 15);
 #undef KVQ_PV
-    st.o = acc0 + acc1;
     wave_sync();
+    return acc0 + acc1;
 }
 
 // Widths and pool offsets of up to 64 consecutive blocks, one per lane, so
@@ -302,7 +307,7 @@ __device__ __forceinline__ f2 meta_of(uint32_t packed)
     return f2{(float)sb[0], (float)sb[1]};
 }
 
-// Partial scores of the wave's group for tokens 4b..4b+3 of head j:
+// Partial scores of one group for tokens 4b..4b+3 of head j:
 // (s/m)(T - 1024 Q) + b Q with token 4b+r's (s, b) from km.
 template <int B>
 __device__ __forceinline__ f4 group_scores(const h4 (*qs)[4], float qg, const uint32_t *kw, uint32_t km)
@@ -320,12 +325,12 @@ __device__ __forceinline__ f4 group_scores(const h4 (*qs)[4], float qg, const ui
 }
 
 // Full scores from the waves' partials: each wave stores its partial in
-// LDS, the workgroup meets at a barrier, and every wave adds the NG
+// LDS, the workgroup meets at a barrier, and every wave adds the NW
 // partials in the same order (so all waves hold identical scores).
-template <int NG>
+template <int NW>
 __device__ __forceinline__ f4 exchange(f4 part, f4 (*xs)[64], int w)
 {
-    if constexpr (NG == 1) {
+    if constexpr (NW == 1) {
         return part;
     } else {
         const int lane = threadIdx.x & 63;
@@ -333,76 +338,91 @@ __device__ __forceinline__ f4 exchange(f4 part, f4 (*xs)[64], int w)
         __syncthreads();
         f4 s = xs[0][lane];
 #pragma unroll
-        for (int u = 1; u < NG; u++) s += xs[u][lane];
+        for (int u = 1; u < NW; u++) s += xs[u][lane];
         return s;
     }
 }
 
-// One 64-token block: K and V group rows of every token issued together,
-// the Q.K products and the exchange, the softmax, then P.V.
-template <int B, int NG>
-__device__ __forceinline__ void round_block(State &st, const h4 (*qs)[4], float qg, const uint8_t *kblk,
+// One 64-token block: the K rows of the wave's GW groups for every token,
+// the Q.K products and the exchange, then the V rows, the softmax and P.V
+// per group.
+template <int B, int NG, int GW>
+__device__ __forceinline__ void round_block(State<GW> &st, const h4 (*qs)[4], const float *qg, const uint8_t *kblk,
                                             const uint8_t *vblk, int H, int g, int w, float c, _Float16 *vr,
                                             f4 (*xs)[64])
 {
+    constexpr int NW = NG / GW, ND = GroupRow<B>::NDW;
     constexpr uint32_t ROW = 8 * NG * B;                  // bytes of a full token row
     const uint32_t tok = (uint32_t)g * 64 + (threadIdx.x & 63);
-    const uint32_t roff = tok * ROW + 8 * B * w;
-    const uint32_t moff = (uint32_t)H * 64 * ROW + 4 * (NG * tok + w);
-    uint32_t kw[GroupRow<B>::NDW], vw[GroupRow<B>::NDW];
-    GroupRow<B>::load(kw, kblk + roff);
-    const uint32_t km = *reinterpret_cast<const uint32_t *>(kblk + moff);
-    GroupRow<B>::load(vw, vblk + roff);
-    const uint32_t vm = *reinterpret_cast<const uint32_t *>(vblk + moff);
-
-    const f4 s = exchange<NG>(group_scores<B>(qs, qg, kw, km), xs, w);
-    const f4 p = softmax_round(st, s, 64, c);
-    // p'' = fp16(p s 64/m) per token (the V scale of token 4b+r from its quad)
-    f4 pv, pbv;
+    const uint32_t roff = tok * ROW + 8 * B * GW * w;
+    const uint32_t moff = (uint32_t)H * 64 * ROW + 4 * (NG * tok + GW * w);
+    uint32_t kw[GW * ND], vw[GW * ND], km[GW], vm[GW];
 #pragma unroll
-    for (int r = 0; r < 4; r++) {
-        const f2 vsb = meta_of(quad_bcast(vm, r));
-        pv[r] = p[r] * (vsb[0] * (FV / CodeMul<B>::M));
-        pbv[r] = p[r] * vsb[1];
-    }
-    const h4 pa = __builtin_convertvector(pv, h4);
+    for (int u = 0; u < GW; u++) GroupRow<B>::load(kw + ND * u, kblk + roff + 8 * B * u);
+#pragma unroll
+    for (int u = 0; u < GW; u++) km[u] = reinterpret_cast<const uint32_t *>(kblk + moff)[u];
+
+    f4 part = group_scores<B>(qs, qg[0], kw, km[0]);
+#pragma unroll
+    for (int u = 1; u < GW; u++) part += group_scores<B>(qs + 16 * u, qg[u], kw + ND * u, km[u]);
+    // the V rows are fetched once the K rows' registers are free (measured
+    // faster than issuing them with the K rows: fewer live registers)
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int u = 0; u < GW; u++) GroupRow<B>::load(vw + ND * u, vblk + roff + 8 * B * u);
+#pragma unroll
+    for (int u = 0; u < GW; u++) vm[u] = reinterpret_cast<const uint32_t *>(vblk + moff)[u];
+    const f4 s = exchange<NW>(part, xs, w);
+    const f4 p = softmax_round<GW>(st, s, 64, c);
     st.l_lane += (p[0] + p[1]) + (p[2] + p[3]);
-    st.ps_lane += ((float)pa[0] + (float)pa[1]) + ((float)pa[2] + (float)pa[3]);
-    st.pb_lane += (pbv[0] + pbv[1]) + (pbv[2] + pbv[3]);
     const uint32_t mv = opaque_magic();
-    pv_round(st, pa, vr, [&](int cidx) { return GroupRow<B>::chunk(vw, cidx, mv); });
+#pragma unroll
+    for (int u = 0; u < GW; u++) {
+        // p'' = fp16(p s 64/m) per token (the V scale of token 4b+r from its quad)
+        f4 pv, pbv;
+#pragma unroll
+        for (int r = 0; r < 4; r++) {
+            const f2 vsb = meta_of(quad_bcast(vm[u], r));
+            pv[r] = p[r] * (vsb[0] * (FV / CodeMul<B>::M));
+            pbv[r] = p[r] * vsb[1];
+        }
+        const h4 pa = __builtin_convertvector(pv, h4);
+        st.ps_lane[u] += ((float)pa[0] + (float)pa[1]) + ((float)pa[2] + (float)pa[3]);
+        st.pb_lane[u] += (pbv[0] + pbv[1]) + (pbv[2] + pbv[3]);
+        st.o[u] = pv_round(st.o[u], pa, vr, [&](int cidx) { return GroupRow<B>::chunk(vw + ND * u, cidx, mv); });
+    }
 }
 
 // 64 window tokens w0 .. w0+63 (rows past nw read row nw-1 and are masked):
 // bf16 values straight into the products, probabilities rounded to fp16.
-template <int NG>
-__device__ __forceinline__ void round_window(State &st, const h4 (*qs)[4], const uint16_t *kwin,
+template <int NG, int GW>
+__device__ __forceinline__ void round_window(State<GW> &st, const h4 (*qs)[4], const uint16_t *kwin,
                                              const uint16_t *vwin, int H, int g, int w, int w0, int nw, float c,
                                              _Float16 *vr, f4 (*xs)[64])
 {
-    constexpr int D = 64 * NG;
+    constexpr int D = 64 * NG, NW = NG / GW;
     const int t = min(w0 + (int)(threadIdx.x & 63), nw - 1);
-    const uint4 *kr = reinterpret_cast<const uint4 *>(kwin + ((size_t)t * H + g) * D + 64 * w);
-    const uint4 *vrow = reinterpret_cast<const uint4 *>(vwin + ((size_t)t * H + g) * D + 64 * w);
-    uint4 kx[8], vx[8];
+    const uint4 *kr = reinterpret_cast<const uint4 *>(kwin + ((size_t)t * H + g) * D + 64 * GW * w);
+    const uint4 *vrow = reinterpret_cast<const uint4 *>(vwin + ((size_t)t * H + g) * D + 64 * GW * w);
+    f4 part = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int i = 0; i < 8; i++) kx[i] = kr[i];
-#pragma unroll
-    for (int i = 0; i < 8; i++) vx[i] = vrow[i];
-    const f4 part = group_dot(qs, [&](int cidx) { return bf16_pairs(kx[cidx]); });
-    const f4 s = exchange<NG>(part, xs, w);
-    const f4 p = softmax_round(st, s, nw - w0, c);
+    for (int u = 0; u < GW; u++)
+        part += group_dot(qs + 16 * u, [&](int cidx) { return bf16_pairs(kr[8 * u + cidx]); });
+    const f4 s = exchange<NW>(part, xs, w);
+    const f4 p = softmax_round<GW>(st, s, nw - w0, c);
     const h4 pa = __builtin_convertvector(p, h4);
     // the running sum adds the rounded probabilities the products use
     st.l_lane += ((float)pa[0] + (float)pa[1]) + ((float)pa[2] + (float)pa[3]);
-    pv_round(st, pa, vr, [&](int cidx) { return bf16_pairs(vx[cidx]); });
+#pragma unroll
+    for (int u = 0; u < GW; u++)
+        st.o[u] = pv_round(st.o[u], pa, vr, [&](int cidx) { return bf16_pairs(vrow[8 * u + cidx]); });
 }
 
-// Query rows of KV head g's G heads for dims [64w, 64w+64), fp16, in the
-// unpack order of the key chunks, into qs; and Q of head j: the sum of its
-// fp16 query over the group (lane (b, j) adds slice b, then the 16 lanes of
-// head j combine).
-__device__ __forceinline__ float stage_query(const DecodeArgs &p, int a, int g, int w, h4 (*qs)[4])
+// Query rows of KV head g's G heads for the 64 dims [64gr, 64gr+64), fp16,
+// in the unpack order of the key chunks, into qs; returns Q of head j: the
+// sum of its fp16 query over the group (lane (b, j) adds slice b, then the 16
+// lanes of head j combine).
+__device__ __forceinline__ float stage_query(const DecodeArgs &p, int a, int g, int gr, h4 (*qs)[4])
 {
     const int lane = threadIdx.x & 63, b = lane >> 2, j = lane & 3;
     const int D = p.t.D;
@@ -412,7 +432,7 @@ __device__ __forceinline__ float stage_query(const DecodeArgs &p, int a, int g, 
             Pairs pr;
             if (h < p.G) {
                 const uint4 v = *reinterpret_cast<const uint4 *>(p.q + ((size_t)a * p.Hq + g * p.G + h) * D +
-                                                                 64 * w + 8 * cc);
+                                                                 64 * gr + 8 * cc);
                 pr = bf16_pairs(v);
             } else {
                 pr.p[0] = pr.p[1] = pr.p[2] = pr.p[3] = h2{(_Float16)0.0f, (_Float16)0.0f};
@@ -431,70 +451,21 @@ __device__ __forceinline__ float stage_query(const DecodeArgs &p, int a, int g, 
     return acc;
 }
 
-// Combine the ns splits of rows (a, g*G + i), i < G, for the dims of the
-// wave's group: o = sum_s 2^(m_s - M) acc_s / sum_s 2^(m_s - M) l_s.
-__device__ void merge_splits(const DecodeArgs &p, int a, int g, int w, int ns)
+// NG groups of head_dim, GW of them per wave.
+template <int NG, int GW>
+__global__ __launch_bounds__(64 * (NG / GW)) void decode_g4_split(DecodeArgs p)
 {
-    const int lane = threadIdx.x & 63;
-    const int D = p.t.D;
-    const size_t stride = (size_t)(D + 2);
-    const int d = 64 * w + lane;
-    for (int i = 0; i < p.G; i++) {
-        const size_t row = (size_t)a * p.Hq + (size_t)g * p.G + i;
-        const float *pr = p.part + row * p.n_splits * stride;
-        float M = -INFINITY;
-        for (int s0 = 0; s0 < ns; s0 += 64)
-            if (s0 + lane < ns) M = fmaxf(M, __builtin_nontemporal_load(pr + (size_t)(s0 + lane) * stride));
-#pragma unroll
-        for (int o = 32; o > 0; o >>= 1) M = fmaxf(M, __shfl_xor(M, o));
-        float L = 0.0f, acc = 0.0f;
-        for (int s0 = 0; s0 < ns; s0 += 64) {
-            const int sl = s0 + lane;
-            float wgt = 0.0f;
-            if (sl < ns) {
-                wgt = __builtin_amdgcn_exp2f(__builtin_nontemporal_load(pr + (size_t)sl * stride) - M);
-                L = __builtin_fmaf(wgt, __builtin_nontemporal_load(pr + (size_t)sl * stride + 1), L);
-            }
-            const int n = min(64, ns - s0);
-            for (int u0 = 0; u0 < n; u0 += 16) {
-                float v[16];
-#pragma unroll
-                for (int u = 0; u < 16; u++)
-                    v[u] = (u0 + u < n) ? __builtin_nontemporal_load(pr + (size_t)(s0 + u0 + u) * stride + 2 + d) : 0.0f;
-#pragma unroll
-                for (int u = 0; u < 16; u++)
-                    acc = __builtin_fmaf(__builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, wgt),
-                                                                                            u0 + u)),
-                                         v[u], acc);
-            }
-        }
-#pragma unroll
-        for (int o = 32; o > 0; o >>= 1) L += __shfl_xor(L, o);
-        p.out[row * D + d] = L > 0.0f ? acc * (1.0f / L) : 0.0f;
-    }
-}
-
-template <int NG>
-__global__ __launch_bounds__(64 * NG) void decode_g4_split(DecodeArgs p, uint32_t *tickets)
-{
-    constexpr int D = 64 * NG;
-    __shared__ __attribute__((aligned(16))) h4 qs[NG][16][4];              // [wave][slice][head]
-    __shared__ __attribute__((aligned(16))) _Float16 vt[NG][64 * VS];      // V tile per wave
-    __shared__ __attribute__((aligned(16))) f4 xs[2][NG][64];              // partial scores
-    __shared__ int last;
+    constexpr int D = 64 * NG, NW = NG / GW;
+    __shared__ __attribute__((aligned(16))) h4 qs[NW][16 * GW][4];        // [wave][slice][head]
+    __shared__ __attribute__((aligned(16))) _Float16 vt[NW][64 * VS];      // V tile per wave
+    __shared__ __attribute__((aligned(16))) f4 xs[NW > 1 ? 2 : 1][NW][64]; // partial scores
     const int s = blockIdx.x, g = blockIdx.y, a = blockIdx.z;
     const int lane = threadIdx.x & 63, b = lane >> 2, j = lane & 3;
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int nb = seq_blocks(p.t, a), nw = seq_window(p.t, a);
     const int nsb = (nb + p.SB - 1) / p.SB;
-    const int ns = nsb + (nw > 0 ? 1 : 0);
     const bool win = (s == nsb) && nw > 0;
-    if (s >= ns) {
-        if (s == 0) {                                     // empty sequence: zeros
-            for (int i = 0; i < p.G; i++) p.out[((size_t)a * p.Hq + g * p.G + i) * D + 64 * w + lane] = 0.0f;
-        }
-        return;
-    }
+    if (s > nsb || (s == nsb && !win)) return;
 
     // The split's block table first, so its loads overlap the query loads.
     SplitMeta sm;
@@ -502,16 +473,22 @@ __global__ __launch_bounds__(64 * NG) void decode_g4_split(DecodeArgs p, uint32_
     const int j0 = s * p.SB, j1 = min(j0 + p.SB, nb);
     if (!win) split_meta(sm, p, a, j0, j1, true);
 
-    const float qg = stage_query(p, a, g, w, qs[w]);
+    float qg[GW];
+#pragma unroll
+    for (int u = 0; u < GW; u++) qg[u] = stage_query(p, a, g, GW * w + u, qs[w] + 16 * u);
 
-    State st;
-    st.o = f4{0.f, 0.f, 0.f, 0.f};
+    State<GW> st;
+#pragma unroll
+    for (int u = 0; u < GW; u++) {
+        st.o[u] = f4{0.f, 0.f, 0.f, 0.f};
+        st.ps_lane[u] = st.pb_lane[u] = 0.0f;
+    }
     st.m_run = -INFINITY;
-    st.l_lane = st.ps_lane = st.pb_lane = 0.0f;
+    st.l_lane = 0.0f;
 
     int buf = 0;
     if (!win) {
-        for (int jb = j0; jb < j1; jb++, buf ^= 1) {
+        for (int jb = j0; jb < j1; jb++, buf ^= (NW > 1)) {
             if (jb - sm.base >= 64) split_meta(sm, p, a, jb, j1, true);   // blocks are visited in order
             const int i = jb - sm.base;
             const int bw = __builtin_amdgcn_readlane(sm.bits, i);
@@ -520,26 +497,34 @@ __global__ __launch_bounds__(64 * NG) void decode_g4_split(DecodeArgs p, uint32_
             const uint8_t *vb = p.v.pool + (((uint64_t)(uint32_t)__builtin_amdgcn_readlane(sm.vhi, i) << 32) |
                                             (uint32_t)__builtin_amdgcn_readlane(sm.vlo, i));
             switch (bw) {
-            case 2: round_block<2, NG>(st, qs[w], qg, kb, vb, p.t.H, g, w, p.c, vt[w], xs[buf]); break;
-            case 3: round_block<3, NG>(st, qs[w], qg, kb, vb, p.t.H, g, w, p.c, vt[w], xs[buf]); break;
-            case 4: round_block<4, NG>(st, qs[w], qg, kb, vb, p.t.H, g, w, p.c, vt[w], xs[buf]); break;
-            default: round_block<8, NG>(st, qs[w], qg, kb, vb, p.t.H, g, w, p.c, vt[w], xs[buf]); break;
+            case 2: round_block<2, NG, GW>(st, qs[w], qg, kb, vb, p.t.H, g, w, p.c, vt[w], xs[buf]); break;
+            case 3: round_block<3, NG, GW>(st, qs[w], qg, kb, vb, p.t.H, g, w, p.c, vt[w], xs[buf]); break;
+            case 4: round_block<4, NG, GW>(st, qs[w], qg, kb, vb, p.t.H, g, w, p.c, vt[w], xs[buf]); break;
+            default: round_block<8, NG, GW>(st, qs[w], qg, kb, vb, p.t.H, g, w, p.c, vt[w], xs[buf]); break;
             }
         }
     } else {
         const uint16_t *kwin = p.k.window + (size_t)a * p.t.window_cap * p.t.H * D;
         const uint16_t *vwin = p.v.window + (size_t)a * p.t.window_cap * p.t.H * D;
-        for (int w0 = 0; w0 < nw; w0 += 64, buf ^= 1)
-            round_window<NG>(st, qs[w], kwin, vwin, p.t.H, g, w, w0, nw, p.c, vt[w], xs[buf]);
+        for (int w0 = 0; w0 < nw; w0 += 64, buf ^= (NW > 1))
+            round_window<NG, GW>(st, qs[w], kwin, vwin, p.t.H, g, w, w0, nw, p.c, vt[w], xs[buf]);
     }
 
     // Head j's sums over the 16 lanes that hold it.
-    float l = st.l_lane, ps = st.ps_lane, pb = st.pb_lane;
+    float l = st.l_lane, ps[GW], pb[GW];
+#pragma unroll
+    for (int u = 0; u < GW; u++) {
+        ps[u] = st.ps_lane[u];
+        pb[u] = st.pb_lane[u];
+    }
 #pragma unroll
     for (int o = 4; o < 64; o <<= 1) {
         l += __shfl_xor(l, o);
-        ps += __shfl_xor(ps, o);
-        pb += __shfl_xor(pb, o);
+#pragma unroll
+        for (int u = 0; u < GW; u++) {
+            ps[u] += __shfl_xor(ps[u], o);
+            pb[u] += __shfl_xor(pb[u], o);
+        }
     }
     const size_t stride = (size_t)(D + 2);
     const size_t rbase = (size_t)a * p.Hq + (size_t)g * p.G;
@@ -548,32 +533,25 @@ __global__ __launch_bounds__(64 * NG) void decode_g4_split(DecodeArgs p, uint32_
         pr[0] = st.m_run;
         pr[1] = l;
     }
-    // lane l holds group position l (dim 64w + d) of head i in o[i]:
+    // lane l holds position l (dim 64(GW w + u) + d) of head i in o[u][i]:
     // output = (sum p''(1024+m c) - 1024 sum p'')/64 + sum p b for coded
     // tokens, sum p v for the window (lane i holds head i's sums)
-    const int d = 64 * w + ((lane & ~7) | ((lane & 7) >> 1) | ((lane & 1) << 2));
+    const int d = (lane & ~7) | ((lane & 7) >> 1) | ((lane & 1) << 2);
 #pragma unroll
     for (int i = 0; i < 4; i++) {
-        const float psi = __shfl(ps, i), pbi = __shfl(pb, i);
+        float psi[GW], pbi[GW];
+#pragma unroll
+        for (int u = 0; u < GW; u++) {
+            psi[u] = __shfl(ps[u], i);
+            pbi[u] = __shfl(pb[u], i);
+        }
         if (i < p.G) {
-            const float v = win ? st.o[i] : __builtin_fmaf(st.o[i] - 1024.0f * psi, 1.0f / FV, pbi);
-            p.part[((rbase + i) * p.n_splits + s) * stride + 2 + d] = v;
+            float *pr = p.part + ((rbase + i) * p.n_splits + s) * stride + 2 + 64 * GW * w + d;
+#pragma unroll
+            for (int u = 0; u < GW; u++)
+                pr[64 * u] = win ? st.o[u][i] : __builtin_fmaf(st.o[u][i] - 1024.0f * psi[u], 1.0f / FV, pbi[u]);
         }
     }
-
-    // Last workgroup of (a, g) to finish merges every split.  The release
-    // fence makes this workgroup's partials visible device-wide before its
-    // ticket; the ticket counter wraps to zero on the last ticket.
-    __syncthreads();
-    if (threadIdx.x == 0) {
-        __threadfence();
-        const uint32_t t = atomicInc(tickets + (size_t)a * p.t.H + g, (uint32_t)(ns - 1));
-        last = (t == (uint32_t)(ns - 1));
-    }
-    __syncthreads();
-    if (!last) return;
-    __threadfence();
-    merge_splits(p, a, g, w, ns);
 }
 
 // Block scores for top-K selection: the Q.K products and scale/bias
@@ -636,16 +614,23 @@ __global__ __launch_bounds__(64) void decode_g4_scores(DecodeArgs p, float scale
 
 bool decode_g4_supported(int D, int G) { return G <= 4 && (D == 64 || D == 128 || D == 256); }
 
+// 64-dim groups per wave: head_dim 64 and 128 run one wave per workgroup,
+// head_dim 256 two waves of 128 dims (measured against one wave of 256 dims
+// and four of 64: fewer registers per wave than the first, less repeated
+// softmax work and LDS than the second).
+constexpr int GW256 = 2;
+
+static int g4_waves(int D) { return D == 256 ? 4 / GW256 : 1; }
+
 void decode_g4_plan(int A, int H, int D, int max_blocks, int window_cap, int *SB, int *n_splits)
 {
-    // Longest splits that still give about KVQ_G4_WAVES waves (one wave per
-    // 64 dims of a workgroup); longer splits keep the partials small.
-#ifndef KVQ_G4_WAVES
-#define KVQ_G4_WAVES 4096
-#endif
-    const long ng = D / 64;
+    // Longest splits that still give about 2048 workgroups (more, shorter
+    // splits and fewer, longer ones both measured slower on the Llama and
+    // Gemma decode shapes); the merge reads at most 512 splits.
+    (void)D;
     int sb = 64;
-    while (sb > 1 && (long)A * H * ng * ((max_blocks + sb - 1) / sb) < KVQ_G4_WAVES) sb >>= 1;
+    while (sb > 1 && (long)A * H * ((max_blocks + sb - 1) / sb) < 2048) sb >>= 1;
+    while ((max_blocks + sb - 1) / sb + 1 > 512) sb <<= 1;
     *SB = sb;
     *n_splits = (max_blocks + sb - 1) / sb + (window_cap > 0 ? 1 : 0);
     if (*n_splits < 1) *n_splits = 1;
@@ -665,16 +650,18 @@ hipError_t launch_g4_scores(const DecodeArgs &p, float scale, float *scores_h, h
     return hipGetLastError();
 }
 
-hipError_t launch_decode_g4(const DecodeArgs &p, uint32_t *tickets, hipStream_t s)
+hipError_t launch_decode_g4(const DecodeArgs &p, hipStream_t s)
 {
     dim3 grid(p.n_splits, p.t.H, p.t.A);
     switch (p.t.D) {
-    case 64: decode_g4_split<1><<<grid, 64, 0, s>>>(p, tickets); break;
-    case 128: decode_g4_split<2><<<grid, 128, 0, s>>>(p, tickets); break;
-    case 256: decode_g4_split<4><<<grid, 256, 0, s>>>(p, tickets); break;
+    case 64: decode_g4_split<1, 1><<<grid, 64, 0, s>>>(p); break;
+    case 128: decode_g4_split<2, 2><<<grid, 64, 0, s>>>(p); break;
+    case 256: decode_g4_split<4, GW256><<<grid, 64 * g4_waves(256), 0, s>>>(p); break;
     default: return hipErrorInvalidValue;
     }
-    return hipGetLastError();
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    return launch_decode_merge(p, s);
 }
 
 }  // namespace kvq

@@ -13,16 +13,21 @@
 // in steps of 32 tokens:
 //   1. K rows are the A operand of v_mfma_f32_16x16x32_f16 (16 tokens x 32
 //      dims), the G query heads (padded to 16) the B operand, so one MFMA
-//      tile gives S^T[16 tokens][16 heads].  Each lane loads a contiguous
-//      run of its token's packed codes, turns 8 codes into fp16 with one
-//      and_or per pair (the 1024.0 magic exponent), removes the magic with a
-//      packed fma and applies scale/bias with a second packed fma.
-//   2. V rows are unpacked the same way and written transposed into LDS
-//      (V^T[d][token], fp16), the A operand of the P.V MFMA.
+//      tile gives S^T[16 tokens][16 heads].  Every 32-dim K-step lies in one
+//      64-dim group: lane q of a token row holds codes 16q..16q+15 of each
+//      group, turned into exact fp16 integers (one and_or per pair with the
+//      1024.0 magic exponent, one packed fma to remove it).  Each group's
+//      products accumulate on their own, and the score is
+//      sum_g (s_tg T_tg + b_tg Q_g) in fp32, T_tg = sum_{d in g} q_d c_td,
+//      Q_g = sum_{d in g} q_d, with each token's (scale, bias) read from LDS.
+//   2. V codes, also exact, are written transposed into LDS (V^T[d][token]),
+//      the A operand of the P.V MFMA; the B operand of a 16-dim output tile
+//      is fp16(p_t s_tg) for the tile's group g, and sum_t p_t b_tg is added
+//      in fp32.  No restored value is rounded to fp16, so the output error
+//      is the rounding of p s, not of the values themselves.
 //   3. Online softmax in fp32 on the S^T tile (exp2, running max per head);
-//      the probabilities, rounded to fp16, are the B operand of P.V, and the
-//      running sum adds those same rounded values (so numerator and
-//      denominator use identical weights).
+//      the probabilities are rounded to fp16 once, and both the running sum
+//      and the products use those rounded values.
 // Each split writes (max, sum, unnormalised output) for its rows; the merge
 // kernel combines splits.
 //
@@ -40,64 +45,45 @@ using namespace dev;
 constexpr int VT_PAD = 8;                  // LDS row padding (halves)
 constexpr int STEP = 32;                   // tokens per step
 
-// A lane's share of one token row: chunks [q*2NG, (q+1)*2NG) of 8 codes
-// (d in [16*NG*q, 16*NG*(q+1))), held as NDW dwords.
-template <int B, int NG>
-struct Row {
-    static constexpr int BYTES = 2 * NG * B;                 // codes bytes of the lane
-    static constexpr bool ODD = (B == 3 && NG == 1);         // 6 bytes at offset 6q
-    static constexpr int NDW = ODD ? 2 : BYTES / 4;
+// Lane q's share of one 64-dim group of a token row: chunks 2q and 2q+1 of
+// 8 codes (2B bytes at byte 2Bq of the group), held as NDW dwords.
+template <int B>
+struct GRow {
+    static constexpr bool ODD = (B == 3);                    // 6 bytes at offset 6q
+    static constexpr int NDW = ODD ? 2 : (2 * B) / 4;
 
-    __device__ static __forceinline__ void load(uint32_t *w, const uint8_t *row, int q)
+    __device__ static __forceinline__ void load(uint32_t *w, const uint8_t *grp, int q)
     {
         if constexpr (ODD) {
-            const uint32_t *p = reinterpret_cast<const uint32_t *>(row + ((6 * q) & ~3));
+            const uint32_t *p = reinterpret_cast<const uint32_t *>(grp + ((6 * q) & ~3));
             w[0] = p[0];
             w[1] = p[1];
+        } else if constexpr (B == 2) {
+            w[0] = reinterpret_cast<const uint32_t *>(grp)[q];
+        } else if constexpr (B == 4) {
+            const uint2 v = reinterpret_cast<const uint2 *>(grp)[q];
+            w[0] = v.x; w[1] = v.y;
         } else {
-            const uint8_t *base = row + q * BYTES;
-            if constexpr (BYTES % 16 == 0) {
-#pragma unroll
-                for (int i = 0; i < BYTES / 16; i++) {
-                    const uint4 v = reinterpret_cast<const uint4 *>(base)[i];
-                    w[4 * i] = v.x; w[4 * i + 1] = v.y; w[4 * i + 2] = v.z; w[4 * i + 3] = v.w;
-                }
-            } else if constexpr (BYTES % 8 == 0) {
-#pragma unroll
-                for (int i = 0; i < BYTES / 8; i++) {
-                    const uint2 v = reinterpret_cast<const uint2 *>(base)[i];
-                    w[2 * i] = v.x; w[2 * i + 1] = v.y;
-                }
-            } else {
-#pragma unroll
-                for (int i = 0; i < NDW; i++) w[i] = reinterpret_cast<const uint32_t *>(base)[i];
-            }
+            const uint4 v = reinterpret_cast<const uint4 *>(grp)[q];
+            w[0] = v.x; w[1] = v.y; w[2] = v.z; w[3] = v.w;
         }
     }
 
-    // Exact codes of chunk c as fp16 pairs.
-    __device__ static __forceinline__ Pairs chunk(const uint32_t *w, int q, int c)
+    // Exact codes of the lane's chunk u (0 or 1) as fp16 pairs.
+    __device__ static __forceinline__ Pairs chunk(const uint32_t *w, int q, int u)
     {
         if constexpr (B == 4) {
-            return Unpack<4>::run(w[c]);
+            return Unpack<4>::run(w[u]);
         } else if constexpr (B == 2) {
-            const uint32_t d = w[c >> 1];
-            return Unpack<2>::run((c & 1) ? (d >> 16) : (d & 0xffffu));
+            return Unpack<2>::run(u ? (w[0] >> 16) : (w[0] & 0xffffu));
         } else if constexpr (B == 8) {
-            return Unpack<8>::run2(w[2 * c], w[2 * c + 1]);
-        } else if constexpr (ODD) {
-            const int o = ((6 * q) & 3) + 3 * c;               // o <= 5
-            return Unpack<3>::run3(o >= 4 ? w[1] : w[0], w[1], o & 3);
+            return Unpack<8>::run2(w[2 * u], w[2 * u + 1]);
         } else {
-            const int o = 3 * c;
-            const int i = o >> 2;
-            const uint32_t lo = w[i];
-            const uint32_t hi = (i + 1 < NDW) ? w[i + 1] : w[i];
-            return Unpack<3>::run3(lo, hi, o & 3);
+            const int o = ((6 * q) & 3) + 3 * u;               // o <= 5
+            return Unpack<3>::run3(o >= 4 ? w[1] : w[0], w[1], o & 3);
         }
     }
 };
-
 
 __device__ __forceinline__ h8 operand(const Pairs &pr)
 {
@@ -116,11 +102,20 @@ __device__ __forceinline__ int tile_token(int m, int tau) { return 8 * (m >> 2) 
 template <int NG>
 struct DecodeState {
     static constexpr int D = 64 * NG;
-    static constexpr int KS = 2 * NG;        // K-steps of 32 dims
+    static constexpr int KS = 2 * NG;        // K-steps of 32 dims (two per group)
     static constexpr int NT = D / 16;        // output tiles of 16 dims
     h8 qop[KS];                              // B operand of Q.K^T
-    f4 acc[NT];                              // O^T tiles: [d = 16nt + 4q + j][head]
+    float qsum[NG];                          // Q_g of the lane's head
+    f4 acc[NT];                              // O^T tiles: [d = 16nt + 4q + j][head], sum p s c
+    float bacc[NG];                          // the lane's share of sum_t p_t b_tg
     float m_run, l_run;                      // log2-domain running max, running sum
+};
+
+// Per-step (scale, bias) of every token and group, K then V, written by the
+// lanes that load them (lane q < NG loads group q of its rows).
+template <int NG>
+struct StepMeta {
+    uint32_t k[NG][STEP], v[NG][STEP];
 };
 
 // Registers of one 32-token step of a quantized block, loaded ahead of use.
@@ -137,55 +132,75 @@ __device__ __forceinline__ size_t step_row(int g, int half, int m, int tau)
     return (size_t)g * 64 + 32 * half + tile_token(m, tau);
 }
 
-template <int B, int NG>
-__device__ __forceinline__ void load_step(Raw<NG> &r, const uint8_t *kblk, const uint8_t *vblk,
-                                          int H, int g, int half)
+template <int B, int NG, int W>
+__device__ __forceinline__ void load_rows(uint32_t (&kw)[2][W], uint32_t (&vw)[2][W], uint32_t km[2],
+                                          uint32_t vm[2], const uint8_t *kblk, const uint8_t *vblk, int H,
+                                          int g, int half)
 {
-    constexpr int CODE_ROW = 64 * NG * B / 8;
+    constexpr int CODE_ROW = 64 * NG * B / 8, GB = 8 * B, ND = GRow<B>::NDW;
     const int lane = threadIdx.x, m = lane & 15, q = lane >> 4;
     const size_t meta0 = (size_t)H * 64 * CODE_ROW;
-    const int grp = (NG * q) >> 2;           // group of the lane's dims [16*NG*q, 16*NG*(q+1))
+    const int grp = q < NG ? q : 0;
 #pragma unroll
     for (int tau = 0; tau < 2; tau++) {
         const size_t row = step_row(g, half, m, tau);
-        Row<B, NG>::load(r.k[tau], kblk + row * CODE_ROW, q);
-        Row<B, NG>::load(r.v[tau], vblk + row * CODE_ROW, q);
-        r.km[tau] = reinterpret_cast<const uint32_t *>(kblk + meta0)[row * NG + grp];
-        r.vm[tau] = reinterpret_cast<const uint32_t *>(vblk + meta0)[row * NG + grp];
+#pragma unroll
+        for (int gg = 0; gg < NG; gg++) {
+            GRow<B>::load(kw[tau] + ND * gg, kblk + row * CODE_ROW + GB * gg, q);
+            GRow<B>::load(vw[tau] + ND * gg, vblk + row * CODE_ROW + GB * gg, q);
+        }
+        km[tau] = reinterpret_cast<const uint32_t *>(kblk + meta0)[row * NG + grp];
+        vm[tau] = reinterpret_cast<const uint32_t *>(vblk + meta0)[row * NG + grp];
     }
 }
 
-// S^T tiles of the step into s[0..1]; V^T rows of the step into LDS.
+template <int B, int NG>
+__device__ __forceinline__ void load_step(Raw<NG> &r, const uint8_t *kblk, const uint8_t *vblk, int H, int g,
+                                          int half)
+{
+    load_rows<B, NG, Raw<NG>::KW>(r.k, r.v, r.km, r.vm, kblk, vblk, H, g, half);
+}
+
+// Per-group S^T tiles of the step into T[tau][group]; V^T codes of the step
+// and the step's (scale, bias) words into LDS.
 template <int B, int NG, int W>
 __device__ __forceinline__ void compute_rows(const DecodeState<NG> &st, const uint32_t (&kw)[2][W],
                                              const uint32_t (&vw)[2][W], const uint32_t km[2],
-                                             const uint32_t vm[2], _Float16 *vt, f4 s[2])
+                                             const uint32_t vm[2], _Float16 *vt, StepMeta<NG> &sm,
+                                             f4 (&T)[2][NG])
 {
-    constexpr int KS = 2 * NG;
+    constexpr int ND = GRow<B>::NDW;
     const int lane = threadIdx.x, m = lane & 15, q = lane >> 4;
 #pragma unroll
     for (int tau = 0; tau < 2; tau++) {
-        f4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int k = 0; k < KS; k++) {
-            Pairs pr = Row<B, NG>::chunk(kw[tau], q, k);
-            dequant(pr, km[tau]);
-            acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(operand(pr), st.qop[k], acc, 0, 0, 0);
+        for (int gg = 0; gg < NG; gg++) {
+            f4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int u = 0; u < 2; u++)
+                acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(operand(GRow<B>::chunk(kw[tau] + ND * gg, q, u)),
+                                                             st.qop[2 * gg + u], acc, 0, 0, 0);
+            T[tau][gg] = acc;
         }
-        s[tau] = acc;
     }
 #pragma unroll
     for (int tau = 0; tau < 2; tau++) {
         const int t = tile_token(m, tau);
+        if (q < NG) {
+            sm.k[q][t] = km[tau];
+            sm.v[q][t] = vm[tau];
+        }
 #pragma unroll
-        for (int k = 0; k < KS; k++) {
-            Pairs pr = Row<B, NG>::chunk(vw[tau], q, k);
-            dequant(pr, vm[tau]);
-            const int d0 = 8 * (q * KS + k);
+        for (int gg = 0; gg < NG; gg++) {
 #pragma unroll
-            for (int i = 0; i < 4; i++) {
-                vt[(d0 + i) * (STEP + VT_PAD) + t] = pr.p[i][0];
-                vt[(d0 + i + 4) * (STEP + VT_PAD) + t] = pr.p[i][1];
+            for (int u = 0; u < 2; u++) {
+                const Pairs pr = GRow<B>::chunk(vw[tau] + ND * gg, q, u);
+                const int d0 = 8 * (8 * gg + 2 * q + u);
+#pragma unroll
+                for (int i = 0; i < 4; i++) {
+                    vt[(d0 + i) * (STEP + VT_PAD) + t] = pr.p[i][0];
+                    vt[(d0 + i + 4) * (STEP + VT_PAD) + t] = pr.p[i][1];
+                }
             }
         }
     }
@@ -195,59 +210,57 @@ __device__ __forceinline__ void compute_rows(const DecodeState<NG> &st, const ui
 template <int NG>
 __device__ __forceinline__ void step_block8(const DecodeState<NG> &st, const uint8_t *kblk,
                                             const uint8_t *vblk, int H, int g, int half,
-                                            _Float16 *vt, f4 s[2])
+                                            _Float16 *vt, StepMeta<NG> &sm, f4 (&T)[2][NG])
 {
-    constexpr int W = Row<8, NG>::NDW;
-    constexpr int CODE_ROW = 64 * NG;
-    const int lane = threadIdx.x, m = lane & 15, q = lane >> 4;
-    const size_t meta0 = (size_t)H * 64 * CODE_ROW;
-    const int grp = (NG * q) >> 2;
+    constexpr int W = 4 * NG;
     uint32_t kw[2][W], vw[2][W], km[2], vm[2];
-#pragma unroll
-    for (int tau = 0; tau < 2; tau++) {
-        const size_t row = step_row(g, half, m, tau);
-        Row<8, NG>::load(kw[tau], kblk + row * CODE_ROW, q);
-        Row<8, NG>::load(vw[tau], vblk + row * CODE_ROW, q);
-        km[tau] = reinterpret_cast<const uint32_t *>(kblk + meta0)[row * NG + grp];
-        vm[tau] = reinterpret_cast<const uint32_t *>(vblk + meta0)[row * NG + grp];
-    }
-    compute_rows<8, NG, W>(st, kw, vw, km, vm, vt, s);
+    load_rows<8, NG, W>(kw, vw, km, vm, kblk, vblk, H, g, half);
+    compute_rows<8, NG, W>(st, kw, vw, km, vm, vt, sm, T);
 }
 
 
 // One 32-token step of the bf16 window, tokens t0 .. t0+31 (rows past nw are
-// read from row nw-1 and masked by the caller).
+// read from row nw-1 and masked by the caller): values straight into the
+// products (scale 1, bias 0).
 template <int NG>
 __device__ __forceinline__ void step_window(const DecodeState<NG> &st, const uint16_t *kw,
                                             const uint16_t *vw, int H, int g, int t0, int nw,
-                                            _Float16 *vt, f4 s[2])
+                                            _Float16 *vt, f4 (&T)[2][NG])
 {
-    constexpr int D = 64 * NG, KS = 2 * NG;
+    constexpr int D = 64 * NG;
     const int lane = threadIdx.x, m = lane & 15, q = lane >> 4;
-    uint4 kr[2][KS], vr[2][KS];
+    uint4 kr[2][2 * NG], vr[2][2 * NG];
 #pragma unroll
     for (int tau = 0; tau < 2; tau++) {
         const int t = min(t0 + tile_token(m, tau), nw - 1);
-        const uint4 *kp = reinterpret_cast<const uint4 *>(kw + ((size_t)t * H + g) * D + 16 * NG * q);
-        const uint4 *vp = reinterpret_cast<const uint4 *>(vw + ((size_t)t * H + g) * D + 16 * NG * q);
+        const uint16_t *kp = kw + ((size_t)t * H + g) * D;
+        const uint16_t *vp = vw + ((size_t)t * H + g) * D;
 #pragma unroll
-        for (int k = 0; k < KS; k++) { kr[tau][k] = kp[k]; vr[tau][k] = vp[k]; }
+        for (int k = 0; k < 2 * NG; k++) {
+            const int c = 8 * (k >> 1) + 2 * q + (k & 1);      // chunk of K-step k
+            kr[tau][k] = *reinterpret_cast<const uint4 *>(kp + 8 * c);
+            vr[tau][k] = *reinterpret_cast<const uint4 *>(vp + 8 * c);
+        }
     }
 #pragma unroll
     for (int tau = 0; tau < 2; tau++) {
-        f4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int k = 0; k < KS; k++)
-            acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(operand(bf16_pairs(kr[tau][k])), st.qop[k], acc, 0, 0, 0);
-        s[tau] = acc;
+        for (int gg = 0; gg < NG; gg++) {
+            f4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int u = 0; u < 2; u++)
+                acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(operand(bf16_pairs(kr[tau][2 * gg + u])),
+                                                             st.qop[2 * gg + u], acc, 0, 0, 0);
+            T[tau][gg] = acc;
+        }
     }
 #pragma unroll
     for (int tau = 0; tau < 2; tau++) {
         const int t = tile_token(m, tau);
 #pragma unroll
-        for (int k = 0; k < KS; k++) {
+        for (int k = 0; k < 2 * NG; k++) {
             const Pairs pr = bf16_pairs(vr[tau][k]);
-            const int d0 = 8 * (q * KS + k);
+            const int d0 = 8 * (8 * (k >> 1) + 2 * q + (k & 1));
 #pragma unroll
             for (int i = 0; i < 4; i++) {
                 vt[(d0 + i) * (STEP + VT_PAD) + t] = pr.p[i][0];
@@ -257,20 +270,44 @@ __device__ __forceinline__ void step_window(const DecodeState<NG> &st, const uin
     }
 }
 
-// Online softmax on the step's S^T tiles, then O^T += V^T . P^T.
-// n_valid: tokens of the step that exist (32 except in the last window step).
-template <int NG>
-__device__ __forceinline__ void softmax_pv(DecodeState<NG> &st, const f4 s[2], int n_valid,
-                                           const _Float16 *vt, float c)
+// Online softmax on the step's scores, then O^T += V^T . P'^T per 16-dim
+// tile.  WIN: window step (scores are the plain sums, values carry no scale
+// or bias).  n_valid: tokens of the step that exist (32 except in the last
+// window step).
+template <int NG, bool WIN>
+__device__ __forceinline__ void softmax_pv(DecodeState<NG> &st, const f4 (&T)[2][NG], int n_valid,
+                                           const _Float16 *vt, const StepMeta<NG> &sm, float c)
 {
     constexpr int NT = 4 * NG;
     const int lane = threadIdx.x, m = lane & 15, q = lane >> 4;
+    __syncthreads();                          // V^T and the step's meta are in LDS
     float sc[8];
+    if constexpr (WIN) {
 #pragma unroll
-    for (int tau = 0; tau < 2; tau++)
+        for (int i = 0; i < 8; i++) {
+            float v = 0.0f;
 #pragma unroll
-        for (int j = 0; j < 4; j++)
-            sc[4 * tau + j] = (8 * q + 4 * tau + j < n_valid) ? s[tau][j] * c : -INFINITY;
+            for (int gg = 0; gg < NG; gg++) v += T[i >> 2][gg][i & 3];
+            sc[i] = v;
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < 8; i++) sc[i] = 0.0f;
+#pragma unroll
+        for (int gg = 0; gg < NG; gg++) {
+            const uint4 m0 = *reinterpret_cast<const uint4 *>(&sm.k[gg][8 * q]);
+            const uint4 m1 = *reinterpret_cast<const uint4 *>(&sm.k[gg][8 * q + 4]);
+            const uint32_t mw[8] = {m0.x, m0.y, m0.z, m0.w, m1.x, m1.y, m1.z, m1.w};
+#pragma unroll
+            for (int i = 0; i < 8; i++) {
+                const h2 sb = as_h2(mw[i]);
+                sc[i] = __builtin_fmaf((float)sb[0], T[i >> 2][gg][i & 3],
+                                       __builtin_fmaf((float)sb[1], st.qsum[gg], sc[i]));
+            }
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < 8; i++) sc[i] = (8 * q + i < n_valid) ? sc[i] * c : -INFINITY;
     float mx = sc[0];
 #pragma unroll
     for (int i = 1; i < 8; i++) mx = fmaxf(mx, sc[i]);
@@ -279,12 +316,15 @@ __device__ __forceinline__ void softmax_pv(DecodeState<NG> &st, const f4 s[2], i
     const float m_new = fmaxf(st.m_run, mx);
     const float alpha = __builtin_amdgcn_exp2f(st.m_run - m_new);
     h2 ph[4];
+    float pf[8];
     float lsum = 0.0f;
     const h2 ones = {(_Float16)1.0f, (_Float16)1.0f};
 #pragma unroll
     for (int k = 0; k < 4; k++) {
         const f2 pv = {__builtin_amdgcn_exp2f(sc[2 * k] - m_new), __builtin_amdgcn_exp2f(sc[2 * k + 1] - m_new)};
         ph[k] = __builtin_convertvector(pv, h2);
+        pf[2 * k] = (float)ph[k][0];
+        pf[2 * k + 1] = (float)ph[k][1];
         lsum = __builtin_amdgcn_fdot2(ph[k], ones, lsum, false);
     }
     st.l_run = st.l_run * alpha + lsum;
@@ -292,15 +332,38 @@ __device__ __forceinline__ void softmax_pv(DecodeState<NG> &st, const f4 s[2], i
     if (__any(alpha != 1.0f)) {
 #pragma unroll
         for (int nt = 0; nt < NT; nt++) st.acc[nt] *= alpha;
-    }
-    h8 pb;
 #pragma unroll
-    for (int k = 0; k < 4; k++) { pb[2 * k] = ph[k][0]; pb[2 * k + 1] = ph[k][1]; }
-    __syncthreads();                          // V^T of this step is in LDS
+        for (int gg = 0; gg < NG; gg++) st.bacc[gg] *= alpha;
+    }
+    h8 pb[NG];
+    if constexpr (WIN) {
+        h8 o;
+#pragma unroll
+        for (int k = 0; k < 4; k++) { o[2 * k] = ph[k][0]; o[2 * k + 1] = ph[k][1]; }
+#pragma unroll
+        for (int gg = 0; gg < NG; gg++) pb[gg] = o;
+    } else {
+#pragma unroll
+        for (int gg = 0; gg < NG; gg++) {
+            const uint4 m0 = *reinterpret_cast<const uint4 *>(&sm.v[gg][8 * q]);
+            const uint4 m1 = *reinterpret_cast<const uint4 *>(&sm.v[gg][8 * q + 4]);
+            const uint32_t mw[8] = {m0.x, m0.y, m0.z, m0.w, m1.x, m1.y, m1.z, m1.w};
+            float bsum = 0.0f;
+            h8 o;
+#pragma unroll
+            for (int i = 0; i < 8; i++) {
+                const h2 sb = as_h2(mw[i]);
+                o[i] = (_Float16)(pf[i] * (float)sb[0]);
+                bsum = __builtin_fmaf(pf[i], (float)sb[1], bsum);
+            }
+            pb[gg] = o;
+            st.bacc[gg] += bsum;
+        }
+    }
 #pragma unroll
     for (int nt = 0; nt < NT; nt++) {
         const h8 a = *reinterpret_cast<const h8 *>(vt + (16 * nt + m) * (STEP + VT_PAD) + 8 * q);
-        st.acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, pb, st.acc[nt], 0, 0, 0);
+        st.acc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, pb[nt >> 2], st.acc[nt], 0, 0, 0);
     }
     __syncthreads();                          // reads done before the next step writes
 }
@@ -311,6 +374,7 @@ __global__ __launch_bounds__(64) void decode_gqa_split(DecodeArgs p)
 {
     constexpr int D = 64 * NG, KS = 2 * NG, NT = 4 * NG;
     __shared__ __attribute__((aligned(16))) _Float16 vt[D * (STEP + VT_PAD)];
+    __shared__ __attribute__((aligned(16))) StepMeta<NG> sm;
     const int s = blockIdx.x, g = blockIdx.y, a = blockIdx.z;
     const int lane = threadIdx.x, m = lane & 15, q = lane >> 4;
     const int nb = seq_blocks(p.t, a), nw = seq_window(p.t, a);
@@ -322,14 +386,25 @@ __global__ __launch_bounds__(64) void decode_gqa_split(DecodeArgs p)
     const int h = g * p.G + m;
     const bool hv = m < p.G;
     const uint16_t *qrow = p.q + ((size_t)a * p.Hq + (hv ? h : 0)) * D;
+    const h2 ones = {(_Float16)1.0f, (_Float16)1.0f};
 #pragma unroll
-    for (int k = 0; k < KS; k++) {
-        const int d0 = 8 * (q * KS + k);
-        const uint4 v = *reinterpret_cast<const uint4 *>(qrow + d0);
-        const Pairs pr = bf16_pairs(v);
-        h8 o = operand(pr);
-        if (!hv) o = h8{0, 0, 0, 0, 0, 0, 0, 0};
-        st.qop[k] = o;
+    for (int gg = 0; gg < NG; gg++) {
+        float qs = 0.0f;
+#pragma unroll
+        for (int u = 0; u < 2; u++) {
+            const int c = 8 * gg + 2 * q + u;                 // chunk of K-step 2gg + u
+            const uint4 v = *reinterpret_cast<const uint4 *>(qrow + 8 * c);
+            const Pairs pr = bf16_pairs(v);
+            h8 o = operand(pr);
+            if (!hv) o = h8{0, 0, 0, 0, 0, 0, 0, 0};
+            st.qop[2 * gg + u] = o;
+#pragma unroll
+            for (int i = 0; i < 4; i++) qs = __builtin_amdgcn_fdot2(h2{o[2 * i], o[2 * i + 1]}, ones, qs, false);
+        }
+        qs += __shfl_xor(qs, 16);
+        qs += __shfl_xor(qs, 32);
+        st.qsum[gg] = qs;
+        st.bacc[gg] = 0.0f;
     }
 #pragma unroll
     for (int nt = 0; nt < NT; nt++) st.acc[nt] = f4{0.f, 0.f, 0.f, 0.f};
@@ -357,16 +432,16 @@ __global__ __launch_bounds__(64) void decode_gqa_split(DecodeArgs p)
         auto run = [&](const Raw<NG> &r, int i) {
             const size_t e = e0 + (i >> 1);
             const int b = p.t.bits[e];
-            f4 sc[2];
+            f4 T[2][NG];
             switch (b) {
-            case 2: compute_rows<2, NG, Raw<NG>::KW>(st, r.k, r.v, r.km, r.vm, vt, sc); break;
-            case 3: compute_rows<3, NG, Raw<NG>::KW>(st, r.k, r.v, r.km, r.vm, vt, sc); break;
-            case 4: compute_rows<4, NG, Raw<NG>::KW>(st, r.k, r.v, r.km, r.vm, vt, sc); break;
+            case 2: compute_rows<2, NG, Raw<NG>::KW>(st, r.k, r.v, r.km, r.vm, vt, sm, T); break;
+            case 3: compute_rows<3, NG, Raw<NG>::KW>(st, r.k, r.v, r.km, r.vm, vt, sm, T); break;
+            case 4: compute_rows<4, NG, Raw<NG>::KW>(st, r.k, r.v, r.km, r.vm, vt, sm, T); break;
             default:
-                step_block8<NG>(st, kbase + p.k.offset[e], vbase + p.v.offset[e], H, g, i & 1, vt, sc);
+                step_block8<NG>(st, kbase + p.k.offset[e], vbase + p.v.offset[e], H, g, i & 1, vt, sm, T);
                 break;
             }
-            softmax_pv<NG>(st, sc, STEP, vt, p.c);
+            softmax_pv<NG, false>(st, T, STEP, vt, sm, p.c);
         };
         if (n_steps > 0) issue(ra, 0);
         for (int i = 0; i < n_steps; i += 2) {
@@ -379,22 +454,29 @@ __global__ __launch_bounds__(64) void decode_gqa_split(DecodeArgs p)
         const uint16_t *kw = p.k.window + (size_t)a * p.t.window_cap * p.t.H * D;
         const uint16_t *vw = p.v.window + (size_t)a * p.t.window_cap * p.t.H * D;
         for (int t0 = 0; t0 < nw; t0 += STEP) {
-            f4 sc[2];
-            step_window<NG>(st, kw, vw, p.t.H, g, t0, nw, vt, sc);
-            softmax_pv<NG>(st, sc, nw - t0, vt, p.c);
+            f4 T[2][NG];
+            step_window<NG>(st, kw, vw, p.t.H, g, t0, nw, vt, T);
+            softmax_pv<NG, true>(st, T, nw - t0, vt, sm, p.c);
         }
     }
 
     float l = st.l_run;
     l += __shfl_xor(l, 16);
     l += __shfl_xor(l, 32);
+    float bt[NG];
+#pragma unroll
+    for (int gg = 0; gg < NG; gg++) {
+        bt[gg] = st.bacc[gg];
+        bt[gg] += __shfl_xor(bt[gg], 16);
+        bt[gg] += __shfl_xor(bt[gg], 32);
+    }
     if (hv) {
         float *pr = p.part + ((size_t)(a * p.Hq + h) * p.n_splits + s) * (D + 2);
         if (q == 0) { pr[0] = st.m_run; pr[1] = l; }
 #pragma unroll
         for (int nt = 0; nt < NT; nt++)
 #pragma unroll
-            for (int j = 0; j < 4; j++) pr[2 + 16 * nt + 4 * q + j] = st.acc[nt][j];
+            for (int j = 0; j < 4; j++) pr[2 + 16 * nt + 4 * q + j] = st.acc[nt][j] + bt[nt >> 2];
     }
 }
 

@@ -74,7 +74,6 @@ struct Plan {
     int mla_sb, mla_splits;     // latent decode
     int ch_row_tiles, ch_splits, ch_split_tiles;   // tuned chunk
     bool ch_ok;
-    size_t ticket_bytes;        // decode: per-(sequence, KV head) merge tickets at the start of the workspace
     size_t ws_bytes;
 };
 
@@ -95,7 +94,6 @@ int plan_attention(const kvq_layout *L, int n_q_heads, int rope_dim, int n_new, 
     if ((int64_t)pl->n_row_tiles * L->n_heads > kMaxGrid) return KVQ_EUNSUPPORTED;
     const size_t rows = (size_t)L->n_seqs * n_qtok * n_q_heads;
     if (rows > 0x7fffffffu) return KVQ_EUNSUPPORTED;
-    pl->ticket_bytes = 0;
     pl->ws_bytes = round256(rows * (size_t)pl->n_splits * (size_t)(L->head_dim + 2) * sizeof(float));
     if (n_new == 0) {
         decode_gqa_plan(L->n_seqs, L->n_heads, L->max_blocks, L->window_cap, &pl->sb, &pl->dec_splits);
@@ -112,10 +110,6 @@ int plan_attention(const kvq_layout *L, int n_q_heads, int rope_dim, int n_new, 
             t = round256(rows * (size_t)pl->mla_splits * (size_t)(L->head_dim + 2) * sizeof(float));
             if (t > pl->ws_bytes) pl->ws_bytes = t;
         }
-        // Every decode workspace starts with the tickets (whichever kernel
-        // runs), so no decode call overwrites them with partials.
-        pl->ticket_bytes = round256((size_t)L->n_seqs * L->n_heads * sizeof(uint32_t));
-        pl->ws_bytes += pl->ticket_bytes;
     }
     pl->ch_ok = false;
     if (n_new > 0 && chunk_supported(L->head_dim)) {
@@ -386,8 +380,7 @@ int kvq_attend_decode(const kvq_layout *L, const kvq_store *K, const kvq_store *
     if (!(softmax_scale > 0.0f) || !isfinite(softmax_scale)) return KVQ_EINVAL;
     if (workspace_bytes < pl.ws_bytes) return KVQ_ENOSPC;
     if (!workspace || !aligned(workspace, 256)) return KVQ_EINVAL;
-    uint32_t *tickets = static_cast<uint32_t *>(workspace);
-    float *part = reinterpret_cast<float *>(static_cast<uint8_t *>(workspace) + pl.ticket_bytes);
+    float *part = static_cast<float *>(workspace);
 
     if (V && rope_dim == 0 && decode_gqa_supported(L->head_dim)) {
         DecodeArgs d{};
@@ -406,7 +399,7 @@ int kvq_attend_decode(const kvq_layout *L, const kvq_store *K, const kvq_store *
         if (decode_g4_supported(L->head_dim, d.G)) {
             d.SB = pl.g4_sb;
             d.n_splits = pl.g4_splits;
-            return hip_status(launch_decode_g4(d, tickets, hs));
+            return hip_status(launch_decode_g4(d, hs));
         }
         return hip_status(launch_decode_gqa(d, hs));
     }
@@ -454,9 +447,8 @@ int kvq_attend_decode(const kvq_layout *L, const kvq_store *K, const kvq_store *
 }
 
 namespace {
-// Workspace of a top-K call: the decode's own workspace first (so its merge
-// tickets sit at the start, as for kvq_attend_decode), then the selection
-// tables.
+// Workspace of a top-K call: the decode's own workspace first, then the
+// selection tables.
 struct TopkWs {
     size_t scores, n_sel, sel_idx, sel_bits, sel_koff, sel_voff, rope_sel, dec, total;
     kvq_layout L2;                            // pointers filled in at call time

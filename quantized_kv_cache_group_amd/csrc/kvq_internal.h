@@ -153,7 +153,7 @@ hipError_t launch_append(const AppendArgs &a, hipStream_t s);          // blocks
 hipError_t launch_dequantize(const DequantArgs &a, hipStream_t s);
 hipError_t launch_attend_generic(const AttnArgs &a, hipStream_t s);
 hipError_t launch_decode_gqa(const DecodeArgs &a, hipStream_t s);     // split + merge
-hipError_t launch_decode_g4(const DecodeArgs &a, uint32_t *tickets, hipStream_t s);   // split + merge (G <= 4)
+hipError_t launch_decode_g4(const DecodeArgs &a, hipStream_t s);      // split + merge (G <= 4)
 hipError_t launch_g4_scores(const DecodeArgs &a, float scale, float *scores_h, hipStream_t s);
 hipError_t launch_decode_merge(const DecodeArgs &a, hipStream_t s);
 bool decode_g4_supported(int D, int G);

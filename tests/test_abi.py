@@ -215,18 +215,6 @@ def test_chunk_rejects():
     assert call(n=0) == kvq.KVQ_OK                            # nothing to do, nothing launched
 
 
-def test_decode_workspace_starts_with_tickets():
-    """The decode workspace covers the merge tickets (4 bytes per sequence and
-    KV head, rounded to 256) on top of the partials, whatever kernel runs."""
-    n = ctypes.c_size_t(0)
-    small = _layout(n_seqs=1, n_heads=2)
-    big = _layout(n_seqs=100, n_heads=2)
-    assert kvq.lib().kvq_decode_workspace(ctypes.byref(small), 8, 0, ctypes.byref(n)) == kvq.KVQ_OK
-    a = n.value
-    assert kvq.lib().kvq_decode_workspace(ctypes.byref(big), 8, 0, ctypes.byref(n)) == kvq.KVQ_OK
-    assert n.value >= 100 * 2 * 4 + 256 and a >= 256 + 256
-
-
 def _topk(L, K, V=None, Hq=8, scale=0.125, top_k=4, selected=None, ws=FAKE, ws_bytes=1 << 40):
     P = lambda x: None if x is None else ctypes.c_void_p(x)
     return kvq.lib().kvq_attend_decode_topk(ctypes.byref(L), ctypes.byref(K),

@@ -214,25 +214,20 @@ def test_chunk_mixed_widths_window(D, G):
         close(got[a], _ref_chunk(b, a, qn[a], kn[a], vn[a], D ** -0.5), what=f"chunk D={D} a={a}")
 
 
-def test_decode_workspace_reuse_leaves_tickets_zero():
-    """One zero-filled workspace serves several decode and top-K calls in a
-    row: every call gives the same output as the first, and the merge
-    tickets at the start of the workspace are zero after each call."""
+def test_decode_workspace_reuse():
+    """One workspace serves several decode and top-K calls in a row (the top-K
+    call's selection tables sit after the decode's partials): every decode
+    gives the same output as the first."""
     H, D, G = 8, 128, 4
     lengths = [64 * 30 + 50, 64 * 9, 300]
     b = build(H, D, lengths, keep_recent=60, seed=33)
     c = b.cache
     q = to_dev_bf16(syn.random_normal_bf16((3, G * H, D), 34))
     nb = max(c.topk_workspace_bytes(G * H, 4), c.decode_workspace_bytes(G * H))
-    ws = torch.zeros(nb, dtype=torch.uint8, device="cuda")
-    tb = (3 * H * 4 + 255) // 256 * 256
+    ws = torch.full((nb,), 0xA5, dtype=torch.uint8, device="cuda")
     first = c.attend_decode(q, D ** -0.5, workspace=ws).cpu().numpy()
-    assert int(ws[:tb].count_nonzero()) == 0
     for i in range(3):
         c.attend_decode_topk(q, D ** -0.5, 4, workspace=ws)
-        torch.cuda.synchronize()
-        assert int(ws[:tb].count_nonzero()) == 0
         again = c.attend_decode(q, D ** -0.5, workspace=ws).cpu().numpy()
-        assert int(ws[:tb].count_nonzero()) == 0
         assert np.array_equal(first, again)
     close(first, ref_decode(b, syn.random_normal_bf16((3, G * H, D), 34), D ** -0.5), what="reuse")
