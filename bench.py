@@ -80,8 +80,12 @@ TRAFFIC = {
     (2, "kvq quantize"): (("quantize.hip",), "80dc430f5391874b", 268014.8, 119916.2),
     (3, "kvq dequantize"): (("quantize.hip",), "80dc430f5391874b", 9271.8, 65554.1),
     (3, "kvq attend_chunk"): (("chunk.hip",), "7e9bc99935b2e36f", 47185.6 + 16672.5, 35004.3 + 8192.0),
-    (4, "kvq attend_decode"): (("mla.hip", "decode_gqa.hip"), "dfc24c56db94b551",
-                               27112.9 + 4169.1, 8320.0 + 128.0),
+    (1, "kvq attend_decode"): (("decode_g4.hip", "decode_gqa.hip"), "c27ef61104138f0c",
+                               23481.0 + 2656.3, 5440.0 + 160.0),
+    (2, "kvq attend_decode"): (("decode_g4.hip", "decode_gqa.hip"), "c27ef61104138f0c",
+                               64373.0 + 2256.5, 4488.0 + 128.0),
+    (4, "kvq attend_decode"): (("mla.hip", "decode_gqa.hip"), "7078c6672220cec5",
+                               27112.8 + 4169.3, 8320.2 + 128.0),
     ("alloc", "kvq block_sensitivity"): (("alloc.hip",), "daa276e1c505e00b", 430498.4, 62.0),
 }
 
