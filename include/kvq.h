@@ -263,6 +263,23 @@ int kvq_attend_decode(const kvq_layout *L, const kvq_store *K, const kvq_store *
                       int32_t n_q_heads, float softmax_scale, float *out,
                       void *workspace, size_t workspace_bytes, void *stream);
 
+/* kvq_attend_decode for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation): the same computation and kernels, with the split partials in
+ * a library-owned device array of 16 MiB per GPU (taken once per device on
+ * the first call there, held until the process ends) instead of a caller
+ * workspace.  Arguments as for kvq_attend_decode without the workspace.
+ * Every call on one GPU shares that GPU's array: calls that overlap in time
+ * on one GPU (other streams, other threads) race and give undefined results.
+ * The array needs no clearing: each call writes every partial it reads.
+ * Allocates nothing (no hipMalloc, no allocating library call).
+ * Errors: as kvq_attend_decode; KVQ_ENOSPC when the call's workspace
+ *         (kvq_decode_workspace) exceeds 16 MiB; KVQ_EHIP when the array's
+ *         address cannot be taken on the current device. */
+int kvq_attend_decode_static(const kvq_layout *L, const kvq_store *K, const kvq_store *V,
+                             const uint16_t *rope, int32_t rope_dim, const uint16_t *q,
+                             int32_t n_q_heads, float softmax_scale, float *out, void *stream);
+
 /* Workspace bytes kvq_attend_decode_topk needs (written to *bytes).
  * Errors: KVQ_EINVAL, KVQ_EUNSUPPORTED. */
 int kvq_topk_workspace(const kvq_layout *L, int32_t n_q_heads, int32_t rope_dim, int32_t top_k,

@@ -26,7 +26,7 @@ WIDTHS = (2, 3, 4, 8)
 
 SYMBOLS = ("kvq_block_bytes", "kvq_quantize", "kvq_quantize_kv", "kvq_append", "kvq_dequantize", "kvq_card_bytes",
            "kvq_card_gather", "kvq_card_scatter", "kvq_block_sensitivity", "kvq_allocate_widths",
-           "kvq_decode_workspace", "kvq_attend_decode",
+           "kvq_decode_workspace", "kvq_attend_decode", "kvq_attend_decode_static",
            "kvq_topk_workspace", "kvq_attend_decode_topk", "kvq_chunk_workspace", "kvq_attend_chunk",
            "kvq_strerror")
 
@@ -88,6 +88,8 @@ def lib() -> ctypes.CDLL:
         L.kvq_attend_decode.restype = ctypes.c_int
         L.kvq_topk_workspace.argtypes = [P, i32, i32, i32, ctypes.POINTER(sz)]
         L.kvq_topk_workspace.restype = ctypes.c_int
+        L.kvq_attend_decode_static.argtypes = [P, P, P, P, i32, P, i32, f32, P, P]
+        L.kvq_attend_decode_static.restype = ctypes.c_int
         L.kvq_attend_decode_topk.argtypes = [P, P, P, P, i32, P, i32, f32, i32, P, P, P, sz, P]
         L.kvq_attend_decode_topk.restype = ctypes.c_int
         L.kvq_chunk_workspace.argtypes = [P, i32, i32, ctypes.POINTER(sz)]
@@ -394,6 +396,22 @@ class LayerCache:
                                        _ptr(self.rope), self.rope_dim, _ptr(q), Hq, float(scale),
                                        _ptr(out), _ptr(workspace), workspace.numel(),
                                        _stream(stream)), "kvq_attend_decode")
+        return out
+
+    def attend_decode_static(self, q: torch.Tensor, scale: float, out: torch.Tensor | None = None,
+                             stream=None) -> torch.Tensor:
+        """attend_decode with the library's own device scratch (no workspace):
+        q bf16 [A][Hq][D + rope_dim] -> fp32 [A][Hq][D]."""
+        assert q.dtype == torch.bfloat16 and q.is_contiguous() and q.shape[0] == self.A
+        Hq = q.shape[1]
+        if out is None:
+            out = torch.empty((self.A, Hq, self.D), dtype=torch.float32, device=q.device)
+        kst = self.store("k")
+        vst = self.store("v")
+        _check(lib().kvq_attend_decode_static(ctypes.byref(self._layout), ctypes.byref(kst),
+                                              None if vst is None else ctypes.byref(vst),
+                                              _ptr(self.rope), self.rope_dim, _ptr(q), Hq, float(scale),
+                                              _ptr(out), _stream(stream)), "kvq_attend_decode_static")
         return out
 
     def topk_workspace_bytes(self, n_q_heads: int, top_k: int) -> int:

@@ -3,6 +3,8 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "kvq_internal.h"
 
 using namespace kvq;
@@ -364,13 +366,14 @@ int kvq_decode_workspace(const kvq_layout *L, int32_t n_q_heads, int32_t rope_di
     return KVQ_OK;
 }
 
-int kvq_attend_decode(const kvq_layout *L, const kvq_store *K, const kvq_store *V,
-                      const uint16_t *rope, int32_t rope_dim, const uint16_t *q,
-                      int32_t n_q_heads, float softmax_scale, float *out,
-                      void *workspace, size_t workspace_bytes, void *stream)
+}  // extern "C"
+
+namespace {
+// Argument checks of a decode call other than the workspace (host only).
+int check_decode(const kvq_layout *L, const kvq_store *K, const kvq_store *V, const uint16_t *rope,
+                 int32_t rope_dim, const uint16_t *q, int32_t n_q_heads, float softmax_scale, float *out, Plan *pl)
 {
-    Plan pl;
-    int st = plan_attention(L, n_q_heads, rope_dim, 0, &pl);
+    int st = plan_attention(L, n_q_heads, rope_dim, 0, pl);
     if (st) return st;
     if ((st = check_store(L, K))) return st;
     if (V && (st = check_store(L, V))) return st;
@@ -378,8 +381,37 @@ int kvq_attend_decode(const kvq_layout *L, const kvq_store *K, const kvq_store *
     if (rope && !aligned(rope, 16)) return KVQ_EINVAL;
     if (!q || !out || !aligned(q, 16) || !aligned(out, 16)) return KVQ_EINVAL;
     if (!(softmax_scale > 0.0f) || !isfinite(softmax_scale)) return KVQ_EINVAL;
+    return KVQ_OK;
+}
+
+int attend_decode_impl(const kvq_layout *L, const kvq_store *K, const kvq_store *V, const uint16_t *rope,
+                       int32_t rope_dim, const uint16_t *q, int32_t n_q_heads, float softmax_scale, float *out,
+                       void *workspace, const Plan &pl, void *stream);
+}  // namespace
+
+extern "C" {
+
+int kvq_attend_decode(const kvq_layout *L, const kvq_store *K, const kvq_store *V,
+                      const uint16_t *rope, int32_t rope_dim, const uint16_t *q,
+                      int32_t n_q_heads, float softmax_scale, float *out,
+                      void *workspace, size_t workspace_bytes, void *stream)
+{
+    Plan pl;
+    int st = check_decode(L, K, V, rope, rope_dim, q, n_q_heads, softmax_scale, out, &pl);
+    if (st) return st;
     if (workspace_bytes < pl.ws_bytes) return KVQ_ENOSPC;
     if (!workspace || !aligned(workspace, 256)) return KVQ_EINVAL;
+    return attend_decode_impl(L, K, V, rope, rope_dim, q, n_q_heads, softmax_scale, out, workspace, pl, stream);
+}
+
+}  // extern "C"
+
+namespace {
+// The decode's launches once every argument has been checked.
+int attend_decode_impl(const kvq_layout *L, const kvq_store *K, const kvq_store *V, const uint16_t *rope,
+                       int32_t rope_dim, const uint16_t *q, int32_t n_q_heads, float softmax_scale, float *out,
+                       void *workspace, const Plan &pl, void *stream)
+{
     float *part = static_cast<float *>(workspace);
 
     if (V && rope_dim == 0 && decode_gqa_supported(L->head_dim)) {
@@ -444,6 +476,47 @@ int kvq_attend_decode(const kvq_layout *L, const kvq_store *K, const kvq_store *
     a.part = part;
     a.out = out;
     return hip_status(launch_attend_generic(a, static_cast<hipStream_t>(stream)));
+}
+
+// Scratch of kvq_attend_decode_static: the split partials live in this
+// file-scope device array (one copy per GPU, held until the process ends).
+// Host code never uses its name as an address: the address of each
+// device's copy comes from hipGetSymbolAddress, taken once per device.
+constexpr size_t kStaticScratchBytes = (size_t)16 << 20;
+__device__ __align__(256) uint8_t scratch[kStaticScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices];
+
+// Address of the current device's scratch, or null on a HIP error.
+void *static_scratch()
+{
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void *ptr = nullptr;
+        if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return nullptr;
+        g_scratch_ptr[dev] = ptr;
+    }
+    return g_scratch_ptr[dev];
+}
+}  // namespace
+
+extern "C" {
+
+int kvq_attend_decode_static(const kvq_layout *L, const kvq_store *K, const kvq_store *V,
+                             const uint16_t *rope, int32_t rope_dim, const uint16_t *q,
+                             int32_t n_q_heads, float softmax_scale, float *out, void *stream)
+{
+    Plan pl;
+    int st = check_decode(L, K, V, rope, rope_dim, q, n_q_heads, softmax_scale, out, &pl);
+    if (st) return st;
+    if (pl.ws_bytes > kStaticScratchBytes) return KVQ_ENOSPC;
+    void *ws = static_scratch();
+    if (!ws) return KVQ_EHIP;
+    return attend_decode_impl(L, K, V, rope, rope_dim, q, n_q_heads, softmax_scale, out, ws, pl, stream);
 }
 
 namespace {
