@@ -159,6 +159,19 @@ int kvq_append(const kvq_layout *L, const kvq_store *K, const kvq_store *V,
                int32_t n_new, int32_t keep_recent,
                int32_t *n_blocks_out, int32_t *n_window_out, void *stream);
 
+/* The counts kvq_append leaves, computed on the host from host copies of
+ * the counts it starts from (the same window-roll rule and clamping, one
+ * definition shared with the append kernels), so a caller can keep host
+ * mirrors of the device counts without a device-to-host copy.
+ *   n_blocks, n_window  host int32 [n_seqs]: counts before the append
+ *                       (n_window may be NULL when window_cap == 0)
+ *   n_blocks_out, n_window_out  host int32 [n_seqs]; may alias the inputs
+ * Other arguments as for kvq_append with a layout of these capacities.
+ * Errors: KVQ_EINVAL, KVQ_EUNSUPPORTED. */
+int kvq_append_counts(int32_t n_seqs, int32_t max_blocks, int32_t window_cap, const int32_t *n_blocks,
+                      const int32_t *n_window, int32_t n_new, int32_t keep_recent, int32_t *n_blocks_out,
+                      int32_t *n_window_out);
+
 /* Restore (QKVShare injection path: rebuild 16-bit key/value rows).  For
  * every sequence a write dst[a][t][H][D] for t < 64*n_blocks[a] + n_window[a]:
  * dequantized blocks first (fma(code, scale, bias) in fp32, then rounded to

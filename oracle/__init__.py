@@ -17,11 +17,30 @@ import numpy as np
 HERE = os.path.dirname(os.path.abspath(__file__))
 SRC = os.path.join(HERE, "kvq_ref.c")
 LIB = os.path.join(HERE, "libkvq_ref.so")
+SAN_LIB = os.path.join(HERE, "libkvq_ref_san.so")
+# KVQ_ORACLE_LIB selects another build of the same source (the sanitized one
+# below, for the pin tests run under AddressSanitizer/UBSan).
+_LIB_OVERRIDE = os.environ.get("KVQ_ORACLE_LIB")
 
 # ISO C99 (so gcc does not contract a*b+c into an FMA), no fast-math,
 # OpenMP for the independent loops.
 CFLAGS = ["-std=c99", "-O2", "-ffp-contract=off", "-fno-fast-math", "-fopenmp",
           "-fPIC", "-shared", "-Wall", "-Wextra"]
+
+
+SAN_FLAGS = ["-std=c99", "-O1", "-g", "-fno-omit-frame-pointer", "-ffp-contract=off", "-fno-fast-math",
+             "-fopenmp", "-fPIC", "-shared", "-Wall", "-Wextra",
+             "-fsanitize=address,undefined", "-fno-sanitize-recover=all"]
+
+
+def build_sanitized() -> str:
+    """The same source with AddressSanitizer and UBSan (gcc), into
+    ``oracle/libkvq_ref_san.so``; loaded with KVQ_ORACLE_LIB and the ASan
+    runtime preloaded."""
+    tmp = SAN_LIB + ".tmp"
+    subprocess.check_call(["gcc", *SAN_FLAGS, SRC, "-o", tmp, "-lm"])
+    os.replace(tmp, SAN_LIB)
+    return SAN_LIB
 
 
 def build(force: bool = True) -> str:
@@ -39,9 +58,12 @@ _lib = None
 def lib() -> ctypes.CDLL:
     global _lib
     if _lib is None:
-        if not os.path.exists(LIB) or os.path.getmtime(LIB) < os.path.getmtime(SRC):
-            build(force=True)
-        L = ctypes.CDLL(LIB)
+        if _LIB_OVERRIDE:
+            L = ctypes.CDLL(_LIB_OVERRIDE)
+        else:
+            if not os.path.exists(LIB) or os.path.getmtime(LIB) < os.path.getmtime(SRC):
+                build(force=True)
+            L = ctypes.CDLL(LIB)
         P = ctypes.c_void_p
         i32, f32, u64, i64 = ctypes.c_int, ctypes.c_float, ctypes.c_uint64, ctypes.c_long
         L.kvq_ref_bf16_to_f32.argtypes = [ctypes.c_uint16]

@@ -24,7 +24,8 @@ KVQ_OK, KVQ_EINVAL, KVQ_ENOSPC, KVQ_EUNSUPPORTED, KVQ_EHIP = 0, -1, -2, -3, -4
 OUT_BF16, OUT_F32 = 0, 1
 WIDTHS = (2, 3, 4, 8)
 
-SYMBOLS = ("kvq_block_bytes", "kvq_quantize", "kvq_quantize_kv", "kvq_append", "kvq_dequantize", "kvq_card_bytes",
+SYMBOLS = ("kvq_block_bytes", "kvq_quantize", "kvq_quantize_kv", "kvq_append", "kvq_append_counts",
+           "kvq_dequantize", "kvq_card_bytes",
            "kvq_card_gather", "kvq_card_scatter", "kvq_block_sensitivity", "kvq_allocate_widths",
            "kvq_decode_workspace", "kvq_attend_decode", "kvq_attend_decode_static",
            "kvq_topk_workspace", "kvq_attend_decode_topk", "kvq_chunk_workspace", "kvq_attend_chunk",
@@ -69,6 +70,8 @@ def lib() -> ctypes.CDLL:
         L.kvq_quantize_kv.restype = ctypes.c_int
         L.kvq_append.argtypes = [P, P, P, P, P, P, P, i32, i32, i32, P, P, P]
         L.kvq_append.restype = ctypes.c_int
+        L.kvq_append_counts.argtypes = [i32, i32, i32, P, P, i32, i32, P, P]
+        L.kvq_append_counts.restype = ctypes.c_int
         u64 = ctypes.c_uint64
         L.kvq_card_bytes.argtypes = [i32, i32, i32, i32, i32, P, i32]
         L.kvq_card_bytes.restype = u64
@@ -314,13 +317,14 @@ class LayerCache:
         self._cur = nxt
         self._layout.n_blocks = self.n_blocks.data_ptr()
         self._layout.n_window = self.n_window.data_ptr()
-        for a in range(self.A):
-            nb, w = self.n_blocks_host[a], self.n_window_host[a]
-            total = w + n
-            k = (total - keep_recent) // 64 if total > keep_recent else 0
-            k = min(k, self.max_blocks - nb)
-            self.n_blocks_host[a] = nb + k
-            self.n_window_host[a] = min(total - 64 * k, self.window_cap)
+        # host mirrors: the library's own window-roll rule on the host copies
+        nbh = np.ascontiguousarray(self.n_blocks_host, dtype=np.int32)
+        nwh = np.ascontiguousarray(self.n_window_host, dtype=np.int32)
+        vp = lambda x: x.ctypes.data_as(ctypes.c_void_p)
+        _check(lib().kvq_append_counts(self.A, self.max_blocks, self.window_cap, vp(nbh), vp(nwh), n,
+                                       int(keep_recent), vp(nbh), vp(nwh)), "kvq_append_counts")
+        self.n_blocks_host[:] = [int(v) for v in nbh]
+        self.n_window_host[:] = [int(v) for v in nwh]
 
     # ---- CacheCards (one sequence as a safetensors-compatible file) --------
     def card_bytes(self, seq: int) -> int:

@@ -194,6 +194,31 @@ int kvq_quantize_kv(const kvq_layout *L, const kvq_store *K, const kvq_store *V,
     return quantize_call(L, K, V, k_src, v_src, src_seq_tokens, stream);
 }
 
+int kvq_append_counts(int32_t n_seqs, int32_t max_blocks, int32_t window_cap, const int32_t *n_blocks,
+                      const int32_t *n_window, int32_t n_new, int32_t keep_recent, int32_t *n_blocks_out,
+                      int32_t *n_window_out)
+{
+    if (n_seqs < 1 || max_blocks < 0 || window_cap < 0 || n_new < 0 || keep_recent < 0) return KVQ_EINVAL;
+    if (!n_blocks || !n_blocks_out || (window_cap > 0 && (!n_window || !n_window_out))) return KVQ_EINVAL;
+    if (window_cap > 0) {
+        if ((int64_t)keep_recent + 63 > window_cap) return KVQ_EINVAL;
+    } else if (keep_recent != 0 || n_new % 64 != 0) {
+        return KVQ_EINVAL;
+    }
+    if ((int64_t)window_cap + n_new > (int64_t)1 << 30) return KVQ_EUNSUPPORTED;
+    for (int32_t a = 0; a < n_seqs; a++) {
+        // the kernels' clamping of the device counts to the capacities
+        int nb = n_blocks[a] < 0 ? 0 : (n_blocks[a] > max_blocks ? max_blocks : n_blocks[a]);
+        int w = 0;
+        if (window_cap > 0) w = n_window[a] < 0 ? 0 : (n_window[a] > window_cap ? window_cap : n_window[a]);
+        int k = 0, w2 = 0;
+        append_counts(nb, w, n_new, keep_recent, max_blocks, window_cap, &k, &w2);
+        n_blocks_out[a] = nb + k;
+        if (window_cap > 0) n_window_out[a] = w2;
+    }
+    return KVQ_OK;
+}
+
 int kvq_append(const kvq_layout *L, const kvq_store *K, const kvq_store *V,
                const uint16_t *k_new, const uint16_t *v_new,
                uint16_t *rope, const uint16_t *rope_new, int32_t rope_dim,

@@ -96,6 +96,22 @@ struct ChunkArgs {
     float *out;                 // [A][n_new][Hq][D]
 };
 
+// Window roll of one sequence with nb blocks and W window tokens (already
+// clamped to the capacities) when n_new tokens arrive and keep recent ones
+// stay bf16: k new blocks are cut and W2 tokens remain in the window.  The
+// append kernels and kvq_append_counts share this one definition.
+__host__ __device__ inline void append_counts(int nb, int W, int n_new, int keep, int max_blocks, int window_cap,
+                                              int *k, int *W2)
+{
+    const int T = W + n_new;
+    int kk = T > keep ? (T - keep) / 64 : 0;
+    if (kk > max_blocks - nb) kk = max_blocks - nb;
+    int w2 = T - 64 * kk;
+    if (w2 > window_cap) w2 = window_cap;
+    *k = kk;
+    *W2 = w2;
+}
+
 // Append new tokens to the windows, quantizing every full 64-token block
 // that leaves the kept recent window.
 struct AppendArgs {

@@ -266,11 +266,7 @@ __device__ __forceinline__ void append_plan(const AppendArgs &p, int a, int &nb,
 {
     nb = seq_blocks(p.t, a);
     W = seq_window(p.t, a);
-    const int T = W + p.n_new;
-    k = T > p.keep ? (T - p.keep) / 64 : 0;
-    if (k > p.t.max_blocks - nb) k = p.t.max_blocks - nb;
-    W2 = T - 64 * k;
-    if (W2 > p.t.window_cap) W2 = p.t.window_cap;
+    append_counts(nb, W, p.n_new, p.keep, p.t.max_blocks, p.t.window_cap, &k, &W2);
 }
 
 // A 64-element slice (16-byte piece c of 8) of stream token t of head h:
