@@ -48,8 +48,10 @@ def parse():
     p.add_argument("--topk", type=int, default=0, metavar="K",
                    help="time top-K sparse decode (K of the T/64 blocks per agent, T = --topk-tokens) "
                         "on Llama 10-agent caches, beside the full decode, instead of the workload step")
-    p.add_argument("--topk-tokens", type=int, default=4096, metavar="T",
-                   help="cached tokens per agent for --topk (a multiple of 64)")
+    p.add_argument("--topk-tokens", type=int, default=0, metavar="T",
+                   help="cached tokens per agent for --topk (a multiple of 64; default 4096, 32768 with --topk-mla)")
+    p.add_argument("--topk-mla", action="store_true",
+                   help="--topk on the DeepSeek-V2-Lite latent shape (4 agents, 512-dim latent + 64 rope dims)")
     p.add_argument("--restore", action="store_true",
                    help="time the restore (dequantize to bf16) of the 32 768-token Q4 cache, K then V")
     p.add_argument("--alloc", action="store_true",
@@ -368,38 +370,48 @@ def append_bench(args):
 
 
 def topk_bench(args):
-    """Top-K sparse decode on the Llama-3.1-8B layer shape, 10 agents x T
-    Q4 tokens (T/64 blocks each, T = --topk-tokens, 4096 by default): block
-    scores over every K block, selection, then decode over the K kept blocks;
-    timed beside the full decode of the same caches.  Algorithmic bytes: all
-    K blocks (scores), the kept blocks' K and V again, q and out.  Cache
-    copies rotate past the 256 MB cache."""
+    """Top-K sparse decode, timed beside the full decode of the same caches.
+    Default shape: the Llama-3.1-8B layer, 10 agents x T Q4 tokens (T/64
+    blocks each, T = --topk-tokens, 4096 by default), K and V caches.  With
+    --topk-mla: the DeepSeek-V2-Lite latent shape, 4 agents x T tokens (T
+    defaults to 32768 there), one 512-dim Q4 latent head plus 64 bf16 rope
+    dims, 16 query heads (the block scores then run the generic scoring
+    kernel over latent and rope dims).  Algorithmic bytes per call: every
+    block's codes (and rope rows) for the scores, the kept blocks' codes (and
+    rope rows) again for the decode, q and out.  Cache copies rotate past the
+    256 MB cache."""
     import torch
     import kvq_synth as syn
     import quantized_kv_cache_group_amd as kvq
 
     kvq.lib()
     torch.cuda.set_device(0)
-    w = syn.workload(1)
-    A, H, D, Hq, K = w.n_agents, w.n_kv_heads, w.head_dim, w.n_q_heads, args.topk
-    T = args.topk_tokens
+    mla = args.topk_mla
+    w = syn.workload(4 if mla else 1)
+    A, H, D, Hq, K, R_ = w.n_agents, w.n_kv_heads, w.head_dim, w.n_q_heads, args.topk, w.rope_dim
+    T = args.topk_tokens if args.topk_tokens else (32768 if mla else 4096)
     if T < 64 or T % 64:
         print("--topk-tokens must be a positive multiple of 64", file=sys.stderr)
         sys.exit(2)
     nblk = T // 64
     blk = kvq.block_bytes(4, H, D)
-    one = 2 * A * nblk * blk
+    n_t = 1 if mla else 2
+    rope_tok = H * R_ * 2                            # rope bytes per token
+    one = A * nblk * (n_t * blk + 64 * rope_tok)
     R = min(12, max(2, int(np.ceil(2 * MALL_BYTES / one)) + 1))
-    caches = [kvq.LayerCache(H, D, [nblk] * A, [0] * A, None) for _ in range(R)]
+    caches = [kvq.LayerCache(H, D, [nblk] * A, [0] * A, None, latent=mla, rope_dim=R_) for _ in range(R)]
     g = torch.Generator(device="cuda")
     g.manual_seed(5)
     src = [torch.randn((A, T, H, D), generator=g, device="cuda").to(torch.bfloat16) for _ in range(2)]
     for i, c in enumerate(caches):
         c.quantize("k", src[i % 2])
-        c.quantize("v", src[(i + 1) % 2])
-    q = torch.randn((A, Hq, D), generator=g, device="cuda").to(torch.bfloat16)
+        if not mla:
+            c.quantize("v", src[(i + 1) % 2])
+        if c.rope is not None:
+            c.rope.normal_(generator=g)
+    q = torch.randn((A, Hq, D + R_), generator=g, device="cuda").to(torch.bfloat16)
     out = torch.empty((A, Hq, D), dtype=torch.float32, device="cuda")
-    ws = torch.zeros(max(caches[0].topk_workspace_bytes(Hq, K), caches[0].decode_workspace_bytes(Hq)),
+    ws = torch.empty(max(caches[0].topk_workspace_bytes(Hq, K), caches[0].decode_workspace_bytes(Hq)),
                      dtype=torch.uint8, device="cuda")
     stream = torch.cuda.current_stream()
 
@@ -420,18 +432,21 @@ def topk_bench(args):
     run(False, args.warmup)
     full_us = run(False, args.steps)
     kb = min(K, nblk)
-    algo = A * (nblk * blk + 2 * kb * blk) + A * Hq * D * 2 + A * Hq * D * 4
+    algo = (A * nblk * (blk + 64 * rope_tok)                   # scores: every block's K codes and rope rows
+            + A * kb * (n_t * blk + 64 * rope_tok)              # decode over the kept blocks
+            + A * Hq * (D + R_) * 2 + A * Hq * D * 4)
     gbs = algo / (sp_us * 1e-6) / 1e9
+    name = (f"deepseek-v2-lite-mla-4agent-{T}tok-q4-top{K}" if mla else f"llama8b-10agent-{T}tok-q4-top{K}")
     res = {"metric": "top-K sparse decode GB/s", "value": round(gbs, 2), "unit": "GB/s", "n_gpus": 1,
-           "steps": args.steps, "warmup": args.warmup, "higher_is_better": True, "dtype": "f32",
+           "steps": args.steps, "warmup": args.warmup, "higher_is_better": True, "dtype": "fp16 mfma, fp32 acc",
            "data": "synthetic",
-           "config": {"workload": f"llama8b-10agent-{T}tok-q4-top{K}", "agents": A, "q_heads": Hq,
-                      "kv_heads": H, "head_dim": D, "blocks": nblk, "top_k": K, "bits": 4, "rotated_copies": R},
+           "config": {"workload": name, "agents": A, "q_heads": Hq, "kv_heads": H, "head_dim": D,
+                      "rope_dim": R_, "blocks": nblk, "top_k": K, "bits": 4, "rotated_copies": R},
            "sparse_us": round(sp_us, 3), "full_decode_us": round(full_us, 3),
            "speedup_vs_full": round(full_us / sp_us, 3), "bytes_per_call": algo,
            "roofline": {"kernel": "kvq attend_decode_topk", "bound": "hbm", "achieved": round(gbs, 2),
                         "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
-                        "traffic": traffic_bytes("alloc", "kvq block_sensitivity")}}
+                        "traffic": None}}
     print(json.dumps(res), flush=True)
 
 

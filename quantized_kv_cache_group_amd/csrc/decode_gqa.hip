@@ -45,56 +45,6 @@ using namespace dev;
 constexpr int VT_PAD = 8;                  // LDS row padding (halves)
 constexpr int STEP = 32;                   // tokens per step
 
-// Lane q's share of one 64-dim group of a token row: chunks 2q and 2q+1 of
-// 8 codes (2B bytes at byte 2Bq of the group), held as NDW dwords.
-template <int B>
-struct GRow {
-    static constexpr bool ODD = (B == 3);                    // 6 bytes at offset 6q
-    static constexpr int NDW = ODD ? 2 : (2 * B) / 4;
-
-    __device__ static __forceinline__ void load(uint32_t *w, const uint8_t *grp, int q)
-    {
-        if constexpr (ODD) {
-            const uint32_t *p = reinterpret_cast<const uint32_t *>(grp + ((6 * q) & ~3));
-            w[0] = p[0];
-            w[1] = p[1];
-        } else if constexpr (B == 2) {
-            w[0] = reinterpret_cast<const uint32_t *>(grp)[q];
-        } else if constexpr (B == 4) {
-            const uint2 v = reinterpret_cast<const uint2 *>(grp)[q];
-            w[0] = v.x; w[1] = v.y;
-        } else {
-            const uint4 v = reinterpret_cast<const uint4 *>(grp)[q];
-            w[0] = v.x; w[1] = v.y; w[2] = v.z; w[3] = v.w;
-        }
-    }
-
-    // Exact codes of the lane's chunk u (0 or 1) as fp16 pairs.
-    __device__ static __forceinline__ Pairs chunk(const uint32_t *w, int q, int u)
-    {
-        if constexpr (B == 4) {
-            return Unpack<4>::run(w[u]);
-        } else if constexpr (B == 2) {
-            return Unpack<2>::run(u ? (w[0] >> 16) : (w[0] & 0xffffu));
-        } else if constexpr (B == 8) {
-            return Unpack<8>::run2(w[2 * u], w[2 * u + 1]);
-        } else {
-            const int o = ((6 * q) & 3) + 3 * u;               // o <= 5
-            return Unpack<3>::run3(o >= 4 ? w[1] : w[0], w[1], o & 3);
-        }
-    }
-};
-
-__device__ __forceinline__ h8 operand(const Pairs &pr)
-{
-    h8 v;
-    v[0] = pr.p[0][0]; v[1] = pr.p[0][1];
-    v[2] = pr.p[1][0]; v[3] = pr.p[1][1];
-    v[4] = pr.p[2][0]; v[5] = pr.p[2][1];
-    v[6] = pr.p[3][0]; v[7] = pr.p[3][1];
-    return v;
-}
-
 // Local token (0..31) of row m of S^T tile tau within a step: lane (head, q)
 // of the accumulator then holds tokens 8q + 4*tau + j.
 __device__ __forceinline__ int tile_token(int m, int tau) { return 8 * (m >> 2) + 4 * tau + (m & 3); }

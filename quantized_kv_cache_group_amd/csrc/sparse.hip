@@ -12,86 +12,131 @@
 // tables that the ordinary decode kernels then read; the bf16 window is
 // always active.
 #include "kvq_internal.h"
+#include "unpack.h"
 
 namespace kvq {
 namespace {
 
-__device__ __forceinline__ float bf16f(uint16_t h) { return __uint_as_float((uint32_t)h << 16); }
+using namespace dev;
 
-// Scores: one workgroup (4 waves) per (block j, sequence a); lane = token,
-// wave w takes the query heads h of each group with h % 4 == w.  The query
-// rows of one KV head's group are staged in LDS as fp32.
 constexpr int MAXQ = 16 * (512 + 64);                 // G <= 16 rows of D + rope <= 576
 
-__global__ __launch_bounds__(256) void block_scores(TopkArgs p)
+// Scores on matrix cores: one wave per (block j, sequence a) computes
+// S^T[key][head] for the block's 64 keys (four 16-key tiles) and the query
+// heads of every KV head, on exact codes: per 64-dim group g,
+// T_g = sum_{d in g} q_d c_d on v_mfma_f32_16x16x32_f16 (every 32-dim K-step
+// lies in one group), then sum_g (s_g T_g + b_g Q_g) in fp32 with the key's
+// (scale, bias) and Q_g the group's sum of the fp16 query; the rope dims
+// (bf16, exact in fp16) add two K-steps.  The block's score is the largest
+// over its keys and the heads, times the softmax scale.
+template <int B, int NG, int R>
+__device__ __forceinline__ float block_tiles(const TopkArgs &p, const uint8_t *blk, int a, int j, int g,
+                                             const h8 *qop, const float *qsum)
 {
-    __shared__ float qs[MAXQ];
-    __shared__ float wmax[4];
+    constexpr int CODE_ROW = 8 * NG * B, ND = GRow<B>::NDW;
+    const int lane = threadIdx.x, m = lane & 15, q = lane >> 4;
+    const int H = p.t.H;
+    const size_t rope_tokens = (size_t)64 * p.t.max_blocks + p.t.window_cap;
+    const uint32_t *meta = reinterpret_cast<const uint32_t *>(blk + (size_t)H * 64 * CODE_ROW);
+    float best = -INFINITY;
+#pragma unroll 1
+    for (int tau = 0; tau < 4; tau++) {
+        const int key = 16 * tau + m;                           // A operand row of this lane
+        const uint8_t *row = blk + ((size_t)g * 64 + key) * CODE_ROW;
+        f4 T[NG], Tr = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int gg = 0; gg < NG; gg++) {
+            uint32_t w[ND];
+            GRow<B>::load(w, row + 8 * B * gg, q);
+            f4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int u = 0; u < 2; u++)
+                acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(operand(GRow<B>::chunk(w, q, u)), qop[2 * gg + u], acc,
+                                                             0, 0, 0);
+            T[gg] = acc;
+        }
+        if constexpr (R > 0) {
+            const uint16_t *rr = p.rope + (((size_t)a * rope_tokens + (size_t)64 * j + key) * H + g) * R;
+#pragma unroll
+            for (int r = 0; r < R / 32; r++)
+                Tr = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+                    operand(bf16_pairs(*reinterpret_cast<const uint4 *>(rr + 32 * r + 8 * q))), qop[2 * NG + r], Tr, 0,
+                    0, 0);
+        }
+        // lane (head m, q) holds keys 16 tau + 4q + i, i = 0..3
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+            const uint32_t *km = meta + ((size_t)g * 64 + 16 * tau + 4 * q + i) * NG;
+            float sc = Tr[i];
+#pragma unroll
+            for (int gg = 0; gg < NG; gg++) {
+                const h2 sb = as_h2(km[gg]);
+                sc = __builtin_fmaf((float)sb[0], T[gg][i], __builtin_fmaf((float)sb[1], qsum[gg], sc));
+            }
+            best = fmaxf(best, sc);
+        }
+    }
+    return best;
+}
+
+template <int NG, int R>
+__global__ __launch_bounds__(64) void block_scores_mfma(TopkArgs p)
+{
+    constexpr int D = 64 * NG, KS = 2 * NG + R / 32;
     const int j = blockIdx.x, a = blockIdx.y;
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int H = p.t.H, D = p.t.D, R = p.rope_dim, Dk = D + R, G = p.G;
+    const int lane = threadIdx.x, m = lane & 15, q = lane >> 4;
+    const int H = p.t.H, G = p.G;
     int nb = p.t.n_blocks[a];
     nb = nb < 0 ? 0 : (nb > p.t.max_blocks ? p.t.max_blocks : nb);
-    if (j >= p.t.max_blocks) return;
     if (j >= nb) {
-        if (threadIdx.x == 0) p.scores[(size_t)a * p.t.max_blocks + j] = -INFINITY;
+        if (lane == 0) p.scores[(size_t)a * p.t.max_blocks + j] = -INFINITY;
         return;
     }
     const size_t e = (size_t)a * p.t.max_blocks + j;
     const int B = p.t.bits[e];
     const uint8_t *blk = p.k.pool + p.k.offset[e];
-    const int code_row = D * B / 8, NG = D / 64;
-    const size_t rope_tokens = (size_t)64 * p.t.max_blocks + p.t.window_cap;
+    const h2 ones = {(_Float16)1.0f, (_Float16)1.0f};
     float best = -INFINITY;
     for (int g = 0; g < H; g++) {
-        __syncthreads();                               // previous group's rows are consumed
-        for (int i = threadIdx.x; i < G * Dk; i += 256)
-            qs[i] = bf16f(p.q[((size_t)a * p.Hq + (size_t)g * G) * Dk + i]);
-        __syncthreads();
-        float acc[4] = {0.f, 0.f, 0.f, 0.f};          // heads wave, wave+4, wave+8, wave+12
-        const uint32_t *row = reinterpret_cast<const uint32_t *>(blk + ((size_t)g * 64 + lane) * code_row);
-        const uint32_t *meta = reinterpret_cast<const uint32_t *>(blk + (size_t)H * 64 * code_row) +
-                               ((size_t)g * 64 + lane) * NG;
+        // the G query rows of KV head g as B operands (heads past G are zero)
+        const bool hv = m < G;
+        const uint16_t *qrow = p.q + ((size_t)a * p.Hq + (size_t)g * G + (hv ? m : 0)) * (D + R);
+        h8 qop[KS];
+        float qsum[NG];
+#pragma unroll
         for (int gg = 0; gg < NG; gg++) {
-            const uint32_t m = meta[gg];
-            const float s = (float)__builtin_bit_cast(_Float16, (uint16_t)(m & 0xffff));
-            const float b = (float)__builtin_bit_cast(_Float16, (uint16_t)(m >> 16));
-            const uint32_t *w = row + gg * 2 * B;      // the group's 2B code words
-            for (int i = 0; i < 64; i++) {
-                const int bit = B * i, wi = bit >> 5, sh = bit & 31;
-                uint32_t c = w[wi] >> sh;
-                if (sh + B > 32) c |= w[wi + 1] << (32 - sh);
-                c &= (1u << B) - 1u;
-                const float k = __builtin_fmaf((float)c, s, b);    // restored key value
-                const int d = 64 * gg + i;
+            float qs = 0.0f;
 #pragma unroll
-                for (int r = 0; r < 4; r++) {
-                    const int h = wave + 4 * r;
-                    if (h < G) acc[r] = __builtin_fmaf(qs[h * Dk + d], k, acc[r]);
-                }
-            }
-        }
-        if (R) {
-            const uint16_t *rr = p.rope + (((size_t)a * rope_tokens + (size_t)64 * j + lane) * H + g) * R;
-            for (int d = 0; d < R; d++) {
-                const float k = bf16f(rr[d]);
+            for (int u = 0; u < 2; u++) {
+                const int c = 8 * gg + 2 * q + u;
+                h8 o = operand(bf16_pairs(*reinterpret_cast<const uint4 *>(qrow + 8 * c)));
+                if (!hv) o = h8{0, 0, 0, 0, 0, 0, 0, 0};
+                qop[2 * gg + u] = o;
 #pragma unroll
-                for (int r = 0; r < 4; r++) {
-                    const int h = wave + 4 * r;
-                    if (h < G) acc[r] = __builtin_fmaf(qs[h * Dk + D + d], k, acc[r]);
-                }
+                for (int i = 0; i < 4; i++) qs = __builtin_amdgcn_fdot2(h2{o[2 * i], o[2 * i + 1]}, ones, qs, false);
             }
+            qs += __shfl_xor(qs, 16);
+            qs += __shfl_xor(qs, 32);
+            qsum[gg] = qs;
         }
 #pragma unroll
-        for (int r = 0; r < 4; r++)
-            if (wave + 4 * r < G) best = fmaxf(best, p.scale * acc[r]);
+        for (int r = 0; r < R / 32; r++) {
+            h8 o = operand(bf16_pairs(*reinterpret_cast<const uint4 *>(qrow + D + 32 * r + 8 * q)));
+            if (!hv) o = h8{0, 0, 0, 0, 0, 0, 0, 0};
+            qop[2 * NG + r] = o;
+        }
+        float t;
+        switch (B) {
+        case 2: t = block_tiles<2, NG, R>(p, blk, a, j, g, qop, qsum); break;
+        case 3: t = block_tiles<3, NG, R>(p, blk, a, j, g, qop, qsum); break;
+        case 4: t = block_tiles<4, NG, R>(p, blk, a, j, g, qop, qsum); break;
+        default: t = block_tiles<8, NG, R>(p, blk, a, j, g, qop, qsum); break;
+        }
+        if (hv) best = fmaxf(best, t);
     }
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) best = fmaxf(best, __shfl_xor(best, o));
-    if (lane == 0) wmax[wave] = best;
-    __syncthreads();
-    if (threadIdx.x == 0)
-        p.scores[e] = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));
+    if (lane == 0) p.scores[e] = p.scale * best;
 }
 
 // Selection: one workgroup per sequence.  Block i is kept when fewer than
@@ -350,7 +395,31 @@ hipError_t launch_topk_select(const TopkArgs &p, const DecodeArgs *g4, hipStream
         if (g4) {                                     // per KV head, from the decode's own products
             e = launch_g4_scores(*g4, p.scale, p.scores, s);
         } else {
-            block_scores<<<dim3(p.t.max_blocks, p.t.A), 256, 0, s>>>(p);
+            const dim3 grid(p.t.max_blocks, p.t.A);
+            const int ng = p.t.D / 64;
+            if (p.rope_dim == 0) {
+                switch (ng) {
+                case 1: block_scores_mfma<1, 0><<<grid, 64, 0, s>>>(p); break;
+                case 2: block_scores_mfma<2, 0><<<grid, 64, 0, s>>>(p); break;
+                case 3: block_scores_mfma<3, 0><<<grid, 64, 0, s>>>(p); break;
+                case 4: block_scores_mfma<4, 0><<<grid, 64, 0, s>>>(p); break;
+                case 5: block_scores_mfma<5, 0><<<grid, 64, 0, s>>>(p); break;
+                case 6: block_scores_mfma<6, 0><<<grid, 64, 0, s>>>(p); break;
+                case 7: block_scores_mfma<7, 0><<<grid, 64, 0, s>>>(p); break;
+                default: block_scores_mfma<8, 0><<<grid, 64, 0, s>>>(p); break;
+                }
+            } else {
+                switch (ng) {
+                case 1: block_scores_mfma<1, 64><<<grid, 64, 0, s>>>(p); break;
+                case 2: block_scores_mfma<2, 64><<<grid, 64, 0, s>>>(p); break;
+                case 3: block_scores_mfma<3, 64><<<grid, 64, 0, s>>>(p); break;
+                case 4: block_scores_mfma<4, 64><<<grid, 64, 0, s>>>(p); break;
+                case 5: block_scores_mfma<5, 64><<<grid, 64, 0, s>>>(p); break;
+                case 6: block_scores_mfma<6, 64><<<grid, 64, 0, s>>>(p); break;
+                case 7: block_scores_mfma<7, 64><<<grid, 64, 0, s>>>(p); break;
+                default: block_scores_mfma<8, 64><<<grid, 64, 0, s>>>(p); break;
+                }
+            }
             e = hipGetLastError();
         }
         if (e != hipSuccess) return e;
