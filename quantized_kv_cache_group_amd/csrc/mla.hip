@@ -343,43 +343,56 @@ __global__ __launch_bounds__(512, 1) void mla_split(DecodeArgs p, const uint16_t
         }
     }
 
-    // Combine the four key groups: (m, l) per head and O^T rows per head in
-    // stored-position order, 4 positions per 16-byte write (the row pitch of
-    // OB floats keeps eight heads' writes on distinct banks).
-    constexpr int OB = DL + 4;
-    static_assert((128 + 4 * 16 * OB) * 4 <= 2 * C::BUF * 2, "combine buffer exceeds the tile buffers");
+    // Combine the four key groups: wave (kg, dh) writes its 16 O^T tiles as
+    // they sit in its registers ([tile][lane] 16-byte units), the dh = 0
+    // waves their (m, l); after one barrier wave (kg, dh) sums tiles
+    // 4kg..+3 of its dim half over the four key groups, rescaled to the
+    // common max per head, and writes them to the partial rows (lane (h, kq)
+    // holds stored positions 256dh + 16t + 4kq..+3 of head h).
+    constexpr int TB = OT * 64 * 16;                       // one wave's tiles (bytes)
+    static_assert(8 * TB + 128 * 4 <= 2 * C::BUF * 2, "combine buffer exceeds the tile buffers");
     float l = w.l_run + __shfl_xor(w.l_run, 16);
     l += __shfl_xor(l, 32);
-    float *ml = reinterpret_cast<float *>(lds);           // [4][2][16]
-    float *ob = ml + 128;                                  // [4][16][OB]
+    uint8_t *cbuf = reinterpret_cast<uint8_t *>(lds);
+    float *ml = reinterpret_cast<float *>(cbuf + 8 * TB);   // m [4][16], l [4][16]
+#pragma unroll
+    for (int t = 0; t < OT; t++) *reinterpret_cast<f4 *>(cbuf + wave * TB + (t * 64 + lane) * 16) = w.acc[t];
     if (kq == 0 && dh == 0) {
-        ml[(kg * 2) * 16 + m] = w.m_run;
-        ml[(kg * 2 + 1) * 16 + m] = l;
+        ml[kg * 16 + m] = w.m_run;
+        ml[64 + kg * 16 + m] = l;
     }
-    float *orow = ob + (kg * 16 + m) * OB + 256 * dh + 4 * kq;
-#pragma unroll
-    for (int t = 0; t < OT; t++) *reinterpret_cast<f4 *>(orow + 16 * t) = w.acc[t];
     __syncthreads();
-    // one head's (m, l, acc[512]) per 514 consecutive threads, so the
-    // partial rows are written contiguously
+    float fu[4];
+    float M = -INFINITY;
+#pragma unroll
+    for (int u = 0; u < 4; u++) M = fmaxf(M, ml[u * 16 + m]);
+    float L = 0.0f;
+#pragma unroll
+    for (int u = 0; u < 4; u++) {
+        const float mu = ml[u * 16 + m];
+        fu[u] = (mu == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(mu - M);
+        L += fu[u] * ml[64 + u * 16 + m];
+    }
     const int stride = DL + 2;
-    for (int i = tid; i < p.Hq * stride; i += 512) {
-        const int h = i / stride, d = i - h * stride;      // d: 0 m, 1 l, 2.. acc (true dims)
-        float M = -INFINITY;
+    float *prow = p.part + ((size_t)(a * p.Hq + m) * p.n_splits + s) * stride;
 #pragma unroll
-        for (int u = 0; u < 4; u++) M = fmaxf(M, ml[(u * 2) * 16 + h]);
-        float v = M;
-        if (d > 0) {
-            const int k = d - 2, pos = (k & ~7) | ((k & 3) << 1) | ((k >> 2) & 1);   // stored position of dim k
-            v = 0.0f;
+    for (int tt = 0; tt < 4; tt++) {
+        const int t = 4 * kg + tt;
+        f4 v = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int u = 0; u < 4; u++) {
-                const float mu = ml[(u * 2) * 16 + h];
-                const float f = (mu == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(mu - M);
-                v += f * (d == 1 ? ml[(u * 2 + 1) * 16 + h] : ob[(u * 16 + h) * OB + pos]);
+        for (int u = 0; u < 4; u++) v += fu[u] * *reinterpret_cast<const f4 *>(cbuf + (4 * dh + u) * TB + (t * 64 + lane) * 16);
+        if (hv) {
+#pragma unroll
+            for (int r = 0; r < 4; r++) {
+                const int pos = 256 * dh + 16 * t + 4 * kq + r;            // stored position -> dim
+                const int dim = (pos & ~7) | ((pos >> 1) & 3) | ((pos & 1) << 2);
+                prow[2 + dim] = v[r];
             }
         }
-        p.part[((size_t)(a * p.Hq + h) * p.n_splits + s) * stride + d] = v;
+    }
+    if (wave == 0 && kq == 0 && hv) {
+        prow[0] = M;
+        prow[1] = L;
     }
 }
 
