@@ -277,6 +277,32 @@ __device__ __forceinline__ void tile_compute(MlaState<R> &w, const _Float16 *kh,
     }
 }
 
+// Query chunks loaded by stage's lanes (chunk tid + 512 i = head, K-step,
+// quarter) into LDS in operand form, and each lane's operands back.
+template <int R>
+__device__ __forceinline__ void stage_query(_Float16 *qs, const uint4 (&qv)[(16 * MCfg<R>::KS * 4 + 511) / 512])
+{
+    constexpr int QCH = 16 * MCfg<R>::KS * 4, QPL = (QCH + 511) / 512;
+#pragma unroll
+    for (int i = 0; i < QPL; i++) {
+        const int ch = threadIdx.x + 512 * i;
+        if (ch < QCH) *reinterpret_cast<h8 *>(qs + 8 * ch) = row_order(bf16_pairs(qv[i]));
+    }
+}
+
+template <int R>
+__device__ __forceinline__ void load_query(MlaState<R> &w, const _Float16 *qs, bool hv)
+{
+    constexpr int KS = MCfg<R>::KS;
+    const int lane = threadIdx.x & 63, m = lane & 15, kq = lane >> 4;
+#pragma unroll
+    for (int k = 0; k < KS; k++) {
+        h8 o = *reinterpret_cast<const h8 *>(qs + 8 * ((m * KS + k) * 4 + kq));
+        if (!hv) o = h8{0, 0, 0, 0, 0, 0, 0, 0};
+        w.qop[k] = o;
+    }
+}
+
 template <int R>
 __global__ __launch_bounds__(512, 1) void mla_split(DecodeArgs p, const uint16_t *rope, int64_t rope_tokens)
 {
@@ -299,12 +325,20 @@ __global__ __launch_bounds__(512, 1) void mla_split(DecodeArgs p, const uint16_t
 
     MlaState<R> w;
     const bool hv = m < p.Hq;
-    const uint16_t *qrow = p.q + ((size_t)a * p.Hq + (hv ? m : 0)) * C::DK;
+    // The query rows once per workgroup: 16 heads x KS K-steps x 4 lane
+    // quarters of 8 dims, as fp16 operand chunks, into the second tile buffer
+    // (unused until tile 1 is stored); each wave then reads its operands from
+    // LDS instead of every wave fetching all rows.  The loads go out before the
+    // first tiles' loads, the LDS stores after them.
+    constexpr int QCH = 16 * C::KS * 4, QPL = (QCH + 511) / 512;
+    _Float16 *qs = lds + C::BUF;
+    uint4 qv[QPL];
 #pragma unroll
-    for (int k = 0; k < C::KS; k++) {
-        h8 o = row_order(bf16_pairs(*reinterpret_cast<const uint4 *>(qrow + 32 * k + 8 * kq)));
-        if (!hv) o = h8{0, 0, 0, 0, 0, 0, 0, 0};
-        w.qop[k] = o;
+    for (int i = 0; i < QPL; i++) {
+        const int ch = tid + 512 * i, h = ch / (4 * C::KS), k = (ch >> 2) % C::KS, q4 = ch & 3;
+        qv[i] = uint4{0, 0, 0, 0};
+        if (ch < QCH && h < p.Hq)
+            qv[i] = *reinterpret_cast<const uint4 *>(p.q + ((size_t)a * p.Hq + h) * C::DK + 32 * k + 8 * q4);
     }
 #pragma unroll
     for (int t = 0; t < OT; t++) w.acc[t] = f4{0.f, 0.f, 0.f, 0.f};
@@ -318,6 +352,10 @@ __global__ __launch_bounds__(512, 1) void mla_split(DecodeArgs p, const uint16_t
         MlaRaw raw, raw1;
         load_block<R>(raw, mm, p, rope, rope_tokens, a, j0, j1);
         if (n > 1) load_block<R>(raw1, mm, p, rope, rope_tokens, a, j0 + 1, j1);
+        stage_query<R>(qs, qv);
+        __syncthreads();
+        load_query<R>(w, qs, hv);
+        __syncthreads();
         store_raw<R>(raw, lds);
         if (n > 1) raw = raw1;
         __syncthreads();
@@ -335,6 +373,10 @@ __global__ __launch_bounds__(512, 1) void mla_split(DecodeArgs p, const uint16_t
             __syncthreads();
         }
     } else {
+        stage_query<R>(qs, qv);
+        __syncthreads();
+        load_query<R>(w, qs, hv);
+        __syncthreads();
         for (int w0 = 0; w0 < nw; w0 += TILE) {
             store_window<R>(p, rope, rope_tokens, a, nb, nw, w0, lds);
             __syncthreads();

@@ -68,6 +68,37 @@ def test_decode_more_sequences_than_a_wave():
     close(got, ref_decode(b, q, 0.125), what="70 sequences")
 
 
+def test_decode_many_sequences_one_split_each():
+    """300 sequences x 16 KV heads of 0..4 blocks with windows: more splits
+    than resident workgroups, so the balanced split plan gives each sequence
+    one block split and one window split; the plan's scans over sequences
+    run in five chunks of 64."""
+    rng = np.random.default_rng(300)
+    H, D, G, A = 16, 64, 2, 300
+    nb = [int(v) for v in rng.integers(0, 5, size=A)]
+    window = [int(v) for v in rng.integers(1, 64, size=A)]
+    lengths = [64 * n + w for n, w in zip(nb, window)]
+    bits = [rng.choice(np.array([2, 3, 4, 8], np.uint8), size=n) for n in nb]
+    b = build(H, D, lengths, bits=bits, window=window, seed=300)
+    q = syn.random_normal_bf16((A, G * H, D), 19)
+    close(_decode(b, q, 0.125), ref_decode(b, q, 0.125), what="300 sequences")
+
+
+def test_decode_long_sequence_among_short():
+    """One 1 200-block sequence among 30 of 0..3 blocks, one KV head: the
+    balanced plan's splits are a few blocks long, at least ceil(1200 / 511)
+    so that no row has more than 512 splits to merge."""
+    rng = np.random.default_rng(1200)
+    H, D, G = 1, 128, 4
+    nb = [1200] + [int(v) for v in rng.integers(0, 4, size=30)]
+    window = [17] + [int(v) for v in rng.integers(0, 80, size=30)]
+    lengths = [64 * n + w for n, w in zip(nb, window)]
+    bits = [rng.choice(np.array([2, 3, 4, 8], np.uint8), size=n) for n in nb]
+    b = build(H, D, lengths, bits=bits, window=window, seed=1200)
+    q = syn.random_normal_bf16((len(nb), G * H, D), 20)
+    close(_decode(b, q, D ** -0.5), ref_decode(b, q, D ** -0.5), what="long among short")
+
+
 def test_decode_long_window():
     """A 9 000-token bf16 window: more than 128 rounds of 64 tokens, so each
     window split takes 128 tokens."""
