@@ -278,15 +278,17 @@ __device__ __forceinline__ void tile_compute(MlaState<R> &w, const _Float16 *kh,
 }
 
 // Query chunks loaded by stage's lanes (chunk tid + 512 i = head, K-step,
-// quarter) into LDS in operand form, and each lane's operands back.
+// quarter) into LDS in operand form, and each lane's operands back.  A head's
+// 4 KS chunks sit 4 KS + 1 chunks apart, so the 16 heads a read serves start
+// on 16 different 4-bank groups (no bank conflicts).
 template <int R>
 __device__ __forceinline__ void stage_query(_Float16 *qs, const uint4 (&qv)[(16 * MCfg<R>::KS * 4 + 511) / 512])
 {
-    constexpr int QCH = 16 * MCfg<R>::KS * 4, QPL = (QCH + 511) / 512;
+    constexpr int HC = MCfg<R>::KS * 4, QCH = 16 * HC, QPL = (QCH + 511) / 512;
 #pragma unroll
     for (int i = 0; i < QPL; i++) {
         const int ch = threadIdx.x + 512 * i;
-        if (ch < QCH) *reinterpret_cast<h8 *>(qs + 8 * ch) = row_order(bf16_pairs(qv[i]));
+        if (ch < QCH) *reinterpret_cast<h8 *>(qs + 8 * (ch + ch / HC)) = row_order(bf16_pairs(qv[i]));
     }
 }
 
@@ -297,7 +299,7 @@ __device__ __forceinline__ void load_query(MlaState<R> &w, const _Float16 *qs, b
     const int lane = threadIdx.x & 63, m = lane & 15, kq = lane >> 4;
 #pragma unroll
     for (int k = 0; k < KS; k++) {
-        h8 o = *reinterpret_cast<const h8 *>(qs + 8 * ((m * KS + k) * 4 + kq));
+        h8 o = *reinterpret_cast<const h8 *>(qs + 8 * (m * (4 * KS + 1) + 4 * k + kq));
         if (!hv) o = h8{0, 0, 0, 0, 0, 0, 0, 0};
         w.qop[k] = o;
     }
@@ -423,13 +425,17 @@ __global__ __launch_bounds__(512, 1) void mla_split(DecodeArgs p, const uint16_t
         f4 v = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int u = 0; u < 4; u++) v += fu[u] * *reinterpret_cast<const f4 *>(cbuf + (4 * dh + u) * TB + (t * 64 + lane) * 16);
+        // stored positions 8c..8c+7 hold dims 8c + (0 4 1 5 2 6 3 7): lanes kq
+        // and kq ^ 1 (16 lanes apart) trade two values so that the even one
+        // holds dims 8c..8c+3 and the odd one 8c+4..8c+7, written as two
+        // 8-byte stores (a partial row starts 8-byte aligned)
+        const bool odd = kq & 1;
+        const float y0 = __shfl_xor(odd ? v[0] : v[1], 16), y1 = __shfl_xor(odd ? v[2] : v[3], 16);
         if (hv) {
-#pragma unroll
-            for (int r = 0; r < 4; r++) {
-                const int pos = 256 * dh + 16 * t + 4 * kq + r;            // stored position -> dim
-                const int dim = (pos & ~7) | ((pos >> 1) & 3) | ((pos & 1) << 2);
-                prow[2 + dim] = v[r];
-            }
+            const int d0 = 256 * dh + 16 * t + 8 * (kq >> 1) + 4 * odd;
+            float2 *dst = reinterpret_cast<float2 *>(prow + 2 + d0);
+            dst[0] = odd ? float2{y0, y1} : float2{v[0], v[2]};
+            dst[1] = odd ? float2{v[1], v[3]} : float2{y0, y1};
         }
     }
     if (wave == 0 && kq == 0 && hv) {
