@@ -88,8 +88,9 @@ TRAFFIC = {
                                23481.7 + 2656.4, 5440.0 + 160.0),
     (2, "kvq attend_decode"): (("decode_g4.hip", "decode_gqa.hip"), "f633df87aab3ffcf",
                                64375.4 + 2256.5, 4488.0 + 128.0),
-    (4, "kvq attend_decode"): (("mla.hip", "decode_gqa.hip"), "360edc36c8959476",
-                               27114.2 + 4169.3, 10953.8 + 128.0),
+    (4, "kvq quantize"): (("quantize.hip",), "7dbb68a3958abdc3", 65779.2, 36881.8),
+    (4, "kvq attend_decode"): (("mla.hip", "decode_gqa.hip"), "bf375907107cbd5a",
+                               27101.0 + 4169.1, 10792.0 + 128.0),
     ("alloc", "kvq block_sensitivity"): (("alloc.hip",), "daa276e1c505e00b", 430498.4, 62.0),
 }
 
@@ -378,7 +379,7 @@ def append_bench(args):
            "bytes_per_call": round(total / args.steps),
            "roofline": {"kernel": "kvq append", "bound": "hbm", "achieved": round(gbs, 2),
                         "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
-                        "traffic": traffic_bytes("alloc", "kvq block_sensitivity")}}
+                        "traffic": None}}
     print(json.dumps(res), flush=True)
 
 

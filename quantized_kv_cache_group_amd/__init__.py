@@ -219,6 +219,7 @@ class LayerCache:
         dev = torch.device(device)
         # two sets of device counts: append writes the other set and then
         # makes it current, so its kernels never overwrite counts they read
+        self._counts_c = ((ctypes.c_int32 * max(A, 1))(), (ctypes.c_int32 * max(A, 1))())
         self._nb_buf = [torch.tensor(self.n_blocks_host, dtype=torch.int32, device=dev) for _ in range(2)]
         self._nw_buf = [torch.tensor(self.n_window_host, dtype=torch.int32, device=dev) for _ in range(2)]
         self._cur = 0
@@ -318,13 +319,15 @@ class LayerCache:
         self._layout.n_blocks = self.n_blocks.data_ptr()
         self._layout.n_window = self.n_window.data_ptr()
         # host mirrors: the library's own window-roll rule on the host copies
-        nbh = np.ascontiguousarray(self.n_blocks_host, dtype=np.int32)
-        nwh = np.ascontiguousarray(self.n_window_host, dtype=np.int32)
-        vp = lambda x: x.ctypes.data_as(ctypes.c_void_p)
-        _check(lib().kvq_append_counts(self.A, self.max_blocks, self.window_cap, vp(nbh), vp(nwh), n,
-                                       int(keep_recent), vp(nbh), vp(nwh)), "kvq_append_counts")
-        self.n_blocks_host[:] = [int(v) for v in nbh]
-        self.n_window_host[:] = [int(v) for v in nwh]
+        # (through two preallocated int32 arrays: no per-call numpy or
+        # pointer objects)
+        nbh, nwh = self._counts_c
+        nbh[:] = self.n_blocks_host
+        nwh[:] = self.n_window_host
+        _check(lib().kvq_append_counts(self.A, self.max_blocks, self.window_cap, nbh, nwh, n,
+                                       int(keep_recent), nbh, nwh), "kvq_append_counts")
+        self.n_blocks_host[:] = nbh[:]
+        self.n_window_host[:] = nwh[:]
 
     # ---- CacheCards (one sequence as a safetensors-compatible file) --------
     def card_bytes(self, seq: int) -> int:
