@@ -1,21 +1,27 @@
 #!/usr/bin/env python3
 """Benchmark of the quantized KV-cache hot path on one MI355X.
 
-One step = the whole path over one batch of synthetic input: quantize every
-K and V cache of the workload (kvq_quantize_kv: one launch per layer), then attend over the packed
-blocks (kvq_attend_decode, or kvq_attend_chunk for the restore + chunk
-workload).  Inputs are resident in HBM before timing; cache copies rotate
-so that no step reads what the 256 MB Infinity Cache still holds from the
-previous steps.
+One step = one batched decode step over packed caches written beforehand:
+the attention call (kvq_attend_decode: split + merge launches) of every
+layer of the workload over all agents, or one chunk call (kvq_attend_chunk)
+for the restore + chunk workload.  Cache copies rotate so that at least
+2 x 256 MB of other copies pass between two reads of one (the Infinity
+Cache holds nothing a call can use); every copy is visited once before the
+warmup.  The K timed steps run back to back between one pair of HIP events
+on the launch stream (eager launches, or with --graph one replay of their
+captured HIP graph, checked against an eager step).
 
-Prints one JSON line.  `value` is the whole step's algorithmic bytes (bf16
-read + codes/metadata written by quantize; codes, metadata, bf16 window,
-rope, queries and outputs of attention) divided by the step time, in GB/s.
-`roofline` is for the dominant kernel (largest share of the step time), from
-per-launch HIP event timing on the launch stream.  `cpu_baseline` times the
-C oracle on a bounded sample of the same workload on the host cores.
+Prints one JSON line.  `value` is the step's algorithmic attention bytes
+(codes and scale/bias of the blocks, bf16 windows, rope rows, queries and
+outputs) divided by the step time, in GB/s; `roofline` is for that call.
+The quantize launch that builds a layer's K and V caches (kvq_quantize_kv)
+is timed the same way on its own and reported as `quantize_GBps` with
+`roofline_quantize`.  `cpu_baseline` times the C oracle on a bounded sample
+of the same workload on the host cores.
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 1]
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 2] [--graph]
+Side modes (one JSON line each): --restore, --append N, --card, --topk K,
+--alloc, --copy-calibration.
 """
 from __future__ import annotations
 
