@@ -315,15 +315,13 @@ __global__ __launch_bounds__(512, 1) void mla_split(DecodeArgs p, const uint16_t
     const int tid = threadIdx.x, lane = tid & 63, m = lane & 15, kq = lane >> 4;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int kg = wave & 3, dh = wave >> 2;
-    const int nb = seq_blocks(p.t, a), nw = seq_window(p.t, a);
-    const int nsb = (nb + p.SB - 1) / p.SB;
-    const bool win = (s == nsb) && nw > 0;
-    if (s > nsb || (s == nsb && !win)) return;
-
-    // the split's block table first, so its loads overlap the query loads
+    // The split's block table and the query rows do not depend on the
+    // sequence's counts: their loads go out with the count loads (table
+    // entries up to the split's end within max_blocks are valid memory;
+    // those past n_blocks are never used).  Block data waits for the counts.
     MlaMeta mm;
     mm.base = -(1 << 20);
-    if (!win) mla_meta(mm, p, a, s * p.SB, min(s * p.SB + p.SB, nb));
+    if (s * p.SB < p.t.max_blocks) mla_meta(mm, p, a, s * p.SB, min(s * p.SB + p.SB, p.t.max_blocks));
 
     MlaState<R> w;
     const bool hv = m < p.Hq;
@@ -346,6 +344,11 @@ __global__ __launch_bounds__(512, 1) void mla_split(DecodeArgs p, const uint16_t
     for (int t = 0; t < OT; t++) w.acc[t] = f4{0.f, 0.f, 0.f, 0.f};
     w.m_run = -INFINITY;
     w.l_run = 0.0f;
+
+    const int nb = seq_blocks(p.t, a), nw = seq_window(p.t, a);
+    const int nsb = (nb + p.SB - 1) / p.SB;
+    const bool win = (s == nsb) && nw > 0;
+    if (s > nsb || (s == nsb && !win)) return;
 
     if (!win) {
         // Tile j in buffer j&1; between barriers the tile j+1 is stored into
