@@ -737,6 +737,44 @@ __global__ __launch_bounds__(256) void chunk_merge(ChunkArgs p)
     const int ns = (lim + TILE * p.split_tiles - 1) / (TILE * p.split_tiles);
     const size_t stride = (size_t)(D + 2);
     const float *pr = p.part + row * p.n_splits * stride;
+    if (ns <= 8) {
+        // Up to 8 splits: every split's (max, sum) (lane s) and the lane's
+        // dims of every split are loaded before the first use, so the row
+        // costs one memory round trip.
+        float mv = -INFINITY, lv = 0.0f;
+        if (lane < ns) {
+            mv = pr[lane * stride];
+            lv = pr[lane * stride + 1];
+        }
+        float v[8][4];
+#pragma unroll
+        for (int s = 0; s < 8; s++)
+#pragma unroll
+            for (int k = 0; k < 4; k++)
+                v[s][k] = (s < ns && 64 * k + lane < D) ? pr[s * stride + 2 + 64 * k + lane] : 0.0f;
+        float M = mv;
+#pragma unroll
+        for (int x = 32; x > 0; x >>= 1) M = fmaxf(M, __shfl_xor(M, x));
+        const float wgt = (lane < ns && M > -INFINITY) ? __builtin_amdgcn_exp2f(mv - M) : 0.0f;
+        float L = wgt * lv;
+#pragma unroll
+        for (int x = 32; x > 0; x >>= 1) L += __shfl_xor(L, x);
+        const float inv = L > 0.0f ? 1.0f / L : 0.0f;
+        float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int s = 0; s < 8; s++) {
+            if (s < ns) {
+                const float ws = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, wgt), s));
+#pragma unroll
+                for (int k = 0; k < 4; k++) acc[k] = __builtin_fmaf(ws, v[s][k], acc[k]);
+            }
+        }
+        float *o = p.out + row * D;
+#pragma unroll
+        for (int k = 0; k < 4; k++)
+            if (64 * k + lane < D) o[64 * k + lane] = acc[k] * inv;
+        return;
+    }
     float M = -INFINITY;
     for (int s = lane; s < ns; s += 64) M = fmaxf(M, pr[s * stride]);
 #pragma unroll
