@@ -1,7 +1,8 @@
-"""Seeded sweep of decode and chunk shapes against the oracle (2e-3 max-abs,
-1e-3 relative L2), through the C ABI: every path the planner picks (the
-G <= 4 and G 5-16 decodes, the latent decode, the generic kernel for other
-head_dims and for latent caches with several heads, the chunk kernels) over
+"""Seeded sweep of decode, top-K and chunk shapes against the oracle (2e-3
+max-abs, 1e-3 relative L2), through the C ABI: every path the planner picks
+(the G <= 4 and G 5-16 decodes, the latent decode, the generic kernel for
+other head_dims and for latent caches with several heads, both top-K scoring
+kernels, the chunk kernels) over
 random sequence counts, block counts (0 included), bf16 windows, mixed
 widths and query scales.  Each case's draw is fixed by its index."""
 import numpy as np
@@ -84,3 +85,25 @@ def test_sweep_chunk(case):
         want = oracle.attend_chunk_seq(b.ref_pool, s["bits"], s["koff"], s["voff"], s["kw"], s["vw"],
                                        c.H, c.D, qn[a], kn[a], vn[a], scale, 0, n_new)
         close(got[a], want, what=f"chunk case {case} seq {a}: H {H} G {G} D {D} n_new {n_new} nb {nb} win {win}")
+
+
+@pytest.mark.parametrize("case", range(12))
+def test_sweep_topk(case):
+    """Top-K over seeded shapes: a valid selection within the scores'
+    rounding allowance, then the oracle's decode over exactly the kept set."""
+    from test_gpu_topk import _check_selection, _ref_sparse, _run
+    rng = np.random.default_rng(8100 + case)
+    latent = case >= 9
+    H = 1 if latent else int(rng.choice([1, 2, 4]))
+    D = 512 if latent else int(rng.choice([64, 128, 256]))
+    R = 64 if latent else 0
+    G = int(rng.choice([2, 8, 16])) if latent else int(rng.choice([1, 2, 4, 8, 16]))
+    A, nb, win, bits = _shape(rng, 40, 100)
+    lengths = [64 * n + w for n, w in zip(nb, win)]
+    b = build(H, D, lengths, bits=bits, window=win, latent=latent, rope_dim=R, seed=8200 + case)
+    q = syn.random_normal_bf16((A, G * H, D + R), 8300 + case, scale=2.0)
+    scale = (D + R) ** -0.5
+    K = int(rng.integers(1, 24))
+    got, sel = _run(b, q, scale, K)
+    _check_selection(b, q, scale, K, sel)
+    close(got, _ref_sparse(b, q, scale, sel), what=f"topk case {case}: H {H} G {G} D {D} K {K} nb {nb}")
