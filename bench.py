@@ -89,14 +89,15 @@ TRAFFIC = {
     (1, "kvq quantize"): (("quantize.hip",), "7dbb68a3958abdc3", 82011.6, 46080.1),
     (2, "kvq quantize"): (("quantize.hip",), "7dbb68a3958abdc3", 268019.0, 119946.0),
     (3, "kvq dequantize"): (("quantize.hip",), "7dbb68a3958abdc3", 9271.5, 65561.8),
-    (3, "kvq attend_chunk"): (("chunk.hip",), "7e9bc99935b2e36f", 47185.6 + 16672.5, 35004.3 + 8192.0),
+    (3, "kvq quantize"): (("quantize.hip",), "7dbb68a3958abdc3", 65619.1, 36864.1),
+    (3, "kvq attend_chunk"): (("chunk.hip",), "f1f82d8b56dc9dce", 47171.2 + 16694.0, 35002.1 + 8192.0),
     (1, "kvq attend_decode"): (("decode_g4.hip", "decode_gqa.hip"), "f633df87aab3ffcf",
                                23481.7 + 2656.4, 5440.0 + 160.0),
     (2, "kvq attend_decode"): (("decode_g4.hip", "decode_gqa.hip"), "f633df87aab3ffcf",
                                64375.4 + 2256.5, 4488.0 + 128.0),
     (4, "kvq quantize"): (("quantize.hip",), "7dbb68a3958abdc3", 65779.2, 36881.8),
-    (4, "kvq attend_decode"): (("mla.hip", "decode_gqa.hip"), "bf375907107cbd5a",
-                               27101.0 + 4169.1, 10792.0 + 128.0),
+    (4, "kvq attend_decode"): (("mla.hip", "decode_gqa.hip"), "a70bab6a9d0fc0e3",
+                               27101.1 + 4169.1, 10700.7 + 128.0),
     ("alloc", "kvq block_sensitivity"): (("alloc.hip",), "daa276e1c505e00b", 430498.4, 62.0),
 }
 
