@@ -39,41 +39,68 @@ __device__ __forceinline__ float block_tiles(const TopkArgs &p, const uint8_t *b
     const size_t rope_tokens = (size_t)64 * p.t.max_blocks + p.t.window_cap;
     const uint32_t *meta = reinterpret_cast<const uint32_t *>(blk + (size_t)H * 64 * CODE_ROW);
     float best = -INFINITY;
+    // two 16-key tiles' code rows and rope rows are loaded before their
+    // products (two memory round trips per block instead of four)
 #pragma unroll 1
-    for (int tau = 0; tau < 4; tau++) {
-        const int key = 16 * tau + m;                           // A operand row of this lane
-        const uint8_t *row = blk + ((size_t)g * 64 + key) * CODE_ROW;
-        f4 T[NG], Tr = {0.f, 0.f, 0.f, 0.f};
+    for (int hf = 0; hf < 2; hf++) {
+        uint32_t w[2][NG][ND];
+        uint4 rq[2][R > 0 ? R / 32 : 1];
 #pragma unroll
-        for (int gg = 0; gg < NG; gg++) {
-            uint32_t w[ND];
-            GRow<B>::load(w, row + 8 * B * gg, q);
-            f4 acc = {0.f, 0.f, 0.f, 0.f};
+        for (int tt = 0; tt < 2; tt++) {
+            const int tau = 2 * hf + tt;
+            const int key = 16 * tau + m;
+            const uint8_t *row = blk + ((size_t)g * 64 + key) * CODE_ROW;
 #pragma unroll
-            for (int u = 0; u < 2; u++)
-                acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(operand(GRow<B>::chunk(w, q, u)), qop[2 * gg + u], acc,
-                                                             0, 0, 0);
-            T[gg] = acc;
+            for (int gg = 0; gg < NG; gg++) GRow<B>::load(w[tt][gg], row + 8 * B * gg, q);
+            if constexpr (R > 0) {
+                const uint16_t *rr = p.rope + (((size_t)a * rope_tokens + (size_t)64 * j + key) * H + g) * R;
+#pragma unroll
+                for (int r = 0; r < R / 32; r++) rq[tt][r] = *reinterpret_cast<const uint4 *>(rr + 32 * r + 8 * q);
+            }
         }
-        if constexpr (R > 0) {
-            const uint16_t *rr = p.rope + (((size_t)a * rope_tokens + (size_t)64 * j + key) * H + g) * R;
 #pragma unroll
-            for (int r = 0; r < R / 32; r++)
-                Tr = __builtin_amdgcn_mfma_f32_16x16x32_f16(
-                    operand(bf16_pairs(*reinterpret_cast<const uint4 *>(rr + 32 * r + 8 * q))), qop[2 * NG + r], Tr, 0,
-                    0, 0);
-        }
-        // lane (head m, q) holds keys 16 tau + 4q + i, i = 0..3
-#pragma unroll
-        for (int i = 0; i < 4; i++) {
-            const uint32_t *km = meta + ((size_t)g * 64 + 16 * tau + 4 * q + i) * NG;
-            float sc = Tr[i];
+        for (int tt = 0; tt < 2; tt++) {
+            const int tau = 2 * hf + tt;
+            f4 T[NG], Tr = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int gg = 0; gg < NG; gg++) {
-                const h2 sb = as_h2(km[gg]);
-                sc = __builtin_fmaf((float)sb[0], T[gg][i], __builtin_fmaf((float)sb[1], qsum[gg], sc));
+                f4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int u = 0; u < 2; u++)
+                    acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(operand(GRow<B>::chunk(w[tt][gg], q, u)),
+                                                                 qop[2 * gg + u], acc, 0, 0, 0);
+                T[gg] = acc;
             }
-            best = fmaxf(best, sc);
+            if constexpr (R > 0) {
+#pragma unroll
+                for (int r = 0; r < R / 32; r++)
+                    Tr = __builtin_amdgcn_mfma_f32_16x16x32_f16(operand(bf16_pairs(rq[tt][r])), qop[2 * NG + r], Tr, 0,
+                                                                0, 0);
+            }
+            // lane (head m, q) holds keys 16 tau + 4q + i, i = 0..3; their NG
+            // metadata words are contiguous (16-byte loads when NG % 4 == 0)
+#pragma unroll
+            for (int i = 0; i < 4; i++) {
+                const uint32_t *km = meta + ((size_t)g * 64 + 16 * tau + 4 * q + i) * NG;
+                uint32_t kmv[NG];
+                if constexpr (NG % 4 == 0) {
+#pragma unroll
+                    for (int c = 0; c < NG / 4; c++) {
+                        const uint4 v = reinterpret_cast<const uint4 *>(km)[c];
+                        kmv[4 * c] = v.x; kmv[4 * c + 1] = v.y; kmv[4 * c + 2] = v.z; kmv[4 * c + 3] = v.w;
+                    }
+                } else {
+#pragma unroll
+                    for (int gg = 0; gg < NG; gg++) kmv[gg] = km[gg];
+                }
+                float sc = Tr[i];
+#pragma unroll
+                for (int gg = 0; gg < NG; gg++) {
+                    const h2 sb = as_h2(kmv[gg]);
+                    sc = __builtin_fmaf((float)sb[0], T[gg][i], __builtin_fmaf((float)sb[1], qsum[gg], sc));
+                }
+                best = fmaxf(best, sc);
+            }
         }
     }
     return best;
