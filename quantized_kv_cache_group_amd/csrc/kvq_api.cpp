@@ -409,9 +409,19 @@ int check_decode(const kvq_layout *L, const kvq_store *K, const kvq_store *V, co
     return KVQ_OK;
 }
 
+// Rope rows of a compacted (top-K) latent layout read in place from the full
+// layout: slot j of sequence a takes block map[a][j]; the window follows
+// block min(nb[a], max_blocks); tokens is the full layout's rows per sequence.
+struct RopeMap {
+    const int32_t *map;
+    const int32_t *nb;
+    int max_blocks;
+    int64_t tokens;
+};
+
 int attend_decode_impl(const kvq_layout *L, const kvq_store *K, const kvq_store *V, const uint16_t *rope,
                        int32_t rope_dim, const uint16_t *q, int32_t n_q_heads, float softmax_scale, float *out,
-                       void *workspace, const Plan &pl, void *stream);
+                       void *workspace, const Plan &pl, void *stream, const RopeMap *rm = nullptr);
 }  // namespace
 
 extern "C" {
@@ -435,7 +445,7 @@ namespace {
 // The decode's launches once every argument has been checked.
 int attend_decode_impl(const kvq_layout *L, const kvq_store *K, const kvq_store *V, const uint16_t *rope,
                        int32_t rope_dim, const uint16_t *q, int32_t n_q_heads, float softmax_scale, float *out,
-                       void *workspace, const Plan &pl, void *stream)
+                       void *workspace, const Plan &pl, void *stream, const RopeMap *rm)
 {
     float *part = static_cast<float *>(workspace);
 
@@ -474,8 +484,14 @@ int attend_decode_impl(const kvq_layout *L, const kvq_store *K, const kvq_store 
         d.SB = pl.mla_sb;
         d.n_splits = pl.mla_splits;
         d.c = softmax_scale * 1.4426950408889634f;
-        return hip_status(launch_mla(d, rope, rope_dim, (int64_t)L->max_blocks * 64 + L->window_cap,
-                                     static_cast<hipStream_t>(stream)));
+        int64_t rope_tokens = (int64_t)L->max_blocks * 64 + L->window_cap;
+        if (rm && rope_dim) {
+            d.rope_map = rm->map;
+            d.rope_nb = rm->nb;
+            d.rope_max_blocks = rm->max_blocks;
+            rope_tokens = rm->tokens;
+        }
+        return hip_status(launch_mla(d, rope, rope_dim, rope_tokens, static_cast<hipStream_t>(stream)));
     }
 
     AttnArgs a{};
@@ -660,7 +676,19 @@ int kvq_attend_decode_topk(const kvq_layout *L, const kvq_store *K, const kvq_st
         decode_g4_plan(L->n_seqs, L->n_heads, L->head_dim, L->max_blocks, 0, &g4.SB, &splits);
         p.score_stride = L->n_heads;
     }
-    if (launch_topk_select(p, use_g4 ? &g4 : nullptr, hs) != hipSuccess) return KVQ_EHIP;
+    // The latent kernel reads the kept blocks' rope rows in place (through
+    // the selection's block indices); other decodes read a compacted copy.
+    const bool mla_route = !V && rope_dim > 0 && mla_supported(L->head_dim, L->n_heads, p.G, rope_dim);
+    if (launch_topk_select(p, use_g4 ? &g4 : nullptr, !mla_route, hs) != hipSuccess) return KVQ_EHIP;
+    if (mla_route) {
+        Plan pl;
+        if ((st = check_decode(&L2, &K2, nullptr, rope, rope_dim, q, n_q_heads, softmax_scale, out, &pl)))
+            return st;
+        if (w.dec_bytes < pl.ws_bytes) return KVQ_ENOSPC;
+        const RopeMap rm{p.sel_idx, L->n_blocks, L->max_blocks, (int64_t)L->max_blocks * 64 + L->window_cap};
+        return attend_decode_impl(&L2, &K2, nullptr, rope, rope_dim, q, n_q_heads, softmax_scale, out, ws + w.dec,
+                                  pl, stream, &rm);
+    }
     return kvq_attend_decode(&L2, &K2, V ? &V2 : nullptr, p.rope_sel, rope_dim, q, n_q_heads, softmax_scale, out,
                              ws + w.dec, w.dec_bytes, stream);
 }

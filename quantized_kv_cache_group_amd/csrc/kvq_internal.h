@@ -78,6 +78,13 @@ struct DecodeArgs {
     int SB;                     // 64-token blocks per split
     int n_splits;               // grid.x: block splits + 1 window split
     float c;                    // softmax_scale * log2(e)
+    // Latent decode over a compacted table (top-K): block slot j of sequence
+    // a takes its rope rows from block rope_map[a][j] of the full layout, and
+    // the window's rope rows follow block min(rope_nb[a], rope_max_blocks) of
+    // it.  Null rope_map: rope rows follow the table itself.
+    const int32_t *rope_map;
+    const int32_t *rope_nb;
+    int rope_max_blocks;
 };
 
 // Chunk attention (matrix cores), head_dim 64/128/256.
@@ -149,7 +156,10 @@ struct TopkArgs {
     int sel_stride;             // >= top_k; columns past top_k get -1
 };
 bool topk_supported(int max_blocks, int G, int head_dim, int rope_dim);
-hipError_t launch_topk_select(const TopkArgs &p, const DecodeArgs *g4, hipStream_t s);  // g4: score with the decode kernel
+// g4: score with the decode kernel; copy_rope: write rope_sel for a decode
+// that reads the compacted layout's rope rows (the latent kernel reads them
+// in place through DecodeArgs::rope_map instead)
+hipError_t launch_topk_select(const TopkArgs &p, const DecodeArgs *g4, bool copy_rope, hipStream_t s);
 
 // Width allocation: block sensitivity (GPU) and the budgeted greedy (host).
 bool sensitivity_supported(int H, int D, int Hq);

@@ -83,6 +83,7 @@ __device__ __forceinline__ void load_share(uint32_t (&c)[16], const uint8_t *p)
 struct MlaMeta {
     int base, bits;
     uint32_t lo, hi;
+    int rope_blk;                       // block of the rope rows (DecodeArgs::rope_map)
 };
 
 __device__ __forceinline__ void mla_meta(MlaMeta &mm, const DecodeArgs &p, int a, int j0, int j1)
@@ -91,8 +92,10 @@ __device__ __forceinline__ void mla_meta(MlaMeta &mm, const DecodeArgs &p, int a
     mm.base = j0;
     mm.bits = 0;
     mm.lo = mm.hi = 0;
+    mm.rope_blk = jb;
     if (jb < j1) {
         const size_t e = (size_t)a * p.t.max_blocks + jb;
+        if (p.rope_map) mm.rope_blk = p.rope_map[e];
         mm.bits = p.t.bits[e];
         const uint64_t o = p.k.offset[e];
         mm.lo = (uint32_t)o;
@@ -125,7 +128,10 @@ __device__ __forceinline__ void load_block(MlaRaw &raw, MlaMeta &mm, const Decod
     }
     const uint32_t mw = *reinterpret_cast<const uint32_t *>(blk + (64 * row_bytes + 4 * (key * (DL / 64) + e8)));
     uint4 rr = {0, 0, 0, 0};
-    if (R) rr = *reinterpret_cast<const uint4 *>(rope + ((size_t)a * rope_tokens + (size_t)kt * TILE + key) * R + 8 * e8);
+    if (R) {
+        const int rb = __builtin_amdgcn_readlane(mm.rope_blk, i);
+        rr = *reinterpret_cast<const uint4 *>(rope + ((size_t)a * rope_tokens + (size_t)rb * TILE + key) * R + 8 * e8);
+    }
 #pragma unroll
     for (int x = 0; x < 16; x++) raw.c[x] = c[x];
     raw.r[0] = rr.x; raw.r[1] = rr.y; raw.r[2] = rr.z; raw.r[3] = rr.w;
@@ -207,8 +213,10 @@ __device__ __forceinline__ void store_window(const DecodeArgs &p, const uint16_t
     for (int ch = 0; ch < 8; ch++)
         *reinterpret_cast<h8 *>(row + ((64 * e8 + 8 * ch) ^ sw)) = row_order(bf16_pairs(src[ch]));
     if (R) {
+        int rnb = nb;
+        if (p.rope_map) rnb = min(max(p.rope_nb[a], 0), p.rope_max_blocks);
         const uint4 *rp = reinterpret_cast<const uint4 *>(
-            rope + ((size_t)a * rope_tokens + (size_t)nb * TILE + w) * R + 8 * e8);
+            rope + ((size_t)a * rope_tokens + (size_t)rnb * TILE + w) * R + 8 * e8);
         *reinterpret_cast<h8 *>(row + ((DL + 8 * e8) ^ sw)) = row_order(bf16_pairs(rp[0]));
     }
 }
@@ -321,6 +329,7 @@ __global__ __launch_bounds__(512, 1) void mla_split(DecodeArgs p, const uint16_t
     // those past n_blocks are never used).  Block data waits for the counts.
     MlaMeta mm;
     mm.base = -(1 << 20);
+    mm.rope_blk = 0;
     if (s * p.SB < p.t.max_blocks) mla_meta(mm, p, a, s * p.SB, min(s * p.SB + p.SB, p.t.max_blocks));
 
     MlaState<R> w;

@@ -415,7 +415,7 @@ bool topk_supported(int max_blocks, int G, int head_dim, int rope_dim)
     return max_blocks <= MAXB && G * (head_dim + rope_dim) <= MAXQ;
 }
 
-hipError_t launch_topk_select(const TopkArgs &p, const DecodeArgs *g4, hipStream_t s)
+hipError_t launch_topk_select(const TopkArgs &p, const DecodeArgs *g4, bool copy_rope, hipStream_t s)
 {
     if (p.t.max_blocks > 0) {
         hipError_t e;
@@ -453,7 +453,7 @@ hipError_t launch_topk_select(const TopkArgs &p, const DecodeArgs *g4, hipStream
     }
     select_blocks<<<p.t.A, 256, 0, s>>>(p);
     hipError_t e = hipGetLastError();
-    if (e != hipSuccess || !p.rope_dim) return e;
+    if (e != hipSuccess || !p.rope_dim || !copy_rope) return e;
     const int wchunks = (p.t.window_cap + 63) / 64;
     compact_rope<<<dim3(p.top_k + wchunks, p.t.A), 256, 0, s>>>(p);
     return hipGetLastError();
