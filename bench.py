@@ -96,8 +96,8 @@ TRAFFIC = {
     (2, "kvq attend_decode"): (("decode_g4.hip", "decode_gqa.hip"), "f633df87aab3ffcf",
                                64375.4 + 2256.5, 4488.0 + 128.0),
     (4, "kvq quantize"): (("quantize.hip",), "7dbb68a3958abdc3", 65779.2, 36881.8),
-    (4, "kvq attend_decode"): (("mla.hip", "decode_gqa.hip"), "a70bab6a9d0fc0e3",
-                               27101.1 + 4169.1, 10700.7 + 128.0),
+    (4, "kvq attend_decode"): (("mla.hip", "decode_gqa.hip"), "0b21d666257d7d17",
+                               27102.6 + 4169.1, 10746.6 + 128.0),
     ("alloc", "kvq block_sensitivity"): (("alloc.hip",), "daa276e1c505e00b", 430498.4, 62.0),
 }
 
