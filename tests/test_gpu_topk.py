@@ -114,6 +114,26 @@ def test_topk_latent_rope():
     close(got, _ref_sparse(b, q, scale, sel), what="topk latent+rope")
 
 
+@pytest.mark.parametrize("G", [4, 16])
+def test_topk_latent_rope_kept_rows_in_place(G):
+    """The latent route reads the kept blocks' rope rows where they lie (at
+    the selected block's position, and the window's after the sequence's full
+    block count): sequences with fewer blocks than K (all kept, window after
+    them), none (window only), K of many with a window, and K of many without
+    one; 2-, 3-, 4- and 8-bit latents mixed."""
+    H, D, R = 1, 512, 64
+    lengths = [64 * 3 + 10, 40, 64 * 25 + 33, 64 * 18]
+    window = [10, 40, 33, 0]
+    nb = [(L - w) // 64 for L, w in zip(lengths, window)]
+    bits = [np.array([(2, 3, 4, 8)[(a + j) % 4] for j in range(n)], np.uint8) for a, n in enumerate(nb)]
+    b = build(H, D, lengths, bits=bits, window=window, latent=True, rope_dim=R, seed=97 + G)
+    q = syn.random_normal_bf16((len(lengths), G, D + R), 98 + G, scale=2.0)
+    scale = (D + R) ** -0.5
+    got, sel = _run(b, q, scale, 5)
+    _check_selection(b, q, scale, 5, sel)
+    close(got, _ref_sparse(b, q, scale, sel), what=f"topk latent rope in place G={G}")
+
+
 def test_topk_many_blocks_per_thread():
     """More blocks than the selection's 256 threads (several blocks per
     thread in the scans), mixed widths, one short sequence."""
