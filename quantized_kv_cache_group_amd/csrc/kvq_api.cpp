@@ -678,16 +678,19 @@ int kvq_attend_decode_topk(const kvq_layout *L, const kvq_store *K, const kvq_st
     }
     // The latent kernel reads the kept blocks' rope rows in place (through
     // the selection's block indices); other decodes read a compacted copy.
+    // Everything the decode checks is checked before the first launch.
     const bool mla_route = !V && rope_dim > 0 && mla_supported(L->head_dim, L->n_heads, p.G, rope_dim);
+    Plan mpl;
+    if (mla_route) {
+        if ((st = check_decode(&L2, &K2, nullptr, rope, rope_dim, q, n_q_heads, softmax_scale, out, &mpl)))
+            return st;
+        if (w.dec_bytes < mpl.ws_bytes) return KVQ_ENOSPC;
+    }
     if (launch_topk_select(p, use_g4 ? &g4 : nullptr, !mla_route, hs) != hipSuccess) return KVQ_EHIP;
     if (mla_route) {
-        Plan pl;
-        if ((st = check_decode(&L2, &K2, nullptr, rope, rope_dim, q, n_q_heads, softmax_scale, out, &pl)))
-            return st;
-        if (w.dec_bytes < pl.ws_bytes) return KVQ_ENOSPC;
         const RopeMap rm{p.sel_idx, L->n_blocks, L->max_blocks, (int64_t)L->max_blocks * 64 + L->window_cap};
         return attend_decode_impl(&L2, &K2, nullptr, rope, rope_dim, q, n_q_heads, softmax_scale, out, ws + w.dec,
-                                  pl, stream, &rm);
+                                  mpl, stream, &rm);
     }
     return kvq_attend_decode(&L2, &K2, V ? &V2 : nullptr, p.rope_sel, rope_dim, q, n_q_heads, softmax_scale, out,
                              ws + w.dec, w.dec_bytes, stream);
