@@ -92,12 +92,12 @@ TRAFFIC = {
     (3, "kvq dequantize"): (("quantize.hip",), "7dbb68a3958abdc3", 9271.5, 65561.8),
     (3, "kvq quantize"): (("quantize.hip",), "7dbb68a3958abdc3", 65619.1, 36864.1),
     (3, "kvq attend_chunk"): (("chunk.hip",), "f1f82d8b56dc9dce", 47171.2 + 16694.0, 35002.1 + 8192.0),
-    (1, "kvq attend_decode"): (("decode_g4.hip", "decode_gqa.hip"), "f633df87aab3ffcf",
+    (1, "kvq attend_decode"): (("decode_g4.hip", "decode_gqa.hip"), "a496b36197a8d745",
                                23481.7 + 2656.4, 5440.0 + 160.0),
-    (2, "kvq attend_decode"): (("decode_g4.hip", "decode_gqa.hip"), "f633df87aab3ffcf",
+    (2, "kvq attend_decode"): (("decode_g4.hip", "decode_gqa.hip"), "a496b36197a8d745",
                                64375.4 + 2256.5, 4488.0 + 128.0),
     (4, "kvq quantize"): (("quantize.hip",), "7dbb68a3958abdc3", 65779.2, 36881.8),
-    (4, "kvq attend_decode"): (("mla.hip", "decode_gqa.hip"), "0b21d666257d7d17",
+    (4, "kvq attend_decode"): (("mla.hip", "decode_gqa.hip"), "5116f3d8b60628e6",
                                27102.6 + 4169.1, 10746.6 + 128.0),
     ("alloc", "kvq block_sensitivity"): (("alloc.hip",), "daa276e1c505e00b", 430498.4, 62.0),
 }

@@ -322,7 +322,7 @@ __device__ __forceinline__ void softmax_pv(DecodeState<NG> &st, const f4 (&T)[2]
 template <int NG>
 __global__ __launch_bounds__(64) void decode_gqa_split(DecodeArgs p)
 {
-    constexpr int D = 64 * NG, KS = 2 * NG, NT = 4 * NG;
+    constexpr int D = 64 * NG, NT = 4 * NG;
     __shared__ __attribute__((aligned(16))) _Float16 vt[D * (STEP + VT_PAD)];
     __shared__ __attribute__((aligned(16))) StepMeta<NG> sm;
     const int s = blockIdx.x, g = blockIdx.y, a = blockIdx.z;
