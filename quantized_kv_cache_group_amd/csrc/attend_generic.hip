@@ -216,7 +216,7 @@ __global__ __launch_bounds__(NT) void attend_split_generic(AttnArgs p)
             }
         }
     }
-    if (threadIdx.x < nrows && k_begin < lim_s[threadIdx.x]) {
+    if ((int)threadIdx.x < nrows && k_begin < lim_s[threadIdx.x]) {
         RowInfo ri = row_info(p, g, tile, threadIdx.x, L.T);
         const size_t row = ((size_t)a * p.n_qtok + ri.i) * p.Hq + ri.h;
         p.part[row * rstride + (size_t)s * (Dv + 2) + 0] = m_run;
