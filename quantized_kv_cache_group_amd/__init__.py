@@ -18,7 +18,9 @@ import numpy as np
 import torch
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(HERE, "libkvq.so")
+# KVQ_LIB selects another build of the same sources (the host-sanitized one
+# that build.build_host_sanitized() writes); by default the in-tree build.
+LIB_PATH = os.environ.get("KVQ_LIB") or os.path.join(HERE, "libkvq.so")
 
 KVQ_OK, KVQ_EINVAL, KVQ_ENOSPC, KVQ_EUNSUPPORTED, KVQ_EHIP = 0, -1, -2, -3, -4
 OUT_BF16, OUT_F32 = 0, 1

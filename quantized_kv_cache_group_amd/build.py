@@ -34,10 +34,18 @@ SOURCES = ["kvq_api.cpp", "quantize.hip", "attend_generic.hip", "decode_gqa.hip"
            "mla.hip", "card.hip", "sparse.hip", "alloc.hip"]
 
 
-def _compile(src: str) -> str:
-    obj = os.path.join(BUILD, os.path.basename(src) + ".o")
+# Host-side AddressSanitizer + UBSan (the device code is compiled as in the
+# normal build): every sanitizer flag applies to the host pass only.
+HOST_SANITIZE = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+                 "-Xarch_host", "-fno-sanitize-recover=all", "-Xarch_host", "-fno-omit-frame-pointer"]
+ASAN_BUILD = os.path.join(HERE, "_build_asan")
+ASAN_LIB = os.path.join(HERE, "libkvq_asan.so")
+
+
+def _compile(src: str, build_dir: str = BUILD, extra=()) -> str:
+    obj = os.path.join(build_dir, os.path.basename(src) + ".o")
     lang = [] if src.endswith(".hip") else ["-x", "hip"]
-    cmd = [HIPCC, *COMMON, *PER_FILE.get(src, []), *lang, "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [HIPCC, *COMMON, *PER_FILE.get(src, []), *extra, *lang, "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode:
         sys.stderr.write(r.stdout + r.stderr)
@@ -57,6 +65,25 @@ def build() -> str:
         raise RuntimeError("link failed")
     os.replace(tmp, LIB)
     return LIB
+
+
+def build_host_sanitized() -> str:
+    """The same library with its host code (argument checks, planning, the
+    width allocator's greedy, launch code) built with AddressSanitizer and
+    UBSan, as libkvq_asan.so beside the normal build.  It is never loaded by
+    default: a process selects it with KVQ_LIB and must preload clang's ASan
+    runtime (the interpreter is not instrumented)."""
+    os.makedirs(ASAN_BUILD, exist_ok=True)
+    with ThreadPoolExecutor(max_workers=min(8, len(SOURCES))) as ex:
+        objs = list(ex.map(lambda src: _compile(src, ASAN_BUILD, HOST_SANITIZE), SOURCES))
+    tmp = ASAN_LIB + ".tmp"
+    cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", *HOST_SANITIZE, "-shared-libsan", *objs, "-o", tmp]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode:
+        sys.stderr.write(r.stdout + r.stderr)
+        raise RuntimeError("link failed")
+    os.replace(tmp, ASAN_LIB)
+    return ASAN_LIB
 
 
 if __name__ == "__main__":
