@@ -488,7 +488,7 @@ def topk_bench(args):
     gbs = algo / (sp_us * 1e-6) / 1e9
     name = (f"deepseek-v2-lite-mla-4agent-{T}tok-q4-top{K}" if mla else f"llama8b-10agent-{T}tok-q4-top{K}")
     res = {"metric": "top-K sparse decode GB/s", "value": round(gbs, 2), "unit": "GB/s", "n_gpus": 1,
-           "steps": args.steps, "warmup": args.warmup, "higher_is_better": True, "dtype": "fp16 mfma, fp32 acc",
+           "steps": args.steps, "warmup": args.warmup, "settle_ms": SETTLE_MS, "higher_is_better": True, "dtype": "fp16 mfma, fp32 acc",
            "data": "synthetic",
            "config": {"workload": name, "agents": A, "q_heads": Hq, "kv_heads": H, "head_dim": D,
                       "rope_dim": R_, "blocks": nblk, "top_k": K, "bits": 4, "rotated_copies": R},
@@ -543,7 +543,7 @@ def alloc_bench(args):
     widths = kvq.allocate_widths(allS, H, D, budget)
     t_alloc = time.perf_counter() - t0
     res = {"metric": "block sensitivity GB/s", "value": round(gbs, 2), "unit": "GB/s", "n_gpus": 1,
-           "steps": args.steps, "warmup": args.warmup, "higher_is_better": True, "dtype": "f32",
+           "steps": args.steps, "warmup": args.warmup, "settle_ms": SETTLE_MS, "higher_is_better": True, "dtype": "f32",
            "data": "synthetic",
            "config": {"workload": "gemma12b-8agent-width-allocation", "agents": A, "q_heads": Hq, "kv_heads": H,
                       "head_dim": D, "rows_per_agent": S_tok, "layers": len(w.layers)},
@@ -607,7 +607,7 @@ def restore_bench(args):
     algo = 2 * (A * w.n_blocks[0] * blk + A * S * H * D * 2)
     gbs = algo / (us * 1e-6) / 1e9
     res = {"metric": "kvq_dequantize (restore) GB/s", "value": round(gbs, 2), "unit": "GB/s", "n_gpus": 1,
-           "steps": args.steps, "warmup": args.warmup, "higher_is_better": True, "dtype": "f32",
+           "steps": args.steps, "warmup": args.warmup, "settle_ms": SETTLE_MS, "higher_is_better": True, "dtype": "f32",
            "data": "synthetic",
            "config": {"workload": "llama8b-32k-restore-kv-bf16", "agents": A, "kv_heads": H, "head_dim": D,
                       "cache_tokens": S, "bits": 4, "rotated_copies": R},
@@ -682,7 +682,7 @@ def card_bench(args):
     g_gbs = 2 * n / (g_us * 1e-6) / 1e9
     s_gbs = 2 * n / (s_us * 1e-6) / 1e9
     res = {"metric": "CacheCard gather GB/s", "value": round(g_gbs, 2), "unit": "GB/s", "n_gpus": 1,
-           "steps": args.steps, "warmup": args.warmup, "higher_is_better": True, "dtype": "u8",
+           "steps": args.steps, "warmup": args.warmup, "settle_ms": SETTLE_MS, "higher_is_better": True, "dtype": "u8",
            "data": "synthetic",
            "config": {"workload": "llama8b-10agent-q4-cachecard", "agents": A, "kv_heads": H, "head_dim": D,
                       "tokens": w.lengths[0], "bits": 4, "image_bytes": n, "rotated_copies": R},
