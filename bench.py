@@ -8,9 +8,10 @@ for the restore + chunk workload.  Cache copies rotate so that at least
 2 x 256 MB of other copies pass between two reads of one (the Infinity
 Cache holds nothing a call can use); every copy is visited once, then the
 step runs untimed for ~100 ms (the GPU's clocks rise over the first few ms
-of sustained work), then the W warmup steps.  The K timed steps run back to back between one pair of HIP events
-on the launch stream (eager launches, or with --graph one replay of their
-captured HIP graph, checked against an eager step).
+of sustained work), then the W warmup steps.  The K timed steps run back to
+back between one pair of HIP events on the launch stream (eager launches,
+or with --graph one replay of their captured HIP graph, checked against an
+eager step).
 
 Prints one JSON line.  `value` is the step's algorithmic attention bytes
 (codes and scale/bias of the blocks, bf16 windows, rope rows, queries and
